@@ -1,0 +1,467 @@
+"""Pins for the CPU oracle: closed forms, brute force, invariants.
+
+Each test fixes the oracle against something other than itself, so that a
+dropped term, a wrong sign, an off-by-one or a transposed operand in
+``oracle/oracle.c`` fails at least one of them.  The method's definitions are
+those of the "DeepSeek-V4 Architecture Analysis" page (INNOVATIONS section 1,
+compressed sparse attention: window, 4:1 / 128:1 compression, indexer with
+per-head importance weights, top-k, per-head sink; section 2: K = V) and the
+DeepSeek-V4-Flash config table (index_n_heads, index_head_dim, index_topk,
+sliding_window).
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from compressed_sparse_attention_indexer_amd import inputs
+
+F32 = "f32"
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ----------------------------------------------------------------------------- visibility (a0)
+
+def test_visible_count_matches_span_definition():
+    """Entry j spans raw tokens [r*j, r*j+r-1]; it is visible when every token
+    of the span is at or before the query (checked token by token here)."""
+    for r in (1, 2, 4, 128):
+        for L in (0, 1, 3, 4, 5, 17, 128, 300):
+            for p in range(0, max(L, 1)):
+                if p >= L:
+                    continue
+                brute = sum(1 for j in range(L // r)
+                            if all(t <= p and t < L for t in range(r * j, r * j + r)))
+                assert oracle.visible_count(L, p, r) == brute, (r, L, p)
+
+
+def test_prefill_visible_counts_closed_form():
+    """2048 queries at positions 1,046,528..1,048,575 over 262,144 entries:
+    counts run from 261,632 to 262,144 and sum to 536,346,112."""
+    pos = range(1046528, 1048576)
+    counts = [oracle.visible_count(1048576, p, 4) for p in (pos[0], pos[-1])]
+    assert counts == [261632, 262144]
+    # sum over t of floor((1046529 + t) / 4) = 2048 * 261632 + sum_{u=1}^{2048} floor(u/4)
+    closed = 2048 * 261632 + (4 * (511 * 512 // 2) + 512)
+    assert closed == 536346112
+    sampled = sum(oracle.visible_count(1048576, p, 4) for p in pos[::97])
+    assert sampled == sum((p + 1) // 4 for p in pos[::97])
+
+
+# ----------------------------------------------------------------------------- scores (a1)
+
+def _scores(q_idx, w, k, L=None, p=None, ratio=1, act=oracle.ACT_RELU, n_max=None):
+    """Single query helper: q_idx [HI,DI], w [HI], k [N,DI]."""
+    N = k.shape[0]
+    L = N * ratio if L is None else L
+    p = L - 1 if p is None else p
+    n_max = N if n_max is None else n_max
+    s = oracle.index_scores(q_idx[None, None].astype(np.float32), w[None, None].astype(np.float32),
+                            [k.astype(np.float32)], np.array([L]), np.array([p]), ratio=ratio,
+                            n_max=n_max, dtype=F32, act=act)
+    return s[0, 0]
+
+
+def test_scores_hand_example():
+    """Two heads, two dims, worked by hand:
+    head 0 reads dim 0, head 1 reads dim 1; weights 1 and 1/2.
+    k0=( 2,-1): relu 2, relu -1 -> 1*2 + 0.5*0 = 2
+    k1=(-3, 4): 0 + 0.5*4 = 2;  k2=(1,1): 1 + 0.5 = 1.5;  k3=(-1,-1): 0.
+    Without the activation: 1.5, -1, 1.5, -1.5."""
+    q = np.array([[1, 0], [0, 1]], np.float32)
+    w = np.array([1.0, 0.5], np.float32)
+    k = np.array([[2, -1], [-3, 4], [1, 1], [-1, -1]], np.float32)
+    assert _scores(q, w, k).tolist() == [2.0, 2.0, 1.5, 0.0]
+    assert _scores(q, w, k, act=oracle.ACT_NONE).tolist() == [1.5, -1.0, 1.5, -1.5]
+
+
+def test_scores_one_head_is_relu_dot():
+    rng = _rng(1)
+    q = rng.standard_normal((1, 16)).astype(np.float32)
+    k = rng.standard_normal((50, 16)).astype(np.float32)
+    got = _scores(q, np.ones(1, np.float32), k)
+    want = np.maximum(0.0, k.astype(np.float64) @ q[0].astype(np.float64)).astype(np.float32)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_scores_without_activation_fold_the_weights():
+    """With no nonlinearity the weighted head sum is one dot product with the
+    weight-folded query: s_j = (sum_h w_h q_h) . k_j."""
+    rng = _rng(2)
+    q = rng.standard_normal((8, 16)).astype(np.float32)
+    w = rng.random(8).astype(np.float32)
+    k = rng.standard_normal((40, 16)).astype(np.float32)
+    got = _scores(q, w, k, act=oracle.ACT_NONE)
+    folded = (w.astype(np.float64)[:, None] * q.astype(np.float64)).sum(0)
+    np.testing.assert_allclose(got, k.astype(np.float64) @ folded, rtol=1e-6, atol=1e-6)
+
+
+def test_scores_head_and_dim_orientation():
+    """One-hot queries and keys: head h reads only dim h, key j is nonzero
+    only on dim j % DI, so each score picks exactly one weight.  A transposed
+    query or key indexing breaks the pattern."""
+    HI, DI, N = 4, 6, 12
+    q = np.zeros((HI, DI), np.float32)
+    for h in range(HI):
+        q[h, h + 1] = 1.0          # head h looks at dim h+1
+    w = np.array([1.0, 2.0, 4.0, 8.0], np.float32)
+    k = np.zeros((N, DI), np.float32)
+    for j in range(N):
+        k[j, j % DI] = 3.0
+    got = _scores(q, w, k)
+    want = [3.0 * w[(j % DI) - 1] if 1 <= j % DI <= HI else 0.0 for j in range(N)]
+    assert got.tolist() == want
+
+
+def test_scores_invariances():
+    rng = _rng(3)
+    q = rng.standard_normal((6, 16)).astype(np.float32)
+    w = rng.random(6).astype(np.float32)
+    k = rng.standard_normal((64, 16)).astype(np.float32)
+    base = _scores(q, w, k)
+    perm = rng.permutation(6)
+    np.testing.assert_allclose(_scores(q[perm], w[perm], k), base, rtol=1e-6)  # head order
+    np.testing.assert_array_equal(_scores(q, 2 * w, k), 2 * base)             # exact scaling
+    assert (base >= 0).all()
+
+
+def test_scores_visibility_mask():
+    """ratio 4, L = 40 (10 entries), query at position 21: entries whose span
+    ends at or before 21 are j <= 4 (span of j=4 is 16..19; j=5 is 20..23)."""
+    rng = _rng(4)
+    q = rng.standard_normal((2, 8)).astype(np.float32)
+    k = rng.standard_normal((10, 8)).astype(np.float32)
+    s = _scores(q, np.ones(2, np.float32), k, L=40, p=21, ratio=4, n_max=12)
+    assert np.isfinite(s[:5]).all() and np.isneginf(s[5:]).all()
+    s = _scores(q, np.ones(2, np.float32), k, L=40, p=23, ratio=4, n_max=12)
+    assert np.isfinite(s[:6]).all() and np.isneginf(s[6:]).all()
+
+
+# ----------------------------------------------------------------------------- top-k (a2)
+
+def _topk1(s, k, L=None, p=None, ratio=1):
+    n = s.shape[0]
+    L = n * ratio if L is None else L
+    p = L - 1 if p is None else p
+    return oracle.topk(s[None, None].astype(np.float32), np.array([L]), np.array([p]),
+                       ratio=ratio, k=k)[0, 0]
+
+
+def _brute_topk(s, k):
+    """O(N^2) rank counting: j is kept iff fewer than k entries beat it, where
+    i beats j when s_i > s_j or (s_i == s_j and i < j)."""
+    n = len(s)
+    keep = [j for j in range(n)
+            if sum(1 for i in range(n) if s[i] > s[j] or (s[i] == s[j] and i < j)) < k]
+    return keep + [-1] * (k - len(keep))
+
+
+@pytest.mark.parametrize("seed,n,k", [(0, 7, 3), (1, 64, 16), (2, 300, 32), (3, 513, 512),
+                                      (4, 40, 64), (5, 1, 1), (6, 200, 1)])
+def test_topk_brute_force(seed, n, k):
+    rng = _rng(seed)
+    s = rng.standard_normal(n).astype(np.float32)
+    s[rng.integers(0, n, n // 3)] = s[rng.integers(0, n, n // 3)]  # plenty of exact ties
+    if n > 4:
+        s[: n // 4] = 0.5
+    assert _topk1(s, k).tolist() == _brute_topk(s.tolist(), k)
+
+
+def test_topk_textbook_sort():
+    """numpy lexsort by (-score, index), first k, sorted ascending."""
+    rng = _rng(7)
+    s = np.round(rng.standard_normal(5000), 1).astype(np.float32)  # many ties
+    order = np.lexsort((np.arange(len(s)), -s.astype(np.float64)))
+    want = np.sort(order[:512])
+    np.testing.assert_array_equal(_topk1(s, 512), want)
+
+
+def test_topk_ties_go_to_lower_index():
+    s = np.array([1, 3, 3, 2, 3, 3], np.float32)
+    assert _topk1(s, 3).tolist() == [1, 2, 4]
+    assert _topk1(s, 1).tolist() == [1]
+    assert _topk1(np.zeros(5, np.float32), 2).tolist() == [0, 1]
+
+
+def test_topk_invariants_and_padding():
+    rng = _rng(8)
+    s = rng.standard_normal(1000).astype(np.float32)
+    sel = _topk1(s, 100)
+    assert (np.diff(sel) > 0).all()
+    rest = np.setdiff1d(np.arange(1000), sel)
+    assert s[sel].min() >= s[rest].max()
+    np.testing.assert_array_equal(_topk1(2.5 * s, 100), sel)          # positive scaling
+    perm = rng.permutation(1000)                                      # equivariance (no ties)
+    np.testing.assert_array_equal(np.sort(perm[_topk1(s[perm], 100)]), sel)
+    short = _topk1(s[:10], 16)
+    assert short[:10].tolist() == list(range(10)) and short[10:].tolist() == [-1] * 6
+
+
+def test_topk_only_visible_entries():
+    """Scores of entries that are not visible are never selected, whatever
+    their value (ratio 4, L=40, p=21: only j<=4 visible)."""
+    s = np.arange(12, dtype=np.float32)[::-1].copy()
+    s[6:] = 100.0
+    sel = _topk1(s, 3, L=40, p=21, ratio=4)
+    assert sel.tolist() == [0, 1, 2]
+
+
+# ----------------------------------------------------------------------------- attention (a3, a4)
+
+def _att(q, rows, vrows=None, sink=None, scale=1.0):
+    return oracle.attend_rows(np.asarray(q, np.float32), np.asarray(rows, np.float32),
+                              None if vrows is None else np.asarray(vrows, np.float32),
+                              None if sink is None else np.asarray(sink, np.float32),
+                              scale=scale, dtype=F32)
+
+
+def test_attention_single_row_is_sigmoid_gate():
+    """One row with logit z and a sink s: weight sigma(z - s) on its value."""
+    q = np.array([[0.5, 0.25, 0.0, 1.0]])
+    k = np.array([[1.0, 2.0, 3.0, 0.25]])         # q.k = 0.5 + 0.5 + 0 + 0.25 = 1.25
+    v = np.array([[2.0, -1.0, 4.0, 8.0]])
+    sink = np.array([-0.5], np.float32)
+    out, lse = _att(q, k, v, sink, scale=0.5)     # z = 0.625
+    z, s = 0.625, float(sink[0])
+    np.testing.assert_allclose(out[0], v[0] / (1.0 + math.exp(s - z)), rtol=1e-12)
+    np.testing.assert_allclose(lse[0], math.log(math.exp(z) + math.exp(s)), rtol=1e-12)
+
+
+def test_attention_zero_query_uniform_with_sink():
+    """q = 0: every logit is 0, so each of the n rows gets 1/(n + e^sink)."""
+    rng = _rng(9)
+    n, D = 7, 5
+    rows = rng.standard_normal((n, D)).astype(np.float32)
+    vrows = rng.standard_normal((n, D)).astype(np.float32).astype(np.float64)
+    sink = np.array([0.3, -2.0], np.float32)
+    out, lse = _att(np.zeros((2, D)), rows, vrows, sink)
+    for h in range(2):
+        den = n + math.exp(float(sink[h]))
+        np.testing.assert_allclose(out[h], vrows.sum(0) / den, rtol=1e-12)
+        np.testing.assert_allclose(lse[h], math.log(den), rtol=1e-12)
+
+
+def test_attention_constant_values_and_sink_mass():
+    """Every value row equal to c gives (1 - p_sink) c with p_sink = e^(sink - lse)."""
+    rng = _rng(10)
+    H, n, D = 3, 11, 6
+    q, rows = rng.standard_normal((H, D)), rng.standard_normal((n, D))
+    c = rng.standard_normal(D).astype(np.float32).astype(np.float64)
+    sink = rng.standard_normal(H).astype(np.float32)
+    out, lse = _att(q, rows, np.tile(c, (n, 1)), sink, scale=0.7)
+    for h in range(H):
+        p_sink = math.exp(float(sink[h]) - lse[h])
+        assert 0 < p_sink < 1
+        np.testing.assert_allclose(out[h], (1 - p_sink) * c, rtol=1e-12, atol=1e-14)
+
+
+def test_attention_probabilities_from_one_hot_values():
+    """With value row i = e_i the output row is the probability vector; it must
+    equal exp(z_i - lse) with z_i = scale * q.k_i and, with the sink's share,
+    sum to one."""
+    rng = _rng(11)
+    H, n, D, scale = 4, 9, 12, 0.37
+    q, rows = rng.standard_normal((H, D)), rng.standard_normal((n, D))
+    vrows = np.eye(n, D)
+    sink = rng.standard_normal(H).astype(np.float32)
+    out, lse = _att(q, rows, vrows, sink, scale=scale)
+    z = scale * (q.astype(np.float32).astype(np.float64) @ rows.astype(np.float32).astype(np.float64).T)
+    np.testing.assert_allclose(out[:, :n], np.exp(z - lse[:, None]), rtol=1e-12)
+    np.testing.assert_allclose(out[:, :n].sum(1) + np.exp(sink.astype(np.float64) - lse), 1.0, rtol=1e-12)
+    assert (out[:, n:] == 0).all()
+
+
+def test_attention_two_rows_no_sink():
+    q = np.array([[1.0, 0.0]])
+    rows = np.array([[2.0, 0.0], [0.0, 5.0]])      # z = 2, 0
+    vrows = np.array([[1.0, 0.0], [0.0, 1.0]])
+    out, lse = _att(q, rows, vrows, None)
+    e = math.exp(2.0)
+    np.testing.assert_allclose(out[0], [e / (e + 1), 1 / (e + 1)], rtol=1e-12)
+    np.testing.assert_allclose(lse[0], math.log(e + 1), rtol=1e-12)
+
+
+def test_attention_values_default_to_keys():
+    rng = _rng(12)
+    q, rows = rng.standard_normal((2, 8)), rng.standard_normal((5, 8))
+    a = _att(q, rows, None, np.zeros(2))
+    b = _att(q, rows, rows, np.zeros(2))
+    np.testing.assert_array_equal(a[0], b[0])
+
+
+def test_merge_of_partials_equals_whole():
+    """Split the rows into random parts, attend to each part without the sink,
+    merge with the sink: same as attending to all rows at once."""
+    rng = _rng(13)
+    H, n, D = 5, 60, 16
+    q, rows, vrows = (rng.standard_normal(s) * 2 for s in ((H, D), (n, D), (n, D)))
+    sink = rng.standard_normal(H).astype(np.float32)
+    whole, lse = _att(q, rows, vrows, sink, scale=0.5)
+    for parts in (1, 2, 7):
+        cuts = np.sort(rng.choice(np.arange(1, n), parts - 1, replace=False)) if parts > 1 else []
+        bounds = [0, *cuts, n]
+        ms, ls, os_ = [], [], []
+        for a, b in zip(bounds[:-1], bounds[1:]):
+            m, l, o = oracle.partial_rows(q.astype(np.float32), rows[a:b].astype(np.float32),
+                                          vrows[a:b].astype(np.float32), scale=0.5, dtype=F32)
+            ms.append(m), ls.append(l), os_.append(o)
+        # an empty part must be harmless
+        ms.append(np.full(H, -np.inf)), ls.append(np.zeros(H)), os_.append(np.zeros((H, D)))
+        out, lse2 = oracle.merge_partials(np.array(ms), np.array(ls), np.array(os_), sink)
+        np.testing.assert_allclose(out, whole, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(lse2, lse, rtol=1e-12)
+
+
+# ----------------------------------------------------------------------------- row sets of the sparse / HCA paths
+
+def _tagged_case(L=64, ratio=4, W=8, K=5, D=64, p=None, H=2):
+    """Compressed rows and window rows whose values are one-hot tags, a zero
+    query (uniform weights) and no sink: the output row shows exactly which
+    rows were attended."""
+    p = L - 1 if p is None else p
+    N = L // ratio
+    kv = np.zeros((N, D), np.float32)
+    for j in range(N):
+        kv[j, j] = 1.0
+    pos0, nrow = max(0, p - W + 1), p - max(0, p - W + 1) + 1
+    win = np.zeros((nrow, D), np.float32)
+    for t in range(nrow):
+        win[t, N + t] = 1.0
+    q = np.zeros((1, 1, H, D), np.float32)
+    sink = np.full(H, -np.inf, np.float32)
+    return dict(q=q, kv=[kv], win=[win], pos0=np.array([pos0]), nrow=np.array([nrow]),
+                L=np.array([L]), p=np.array([p]), sink=sink, N=N)
+
+
+def test_sparse_rows_are_selected_then_window():
+    c = _tagged_case()
+    idx = np.array([[[1, 4, 9, 15, -1]]], np.int32)
+    out, _ = oracle.sparse_mqa(c["q"], c["kv"], None, c["win"], None, c["pos0"], c["nrow"], idx, c["L"],
+                               c["p"], c["sink"], window=8, ratio=4, scale=1.0, dtype=F32)
+    n = 4 + 8
+    want = np.zeros(64)
+    want[[1, 4, 9, 15]] = 1.0 / n
+    want[c["N"]:c["N"] + 8] = 1.0 / n     # raw positions 56..63
+    np.testing.assert_allclose(out[0, 0, 0], want, rtol=1e-12)
+
+
+def test_window_is_last_w_positions_including_query():
+    """Query at position 13 of a 64-token buffer with W=8: raw positions 6..13."""
+    c = _tagged_case(p=13, L=64)
+    W = 8
+    # window buffer covering positions 0..20, tagged by position
+    win = np.zeros((21, 64), np.float32)
+    for t in range(21):
+        win[t, 30 + t] = 1.0
+    idx = np.full((1, 1, 3), -1, np.int32)
+    idx[0, 0, 0] = 2                       # entry 2 spans 8..11 (visible at 13)
+    out, _ = oracle.sparse_mqa(c["q"], c["kv"], None, [win], None, np.array([0]), np.array([21]), idx,
+                               c["L"], c["p"], c["sink"], window=W, ratio=4, scale=1.0, dtype=F32)
+    got = np.nonzero(out[0, 0, 0])[0].tolist()
+    assert got == [2] + [30 + t for t in range(6, 14)]
+
+
+def test_sparse_rejects_invisible_index_and_short_window():
+    c = _tagged_case(p=21, L=64)
+    idx = np.array([[[5, -1, -1, -1, -1]]], np.int32)   # entry 5 spans 20..23, not visible at 21
+    with pytest.raises(oracle.OracleError):
+        oracle.sparse_mqa(c["q"], c["kv"], None, c["win"], None, c["pos0"], c["nrow"], idx, c["L"],
+                          c["p"], c["sink"], window=8, ratio=4, scale=1.0, dtype=F32)
+    idx[0, 0, 0] = 2
+    with pytest.raises(oracle.OracleError):   # window buffer starting one position too late
+        oracle.sparse_mqa(c["q"], c["kv"], None, c["win"], None, c["pos0"] + 1, c["nrow"], idx, c["L"],
+                          c["p"], c["sink"], window=8, ratio=4, scale=1.0, dtype=F32)
+
+
+def test_hca_rows_are_all_visible_entries_then_window():
+    c = _tagged_case(L=64, p=45, ratio=4)   # 11 visible entries (spans up to 40..43)
+    out, _ = oracle.hca_mqa(c["q"], c["kv"], None, c["win"], None, c["pos0"], c["nrow"], c["L"], c["p"],
+                            c["sink"], window=8, ratio=4, scale=1.0, dtype=F32)
+    got = np.nonzero(out[0, 0, 0])[0].tolist()
+    assert got == list(range(11)) + [c["N"] + t for t in range(8)]
+
+
+def test_sparse_with_all_entries_equals_hca():
+    rng = _rng(14)
+    B, H, D, L, W, r = 2, 3, 16, 96, 8, 4
+    N = L // r
+    q = rng.standard_normal((B, 1, H, D)).astype(np.float32)
+    kv = [rng.standard_normal((N, D)).astype(np.float32) for _ in range(B)]
+    v = [rng.standard_normal((N, D)).astype(np.float32) for _ in range(B)]
+    win = [rng.standard_normal((W, D)).astype(np.float32) for _ in range(B)]
+    args = (np.full(B, L - W), np.full(B, W))
+    sink = rng.standard_normal(H).astype(np.float32)
+    Ls, ps = np.full(B, L), np.full(B, L - 1)
+    idx = np.tile(np.arange(N, dtype=np.int32), (B, 1, 1))
+    a = oracle.sparse_mqa(q, kv, v, win, None, *args, idx, Ls, ps, sink, window=W, ratio=r, scale=0.25,
+                          dtype=F32)
+    b = oracle.hca_mqa(q, kv, v, win, None, *args, Ls, ps, sink, window=W, ratio=r, scale=0.25, dtype=F32)
+    np.testing.assert_allclose(a[0], b[0], rtol=1e-12)
+    np.testing.assert_allclose(a[1], b[1], rtol=1e-12)
+
+
+# ----------------------------------------------------------------------------- whole step, tiny sizes
+
+def _dense_brute(case):
+    """A second route for the whole step on tiny inputs: dense masked softmax.
+    Scores by einsum, top-k by rank counting, attention as one softmax over
+    [all compressed rows | window rows | sink column] with -inf on compressed
+    rows that were not selected."""
+    wl = case.wl
+    f = lambda x: inputs.as_float64(x, wl.dtype)
+    B, T, H, D = case.q.shape
+    scale = 1.0 / math.sqrt(D)
+    outs = np.zeros((B, T, H, D))
+    for b, t in itertools.product(range(B), range(T)):
+        p = int(case.q_pos[b * T + t])
+        N = int(case.seq_len[b]) // wl.ratio
+        nv = min(N, (p + 1) // wl.ratio)
+        dots = np.einsum("hd,jd->hj", f(case.q_idx[b, t]), f(case.k_idx[b]))
+        s = (case.w[b, t].astype(np.float64)[:, None] * np.maximum(dots, 0)).sum(0).astype(np.float32)
+        keep = _brute_topk(s[:nv].tolist(), wl.topk)
+        keep = [j for j in keep if j >= 0]
+        lo = max(0, p - wl.window + 1)
+        wrows = f(case.win[b])[lo - case.win_pos0[b]: p - case.win_pos0[b] + 1]
+        wvals = wrows if case.win_v is None else f(case.win_v[b])[lo - case.win_pos0[b]: p - case.win_pos0[b] + 1]
+        K = f(case.kv[b])
+        V = K if case.v is None else f(case.v[b])
+        allk, allv = np.concatenate([K, wrows]), np.concatenate([V, wvals])
+        z = scale * f(case.q[b, t]) @ allk.T                     # [H, N + nwin]
+        mask = np.full(z.shape[1], -np.inf)
+        mask[keep] = 0.0
+        mask[N:] = 0.0
+        z = z + mask
+        zs = np.concatenate([z, case.sink.astype(np.float64)[:, None]], axis=1)
+        pr = np.exp(zs - zs.max(1, keepdims=True))
+        pr /= pr.sum(1, keepdims=True)
+        outs[b, t] = pr[:, :-1] @ allv
+    return outs
+
+
+@pytest.mark.parametrize("L,K", [(512, 32), (160, 64), (64, 8)])
+def test_whole_step_against_dense_brute_force(L, K):
+    wl = inputs.scaled(inputs.WORKLOADS["fixture_b2_l512_fp32"], f"tiny_{L}_{K}", seq_len=L, topk=K)
+    case = inputs.make_case(wl)
+    _, _, out, _ = oracle.csa_attention(case)
+    np.testing.assert_allclose(out, _dense_brute(case), rtol=1e-9, atol=1e-12)
+
+
+def test_fixture_golden_file_matches():
+    """The stored fixture outputs were written by tests/golden/make_golden.py
+    (which calls only the oracle); a change of the oracle's arithmetic shows
+    here."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "fixture_b2_l512_fp32.json")
+    g = json.load(open(path))
+    case = inputs.make_case(inputs.WORKLOADS["fixture_b2_l512_fp32"])
+    scores, idx, out, lse = oracle.csa_attention(case)
+    assert idx.tolist() == g["topk_idx"]
+    np.testing.assert_array_equal(scores, np.array(g["scores"], np.float32))
+    np.testing.assert_allclose(out, np.array(g["out"]), rtol=1e-12)
+    np.testing.assert_allclose(lse, np.array(g["lse"]), rtol=1e-12)
