@@ -1,0 +1,347 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSA decode path on one MI355X.
+
+Workload (default): million-token decode, batch 4, 1,048,576 raw tokens per
+sequence -> 262,144 compressed entries (ratio 4); indexer 64 heads x 128;
+top-512; 128-token window; 64 query heads x 512 with one shared KV head; sink.
+Inputs are seeded synthetic tensors, resident in HBM before timing.
+
+One step = one pass of the CSA layer's hot path: indexer scores -> top-k ->
+sparse MQA with sink (the launch sequence of csa_attention), over the whole
+batch.  Steps are captured in a HIP graph and replayed; the index-key and KV
+caches rotate between several device copies so the 256 MiB last-level cache
+cannot hold them from one step to the next.  The paired HCA layer, the other
+decode workloads and the per-kernel times are reported under "breakdown".
+
+Prints one JSON line.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CSA decode queries/s at 64K–1M ctx; achieved HBM GB/s vs peak (1 GPU)"
+HBM_PEAK_GBS = 8000.0
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_index_scores_decode_b4_1m.json")
+SCORER_SRC = os.path.join(ROOT, "compressed_sparse_attention_indexer_amd", "csrc", "scorer.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="decode_b4_1m")
+    p.add_argument("--copies", type=int, default=2, help="device copies of the caches, rotated per step")
+    p.add_argument("--graph-steps", type=int, default=10, help="steps captured per graph")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--quick", action="store_true", help="skip the other decode workloads")
+    p.add_argument("--prefill", action="store_true", help="also time the 2048-token prefill chunk")
+    p.add_argument("--profile-kernels", action="store_true",
+                   help="run only eager scorer launches (for rocprofv3 counter runs)")
+    return p.parse_args()
+
+
+def sha_of(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+# ------------------------------------------------------------------ algorithmic bytes (per call)
+
+def csa_step_bytes(n_ent, n_queries):
+    """Per query: index keys 256 B/entry, q_idx 16 KiB, weights 256 B, q 64 KiB,
+    512 selected + 128 window rows of 1 KiB, sink 256 B, fp32 output 128 KiB."""
+    return int(sum(256 * int(n) for n in n_ent)) + 868864 * n_queries
+
+
+def scorer_bytes(n_ent, n_queries):
+    """Index keys (256 B per entry) plus index query and weights (16,640 B per query)."""
+    return int(sum(256 * int(n) for n in n_ent)) + 16640 * n_queries
+
+
+def hca_bytes(n_h, n_queries):
+    return int(sum(1024 * (int(n) + 128) for n in n_h)) + 196864 * n_queries
+
+
+# ------------------------------------------------------------------ timing helpers
+
+class Timer:
+    """Times a callable that enqueues work on torch's current stream: HIP
+    events around `reps` back-to-back calls, average per call in ms."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def per_call_ms(self, fn, reps):
+        t = self.torch
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        b.synchronize()
+        return a.elapsed_time(b) / reps
+
+
+def capture(torch, fn, n):
+    """HIP graph of n calls of fn (each enqueues kernels on the capture stream)."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(0)  # warm the code path outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    torch.cuda.synchronize()
+    return g
+
+
+class CsaRunner:
+    """Pre-allocated buffers and rotated cache copies for one CSA workload."""
+
+    def __init__(self, torch, csa, dc, copies):
+        self.t, self.csa, self.dc = torch, csa, dc
+        self.dims = dc.csa_dims()
+        d = self.dims
+        dev = "cuda"
+        self.scores = torch.empty((d.batch, d.q_len, d.max_entries), dtype=torch.float32, device=dev)
+        self.idx = torch.empty((d.batch, d.q_len, d.topk), dtype=torch.int32, device=dev)
+        self.out = torch.empty((d.batch, d.q_len, d.n_heads, d.head_dim), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((d.batch, d.q_len, d.n_heads), dtype=torch.float32, device=dev)
+        self.ws_topk = self._ws(csa.workspace_size(d, csa._lib.CSA_OP_TOPK))
+        self.ws_mqa = self._ws(csa.workspace_size(d, csa._lib.CSA_OP_SPARSE_MQA))
+        self.ws_all = self._ws(csa.workspace_size(d, csa._lib.CSA_OP_ATTENTION))
+        self.kidx_p, self.kv_p = [dc.k_idx_p], [dc.kv_p]
+        self.keep = []
+        for _ in range(copies - 1):
+            k2 = [x.clone() for x in dc.k_idx]
+            v2 = [x.clone() for x in dc.kv]
+            self.keep += [k2, v2]
+            self.kidx_p.append(csa.ptr_array(k2, dev))
+            self.kv_p.append(csa.ptr_array(v2, dev))
+
+    def _ws(self, n):
+        return self.t.empty(max(n, 256), dtype=self.t.uint8, device="cuda")
+
+    def scores_call(self, i):
+        dc = self.dc
+        self.csa.csa_index_scores(self.dims, dc.q_idx, dc.w, self.kidx_p[i % len(self.kidx_p)], dc.seq_len,
+                                  dc.q_pos, scores=self.scores)
+
+    def topk_call(self, i):
+        dc = self.dc
+        self.csa.csa_topk_select(self.dims, self.scores, dc.seq_len, dc.q_pos, topk_idx=self.idx,
+                                 workspace=self.ws_topk)
+
+    def attn_call(self, i):
+        dc = self.dc
+        self.csa.csa_sparse_mqa_decode(self.dims, dc.q, self.kv_p[i % len(self.kv_p)], None, self.idx, dc.win_p,
+                                       None, dc.win_pos0, dc.win_rows, dc.seq_len, dc.q_pos, dc.sink,
+                                       out=self.out, lse=self.lse, workspace=self.ws_mqa)
+
+    def step(self, i):
+        self.scores_call(i)
+        self.topk_call(i)
+        self.attn_call(i)
+
+    def fused(self, i):
+        dc = self.dc
+        self.csa.csa_attention(self.dims, dc.q, dc.q_idx, dc.w, self.kidx_p[i % len(self.kidx_p)],
+                               self.kv_p[i % len(self.kv_p)], None, dc.win_p, None, dc.win_pos0, dc.win_rows,
+                               dc.seq_len, dc.q_pos, dc.sink, out=self.out, lse=self.lse, workspace=self.ws_all)
+
+
+def time_graph(torch, g, graph_steps, steps, warmup):
+    for _ in range(max(1, warmup // graph_steps)):
+        g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // graph_steps)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return a.elapsed_time(b) / (reps * graph_steps), wall, reps * graph_steps
+
+
+def bench_csa(torch, csa, case, args, detail):
+    from compressed_sparse_attention_indexer_amd.staging import DeviceCase
+    dc = DeviceCase(case)
+    r = CsaRunner(torch, csa, dc, args.copies)
+    Q = r.dims.batch * r.dims.q_len
+    n_ent = case.n_entries
+    gs = args.graph_steps
+    g_step = capture(torch, r.step, gs)
+    ms, wall, n = time_graph(torch, g_step, gs, args.steps, args.warmup)
+    # graph replay result == eager result (deterministic kernels)
+    out_graph = r.out.clone()
+    r.step((n - 1) % args.copies)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out_graph, r.out))
+    res = {"ms_per_step": ms, "queries_per_s": Q / (ms * 1e-3), "steps": n, "wall_s": wall,
+           "graph_matches_eager": same,
+           "alg_bytes_per_step": csa_step_bytes(n_ent, Q),
+           "step_GBps": csa_step_bytes(n_ent, Q) / (ms * 1e-3) / 1e9}
+    res["step_frac_hbm_peak"] = res["step_GBps"] / HBM_PEAK_GBS
+    if detail:
+        per = {}
+        for name, fn in (("index_scores", r.scores_call), ("topk_select", r.topk_call),
+                         ("sparse_mqa", r.attn_call)):
+            g = capture(torch, fn, gs)
+            per[name], _, _ = time_graph(torch, g, gs, args.steps, args.warmup)
+        g_f = capture(torch, r.fused, gs)
+        res["fused_entry_ms"], _, _ = time_graph(torch, g_f, gs, args.steps, args.warmup)
+        res["kernel_ms"] = per
+        res["scorer_alg_bytes"] = scorer_bytes(n_ent, Q)
+    return res, r
+
+
+def bench_hca(torch, csa, case, args):
+    from compressed_sparse_attention_indexer_amd.staging import DeviceCase
+    dc = DeviceCase(case)
+    d = dc.hca_dims()
+    Q = d.batch * d.q_len
+    out = torch.empty((d.batch, d.q_len, d.n_heads, d.head_dim), dtype=torch.float32, device="cuda")
+    lse = torch.empty((d.batch, d.q_len, d.n_heads), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(256, csa.workspace_size(d, csa._lib.CSA_OP_HCA_MQA)), dtype=torch.uint8, device="cuda")
+    copies = [dc.hca_kv_p]
+    keep = []
+    for _ in range(args.copies - 1):
+        k2 = [x.clone() for x in dc.hca_kv]
+        keep.append(k2)
+        copies.append(csa.ptr_array(k2, "cuda"))
+
+    def call(i):
+        csa.hca_mqa_decode(d, dc.hca_q, copies[i % len(copies)], None, dc.hca_win_p, None, dc.win_pos0,
+                           dc.win_rows, dc.seq_len, dc.q_pos, dc.hca_sink, out=out, lse=lse, workspace=ws)
+
+    g = capture(torch, call, args.graph_steps)
+    ms, _, n = time_graph(torch, g, args.graph_steps, args.steps, args.warmup)
+    n_h = case.seq_len // case.wl.hca_ratio
+    b = hca_bytes(n_h, Q)
+    return {"ms_per_call": ms, "queries_per_s": Q / (ms * 1e-3), "alg_bytes": b,
+            "GBps": b / (ms * 1e-3) / 1e9, "frac_hbm_peak": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
+def traffic_from_profile():
+    """HBM bytes per scorer launch from the committed rocprofv3 counter runs,
+    only while the scorer source is the one the counters were taken on."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None, "no counter profile committed"
+    rec = json.load(open(PROFILE_TRAFFIC))
+    if rec.get("scorer_sha") != sha_of(SCORER_SRC):
+        return None, "scorer changed since the counters were taken"
+    return int(rec["hbm_bytes_per_launch"]), rec.get("note", "")
+
+
+def cpu_baseline(case):
+    import oracle
+    wl = case.wl
+    t_best, runs, t_total = float("inf"), 0, 0.0
+    while runs < 3 and (runs == 0 or t_total < 10.0):
+        t0 = time.perf_counter()
+        oracle.csa_attention(case)
+        dt = time.perf_counter() - t0
+        t_best, t_total, runs = min(t_best, dt), t_total + dt, runs + 1
+    Q = wl.batch * wl.q_len
+    return {"value": Q / t_best, "unit": "queries/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"whole CSA step of {wl.name} ({Q} queries x {case.max_entries} entries), "
+                      f"best of {runs} runs, {t_best:.2f} s each"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this path has no multi-GPU "
+              f"mode: run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import compressed_sparse_attention_indexer_amd as csa
+    from compressed_sparse_attention_indexer_amd import inputs
+
+    torch.cuda.set_device(0)
+    csa.load_library()
+    wl = inputs.WORKLOADS[args.workload]
+    t0 = time.perf_counter()
+    case = inputs.make_case(wl)
+    print(f"[bench] generated {wl.name} in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    if args.profile_kernels:  # eager scorer launches only, for counter collection
+        from compressed_sparse_attention_indexer_amd.staging import DeviceCase
+        r = CsaRunner(torch, csa, DeviceCase(case), args.copies)
+        for i in range(args.steps):
+            r.scores_call(i)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_kernels": args.steps}))
+        return
+
+    main_res, runner = bench_csa(torch, csa, case, args, detail=True)
+    print(f"[bench] {wl.name}: {main_res['ms_per_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+    breakdown = {wl.name: main_res}
+    if case.hca_q is not None:
+        breakdown[wl.name + "_hca"] = bench_hca(torch, csa, case, args)
+    Q = wl.batch * wl.q_len
+    scorer_ms = main_res["kernel_ms"]["index_scores"]
+    alg = main_res["scorer_alg_bytes"]
+    traffic, traffic_note = traffic_from_profile()
+    roofline = {"kernel": "index_scores_bf16_kernel", "bound": "hbm",
+                "achieved": alg / (scorer_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": alg / (scorer_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": traffic,
+                "alg_bytes_per_launch": alg, "avg_launch_ms": scorer_ms, "traffic_note": traffic_note}
+    del runner
+    torch.cuda.empty_cache()
+
+    if not args.quick:
+        for name in ("decode_b1_64k", "decode_b32_ragged_64k_128k"):
+            if name == wl.name:
+                continue
+            c2 = inputs.make_case(inputs.WORKLOADS[name])
+            r2, rr = bench_csa(torch, csa, c2, args, detail=True)
+            breakdown[name] = r2
+            del rr, c2
+            torch.cuda.empty_cache()
+    if args.prefill:
+        c4 = inputs.make_case(inputs.WORKLOADS["prefill_t2048_1m"])
+        a2 = argparse.Namespace(**vars(args))
+        a2.steps, a2.warmup, a2.graph_steps, a2.copies = 3, 1, 1, 1
+        r4, rr = bench_csa(torch, csa, c4, a2, detail=True)
+        breakdown["prefill_t2048_1m"] = r4
+        del rr, c4
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(case)
+
+    line = {
+        "metric": METRIC, "value": main_res["queries_per_s"], "unit": "queries/s", "n_gpus": 1,
+        "steps": main_res["steps"], "warmup": args.warmup, "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; N(0,1)/sqrt(d) activations and caches, U(0,1) weights, N(0,1) sink)",
+        "config": {"workload": wl.name, "batch": wl.batch, "q_len": wl.q_len, "context": wl.seq_len,
+                   "compressed_entries": int(case.max_entries), "ratio": wl.ratio, "topk": wl.topk,
+                   "window": wl.window, "heads": wl.n_heads, "head_dim": wl.head_dim,
+                   "index_heads": wl.index_heads, "index_dim": wl.index_dim,
+                   "step": "index_scores -> topk_select -> sparse_mqa (+sink), graph-replayed",
+                   "cache_copies_rotated": args.copies},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "breakdown": breakdown,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

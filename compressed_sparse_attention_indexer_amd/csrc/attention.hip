@@ -1,0 +1,416 @@
+// Multi-query attention over a row list with a per-head sink.
+//
+// Rows of one query: the selected compressed entries (top-k indices, or every
+// visible entry for HCA), then the raw window rows of positions
+// max(0, p-W+1)..p; key and value share one row unless separate values are
+// given ("DeepSeek-V4 Architecture Analysis", INNOVATIONS 1: window, CSA/HCA
+// compression, sink; INNOVATIONS 2: unified 512-d key/value).  One softmax
+// over all rows plus the sink logit, which adds exp(sink) to the denominator
+// and has no value vector.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace csa {
+
+namespace {
+
+// Row i of a query's list -> key and value pointers (null if the row is not
+// attended: padding index, out-of-range index, or past the list end).
+struct RowList {
+    int n_sel;   // rows taken from the compressed cache
+    int n_rows;  // n_sel + window rows
+    int wlo;     // first window position
+    int n_ent;   // rows in the compressed cache of this sequence
+};
+
+__device__ __forceinline__ RowList make_rows(const MqaArgs &a, int qi) {
+    const int b = qi / a.T;
+    const int L = a.seq_len[b];
+    const int p = a.q_pos[qi];
+    RowList r;
+    r.n_ent = L > 0 ? L / a.ratio : 0;
+    const int nvis = visible_entries(L, p, a.ratio);
+    r.n_sel = a.topk_idx ? a.K : nvis;
+    const int nwin = window_span(p, a.W, a.win_pos0[b], a.win_rows[b], &r.wlo);
+    r.n_rows = r.n_sel + nwin;
+    return r;
+}
+
+template <typename T>
+__device__ __forceinline__ void row_ptrs(const MqaArgs &a, int qi, const RowList &rl, int i,
+                                         const T **kp, const T **vp) {
+    const int b = qi / a.T;
+    *kp = nullptr;
+    *vp = nullptr;
+    if (i < 0 || i >= rl.n_rows) return;
+    if (i < rl.n_sel) {
+        const int j = a.topk_idx ? a.topk_idx[(size_t)qi * a.K + i] : i;
+        if (j < 0 || j >= rl.n_ent) return;
+        *kp = (const T *)a.kv[b] + (size_t)j * a.D;
+        *vp = a.v ? (const T *)a.v[b] + (size_t)j * a.D : *kp;
+    } else {
+        const int pos = rl.wlo + (i - rl.n_sel);
+        const size_t off = (size_t)(pos - a.win_pos0[b]) * a.D;
+        *kp = (const T *)a.win[b] + off;
+        *vp = a.win_v ? (const T *)a.win_v[b] + off : *kp;
+    }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// fp32 VALU kernel (small shapes).  One workgroup per (head, query).  Pass 1
+// finds the largest logit; pass 2 accumulates exp-weighted values 256 rows at
+// a time (weights staged in LDS); the sink joins the max and the denominator.
+__global__ __launch_bounds__(256) void mqa_f32_kernel(MqaArgs a) {
+    extern __shared__ float smem[];
+    float *sq = smem;                 // [D]
+    float *sp = smem + a.D;           // [256] weights of the current row block
+    __shared__ const float *svp[256];
+    __shared__ float red[4];
+    const int h = blockIdx.x, qi = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const RowList rl = make_rows(a, qi);
+    const float *qrow = (const float *)a.q + ((size_t)qi * a.H + h) * a.D;
+    for (int d = tid; d < a.D; d += 256) sq[d] = qrow[d];
+    __syncthreads();
+    auto logit = [&](const float *k) {
+        float dot = 0.f;
+        for (int d = 0; d < a.D; ++d) dot = fmaf(sq[d], k[d], dot);
+        return dot * a.scale;
+    };
+    float m = -INFINITY;
+    for (int i = tid; i < rl.n_rows; i += 256) {
+        const float *kp, *vp;
+        row_ptrs(a, qi, rl, i, &kp, &vp);
+        if (kp) m = fmaxf(m, logit(kp));
+    }
+    m = wave_max(m);
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float sink = a.sink[h];
+    m = fmaxf(m, sink);
+    __syncthreads();
+    float l = 0.f;
+    float acc0 = 0.f, acc1 = 0.f;  // d = tid and d = tid + 256
+    for (int r0 = 0; r0 < rl.n_rows; r0 += 256) {
+        const float *kp, *vp;
+        row_ptrs(a, qi, rl, r0 + tid, &kp, &vp);
+        const float pw = kp ? expf(logit(kp) - m) : 0.f;
+        l += pw;
+        sp[tid] = pw;
+        svp[tid] = vp;
+        __syncthreads();
+        const int nb = rl.n_rows - r0 < 256 ? rl.n_rows - r0 : 256;
+        for (int t = 0; t < nb; ++t) {
+            const float *v = svp[t];
+            if (!v) continue;
+            if (tid < a.D) acc0 = fmaf(sp[t], v[tid], acc0);
+            if (tid + 256 < a.D) acc1 = fmaf(sp[t], v[tid + 256], acc1);
+        }
+        __syncthreads();
+    }
+    l = wave_sum(l);
+    if (lane == 0) red[wave] = l;
+    __syncthreads();
+    l = red[0] + red[1] + red[2] + red[3] + expf(sink - m);
+    float *orow = a.out + ((size_t)qi * a.H + h) * a.D;
+    if (tid < a.D) orow[tid] = acc0 / l;
+    if (tid + 256 < a.D) orow[tid + 256] = acc1 / l;
+    if (a.lse && tid == 0) a.lse[(size_t)qi * a.H + h] = m + logf(l);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 split-K MFMA kernel, D = 512, H = 16 * HG heads.
+//
+// Workgroup = one (query, split): 2*HG waves; wave (hg, dh) owns heads
+// [16hg, 16hg+16) and output dims [256dh, 256dh+256).  Rows stream through
+// LDS 32 at a time, gathered with 16-byte loads (each thread one row, a
+// prefetch one tile ahead in registers):
+//   krow: bf16 rows [32][520] (padded) feeding QK;
+//   vt:   fp16 values transposed to [d'][32 rows] feeding PV, where
+//         d' = (d % 8) * 64 + d / 8 keeps the transposing writes and the PV
+//         fragment reads free of bank conflicts.
+// QK: S^T[rows x heads] = K * Q^T on v_mfma_f32_16x16x32_bf16, each wave over
+// its 256 dims; the two halves are summed through LDS (a + b in both waves,
+// so both see bit-identical logits).  Online softmax in fp32 (log2 units).
+// PV: O[heads x d] += P * V on v_mfma_f32_16x16x32_f16 with P in fp16 held in
+// registers exactly as QK left it (its row order defines the k order of V).
+// Output: partial (m, l, O) per split, or the final result with the sink when
+// there is one split.
+namespace {
+constexpr int kD = 512;
+constexpr int kTile = 32;
+constexpr int kKrowStride = kD + 8;   // bf16 elements per staged row (1040 B)
+constexpr int kVtRowWords = 18;       // 32 fp16 rows + 2 pad words per d' row
+constexpr int kVtWords = kD * kVtRowWords + 2 * 8;
+
+__device__ __forceinline__ int vt_word(int d, int row) {
+    const int dp = (d & 7) * 64 + (d >> 3);
+    return dp * kVtRowWords + 2 * (dp >> 6) + (row >> 1);
+}
+}  // namespace
+
+template <int HG>
+__global__ __launch_bounds__(128 * HG) void mqa_bf16_kernel(MqaArgs a) {
+    constexpr int NW = 2 * HG;                // waves
+    constexpr int RPW = kTile / NW;           // staged rows per wave
+    constexpr int LPR = 64 / RPW;             // lanes per staged row
+    constexpr int CPL = 64 / LPR;             // 16-byte chunks per lane
+    static_assert(kTile % NW == 0 && 64 % RPW == 0, "staging layout");
+
+    __shared__ __attribute__((aligned(16))) uint16_t krow[kTile * kKrowStride];
+    __shared__ __attribute__((aligned(16))) uint32_t vt[kVtWords];
+    __shared__ float xs[NW][8][64];
+    __shared__ int rowok[kTile];
+
+    const int qi = blockIdx.y, split = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int e = lane & 15, g = lane >> 4;
+    const int hg = wave >> 1, dh = wave & 1;
+    const RowList rl = make_rows(a, qi);
+    const int r0 = split * a.rows_per_split;
+    const int r1 = r0 + a.rows_per_split < rl.n_rows ? r0 + a.rows_per_split : rl.n_rows;
+    const int ntiles = r1 > r0 ? (r1 - r0 + kTile - 1) / kTile : 0;
+    const float scale2 = a.scale * kLog2e;
+
+    // B fragments of Q^T: head 16hg + e, dims 256dh + 32ks + 8g .. +8.
+    bf16x8_t qf[8];
+    {
+        const uint16_t *qrow = (const uint16_t *)a.q + ((size_t)qi * a.H + 16 * hg + e) * kD + 256 * dh + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8_t *)(qrow + 32 * ks);
+    }
+
+    f32x4_t o[16];
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;  // head 16hg + e, log2 units
+
+    // staging role: one row, CPL chunks of 16 bytes
+    const int srow = wave * RPW + (lane % RPW);
+    const int cg = lane / RPW;
+    const bool separate_v = a.v != nullptr || a.win_v != nullptr;
+    u32x4_t kreg[CPL], vreg[CPL];
+    bool have_row = false;
+    auto fetch = [&](int t) {
+        const uint16_t *kp, *vp;
+        row_ptrs(a, qi, rl, r0 + t * kTile + srow < r1 ? r0 + t * kTile + srow : -1, &kp, &vp);
+        have_row = kp != nullptr;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const int ch = cg + LPR * c;
+            kreg[c] = have_row ? *(const u32x4_t *)(kp + 8 * ch) : u32x4_t{0u, 0u, 0u, 0u};
+            if (separate_v) vreg[c] = have_row ? *(const u32x4_t *)(vp + 8 * ch) : u32x4_t{0u, 0u, 0u, 0u};
+        }
+    };
+    if (ntiles > 0) fetch(0);
+
+    for (int t = 0; t < ntiles; ++t) {
+        __syncthreads();  // previous tile fully consumed
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const int ch = cg + LPR * c;
+            *(u32x4_t *)&krow[srow * kKrowStride + 8 * ch] = kreg[c];
+            const u32x4_t vv = separate_v ? vreg[c] : kreg[c];
+            _Float16 *vth = (_Float16 *)vt;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float lo = bf16_bits_to_f32(vv[k] & 0xFFFFu);
+                const float hi = bf16_bits_to_f32(vv[k] >> 16);
+                vth[2 * vt_word(8 * ch + 2 * k, srow) + (srow & 1)] = (_Float16)lo;
+                vth[2 * vt_word(8 * ch + 2 * k + 1, srow) + (srow & 1)] = (_Float16)hi;
+            }
+        }
+        if (cg == 0) rowok[srow] = have_row;
+        if (t + 1 < ntiles) fetch(t + 1);
+        __syncthreads();
+
+        // QK over this wave's 256 dims.
+        f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const bf16x8_t kf = *(const bf16x8_t *)&krow[(16 * mt + e) * kKrowStride + 256 * dh + 32 * ks + 8 * g];
+                sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[mt], 0, 0, 0);
+            }
+#pragma unroll
+        for (int v = 0; v < 8; ++v) xs[wave][v][lane] = sacc[v >> 2][v & 3];
+        __syncthreads();
+        float z[8];
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+            const float s = sacc[v >> 2][v & 3] + xs[wave ^ 1][v][lane];
+            const int row = 16 * (v >> 2) + 4 * g + (v & 3);
+            z[v] = rowok[row] ? s * scale2 : -INFINITY;
+        }
+        // online softmax for head 16hg + e (rows spread over the 4 lane groups)
+        float mx = z[0];
+#pragma unroll
+        for (int v = 1; v < 8; ++v) mx = fmaxf(mx, z[v]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = exp2f(m_run - m_use);
+        float pv[8], ls = 0.f;
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+            pv[v] = exp2f(z[v] - m_use);
+            ls += pv[v];
+        }
+        ls += __shfl_xor(ls, 16);
+        ls += __shfl_xor(ls, 32);
+        l_run = l_run * alpha + ls;
+        m_run = m_new;
+        if (__any(alpha != 1.f)) {
+            float ar[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * g + r);
+#pragma unroll
+            for (int dt = 0; dt < 16; ++dt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[dt][r] *= ar[r];
+        }
+        f16x8_t pf;
+#pragma unroll
+        for (int v = 0; v < 8; ++v) pf[v] = (_Float16)pv[v];
+        // PV over this wave's 256 output dims.
+#pragma unroll
+        for (int dt = 0; dt < 16; ++dt) {
+            const int d = 256 * dh + 16 * dt + e;
+            const int w0 = vt_word(d, 4 * g);
+            const uint32_t x0 = vt[w0], x1 = vt[w0 + 1], x2 = vt[w0 + 8], x3 = vt[w0 + 9];
+            const u32x4_t vw = u32x4_t{x0, x1, x2, x3};
+            const f16x8_t vf = __builtin_bit_cast(f16x8_t, vw);
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, vf, o[dt], 0, 0, 0);
+        }
+    }
+
+    // epilogue: C layout holds O[head 16hg + 4g + r][d = 256dh + 16dt + e]
+    const int hbase = 16 * hg + 4 * g;
+    if (a.n_splits == 1) {
+        const float sink2 = a.sink[16 * hg + e] * kLog2e;
+        const float M = fmaxf(m_run, sink2);
+        const float lf = l_run * exp2f(m_run - M) + exp2f(sink2 - M);
+        const float f = exp2f(m_run - M) / lf;
+        float fr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) fr[r] = __shfl(f, 4 * g + r);
+#pragma unroll
+        for (int dt = 0; dt < 16; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                a.out[((size_t)qi * a.H + hbase + r) * kD + 256 * dh + 16 * dt + e] = o[dt][r] * fr[r];
+        if (a.lse && dh == 0 && g == 0) a.lse[(size_t)qi * a.H + 16 * hg + e] = M * kLn2 + logf(lf);
+    } else {
+        const size_t ps = (size_t)qi * a.n_splits + split;
+        if (dh == 0 && g == 0) {
+            a.part_ml[(ps * a.H + 16 * hg + e) * 2 + 0] = m_run;
+            a.part_ml[(ps * a.H + 16 * hg + e) * 2 + 1] = l_run;
+        }
+        if (ntiles > 0) {
+#pragma unroll
+            for (int dt = 0; dt < 16; ++dt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    a.part_o[(ps * a.H + hbase + r) * kD + 256 * dh + 16 * dt + e] = o[dt][r];
+        }
+    }
+}
+
+// Merge split partials with the sink, counted once: one workgroup per
+// (head, query), 128 threads x 4 output dims.
+__global__ __launch_bounds__(128) void mqa_combine_kernel(MqaArgs a) {
+    __shared__ float sw[1024];
+    __shared__ float red[2];
+    const int h = blockIdx.x, qi = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int S = a.n_splits;
+    const float sink2 = a.sink[h] * kLog2e;
+    float M = sink2;
+    for (int s = tid; s < S; s += 128) {
+        const float m = a.part_ml[(((size_t)qi * S + s) * a.H + h) * 2 + 0];
+        const float l = a.part_ml[(((size_t)qi * S + s) * a.H + h) * 2 + 1];
+        if (l > 0.f) M = fmaxf(M, m);
+    }
+    M = wave_max(M);
+    if ((tid & 63) == 0) red[tid >> 6] = M;
+    __syncthreads();
+    M = fmaxf(red[0], red[1]);
+    __syncthreads();
+    float L = 0.f;
+    for (int s = tid; s < S; s += 128) {
+        const float m = a.part_ml[(((size_t)qi * S + s) * a.H + h) * 2 + 0];
+        const float l = a.part_ml[(((size_t)qi * S + s) * a.H + h) * 2 + 1];
+        const float wgt = l > 0.f ? exp2f(m - M) : 0.f;
+        if (s < 1024) sw[s] = wgt;
+        L += l * wgt;
+    }
+    L = wave_sum(L);
+    if ((tid & 63) == 0) red[tid >> 6] = L;
+    __syncthreads();
+    L = red[0] + red[1] + exp2f(sink2 - M);
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < S; ++s) {
+        const float wgt = sw[s];
+        if (wgt == 0.f) continue;
+        const f32x4_t x = *(const f32x4_t *)&a.part_o[(((size_t)qi * S + s) * a.H + h) * a.D + 4 * tid];
+        acc += wgt * x;
+    }
+    const float inv = 1.f / L;
+    *(f32x4_t *)&a.out[((size_t)qi * a.H + h) * a.D + 4 * tid] = acc * inv;
+    if (a.lse && tid == 0) a.lse[(size_t)qi * a.H + h] = M * kLn2 + logf(L);
+}
+
+void mqa_plan(int n_queries, int max_rows, int *n_splits, int *rows_per_split) {
+    // ~512 workgroups in flight, at least 64 rows per split, whole tiles.
+    const int want_splits = (512 + n_queries - 1) / n_queries;
+    int rps = (max_rows + want_splits - 1) / want_splits;
+    if (rps < 64) rps = 64;
+    rps = (rps + kTile - 1) / kTile * kTile;
+    int s = (max_rows + rps - 1) / rps;
+    if (s < 1) s = 1;
+    if (s > 1024) {
+        s = 1024;
+        rps = ((max_rows + s - 1) / s + kTile - 1) / kTile * kTile;
+        s = (max_rows + rps - 1) / rps;
+    }
+    *n_splits = s;
+    *rows_per_split = rps;
+}
+
+size_t mqa_workspace_bytes(int dtype, int n_queries, int H, int D, int max_rows) {
+    if (dtype != kBF16) return 0;
+    int s, rps;
+    mqa_plan(n_queries, max_rows, &s, &rps);
+    if (s == 1) return 0;
+    const size_t n = (size_t)n_queries * s * H;
+    return n * D * 4 + n * 2 * 4 + 256;
+}
+
+void mqa_carve(MqaArgs &a, void *ws, int n_queries) {
+    a.part_o = nullptr;
+    a.part_ml = nullptr;
+    if (a.n_splits <= 1) return;
+    char *p = (char *)(((uintptr_t)ws + 255) & ~(uintptr_t)255);
+    const size_t n = (size_t)n_queries * a.n_splits * a.H;
+    a.part_o = (float *)p;
+    a.part_ml = (float *)(p + n * a.D * 4);
+}
+
+hipError_t launch_mqa(const MqaArgs &a, int dtype, hipStream_t stream) {
+    const int Q = a.B * a.T;
+    if (dtype == kF32) {
+        const size_t lds = sizeof(float) * (size_t)(a.D + 256);
+        hipLaunchKernelGGL(mqa_f32_kernel, dim3(a.H, Q), dim3(256), lds, stream, a);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(mqa_bf16_kernel<4>, dim3(a.n_splits, Q), dim3(512), 0, stream, a);
+    if (a.n_splits > 1) hipLaunchKernelGGL(mqa_combine_kernel, dim3(a.H, Q), dim3(128), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace csa

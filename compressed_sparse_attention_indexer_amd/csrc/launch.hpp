@@ -1,0 +1,78 @@
+// Kernel argument blocks and launchers (host side of the HIP path).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa {
+
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+
+struct ScoreArgs {
+    const void *q_idx;          // [Q, HI, DI]
+    const float *w;             // [Q, HI]
+    const void *const *k_idx;   // [B] -> [N_b, DI]
+    const int32_t *seq_len;     // [B]
+    const int32_t *q_pos;       // [Q]
+    float *scores;              // [Q, n_max]
+    int B, T, HI, DI, ratio, act, n_max;
+    int chunk;                  // entries per workgroup (bf16 kernel)
+};
+
+hipError_t launch_index_scores(const ScoreArgs &a, int dtype, hipStream_t stream);
+int score_chunk(int n_max, int n_queries);
+
+struct TopkArgs {
+    const float *scores;        // [Q, n_max]
+    const int32_t *seq_len;     // [B]
+    const int32_t *q_pos;       // [Q]
+    int32_t *idx;               // [Q, K]
+    int B, T, ratio, K, n_max;
+    // multi-workgroup path scratch (inside the caller's workspace)
+    uint32_t *hist;             // [Q, kTopkBins]
+    uint32_t *counters;         // [Q, 4]
+    int32_t *sel;               // [Q, K] entries above the threshold bin
+    uint32_t *cand_key;         // [Q, kTopkCand]
+    int32_t *cand_idx;          // [Q, kTopkCand]
+    int chunk;                  // entries per workgroup (multi-workgroup path)
+};
+
+constexpr int kTopkLdsCap = 32768;   // largest score row kept whole in LDS
+constexpr int kTopkBins = 4096;      // first-level histogram (top 12 key bits)
+constexpr int kTopkCand = 8192;      // candidates kept for the final in-LDS pass
+constexpr int kTopkMaxK = 2048;
+
+size_t topk_workspace_bytes(int n_queries, int K, int n_max);
+void topk_carve(TopkArgs &a, void *ws, int n_queries);
+hipError_t launch_topk(const TopkArgs &a, hipStream_t stream);
+
+struct MqaArgs {
+    const void *q;                  // [Q, H, D]
+    const void *const *kv;          // [B] -> [N_b, D]
+    const void *const *v;           // [B] -> [N_b, D] or null (V = K)
+    const int32_t *topk_idx;        // [Q, K] or null (dense: every visible entry)
+    const void *const *win;         // [B] -> [win_rows_b, D]
+    const void *const *win_v;       // or null
+    const int32_t *win_pos0;        // [B]
+    const int32_t *win_rows;        // [B]
+    const int32_t *seq_len;         // [B]
+    const int32_t *q_pos;           // [Q]
+    const float *sink;              // [H]
+    float *out;                     // [Q, H, D]
+    float *lse;                     // [Q, H] or null
+    float *part_o;                  // [Q, S, H, D]   (split partials)
+    float *part_ml;                 // [Q, S, H, 2]
+    int B, T, H, D, K, W, ratio;
+    int n_splits, rows_per_split;
+    float scale;                    // softmax scale (natural units)
+};
+
+// Split plan for the bf16 split-K kernel: max_rows = largest row count of a query.
+void mqa_plan(int n_queries, int max_rows, int *n_splits, int *rows_per_split);
+size_t mqa_workspace_bytes(int dtype, int n_queries, int H, int D, int max_rows);
+void mqa_carve(MqaArgs &a, void *ws, int n_queries);
+hipError_t launch_mqa(const MqaArgs &a, int dtype, hipStream_t stream);
+
+}  // namespace csa

@@ -1,0 +1,163 @@
+// Indexer scorer: s[q, j] = sum_h w[q,h] * act(q_idx[q,h,:] . k_idx_b[j,:]).
+// The indexer compares each query against every compressed entry with a
+// dot product per indexer head and weights the heads by per-query importance
+// weights ("DeepSeek-V4 Architecture Analysis", INNOVATIONS 1, indexer bullet;
+// DeepSeek-V4-Flash config: index_n_heads 64, index_head_dim 128).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace csa {
+
+// ---------------------------------------------------------------------------
+// fp32 VALU kernel for small shapes (fixture).  One thread per entry, the
+// query's index vectors and weights staged in LDS.
+__global__ __launch_bounds__(256) void index_scores_f32_kernel(ScoreArgs a) {
+    extern __shared__ float smem[];
+    float *sq = smem;                           // [HI*DI]
+    float *sw = smem + a.HI * a.DI;             // [HI]
+    const int qi = blockIdx.y;
+    const int b = qi / a.T;
+    const float *qsrc = (const float *)a.q_idx + (size_t)qi * a.HI * a.DI;
+    for (int i = threadIdx.x; i < a.HI * a.DI; i += blockDim.x) sq[i] = qsrc[i];
+    for (int i = threadIdx.x; i < a.HI; i += blockDim.x) sw[i] = a.w[(size_t)qi * a.HI + i];
+    __syncthreads();
+    const int j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= a.n_max) return;
+    int nvis = visible_entries(a.seq_len[b], a.q_pos[qi], a.ratio);
+    nvis = nvis < a.n_max ? nvis : a.n_max;
+    float *dst = a.scores + (size_t)qi * a.n_max + j;
+    if (j >= nvis) {
+        *dst = -INFINITY;
+        return;
+    }
+    const float *kr = (const float *)a.k_idx[b] + (size_t)j * a.DI;
+    float s = 0.f;
+    for (int h = 0; h < a.HI; ++h) {
+        float dot = 0.f;
+        for (int d = 0; d < a.DI; ++d) dot = fmaf(sq[h * a.DI + d], kr[d], dot);
+        const float act = a.act == 0 ? fmaxf(dot, 0.f) : dot;
+        s = fmaf(sw[h], act, s);
+    }
+    *dst = s;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA decode scorer, HI = 64 heads, DI = 128.
+//
+// Per wave and step: 32 entries (two 16-entry column tiles) x 64 heads (four
+// 16-head row tiles) x 128 dims (four k-steps of 32) on
+// v_mfma_f32_16x16x32_bf16.  A = index query (heads x dims, resident in
+// registers), B = index keys (dims x entries) loaded straight from HBM.
+// The contraction order over the 128 dims is free, so lane (e, g) of a tile
+// owns dims [32g, 32g+32) of its entry: 64 contiguous bytes, and the query
+// fragments use the same dim permutation.  The C tile gives each lane 4 heads
+// of one entry; the weighted ReLU sum over those heads is done in registers
+// and the 4 lane groups are summed with two cross-lane adds.
+namespace {
+constexpr int kHI = 64;
+constexpr int kDI = 128;
+constexpr int kScoreWaves = 4;
+constexpr int kEntriesPerWaveStep = 32;
+}  // namespace
+
+__global__ __launch_bounds__(64 * kScoreWaves) void index_scores_bf16_kernel(ScoreArgs a) {
+    const int qi = blockIdx.y;
+    const int b = qi / a.T;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int e = lane & 15;   // entry (B column) / head row (A row) within a tile
+    const int g = lane >> 4;   // dim group: dims [32g, 32g + 32)
+
+    int nvis = visible_entries(a.seq_len[b], a.q_pos[qi], a.ratio);
+    nvis = nvis < a.n_max ? nvis : a.n_max;
+    const int j0 = blockIdx.x * a.chunk;
+    const int j1 = j0 + a.chunk < a.n_max ? j0 + a.chunk : a.n_max;
+    float *srow = a.scores + (size_t)qi * a.n_max;
+
+    // A fragments: head 16*ht + e, dims 32g + 8s .. +8 for k-step s.
+    bf16x8_t qa[4][4];
+    const uint16_t *qb = (const uint16_t *)a.q_idx + (size_t)qi * kHI * kDI;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            qa[ht][s] = *(const bf16x8_t *)(qb + (16 * ht + e) * kDI + 32 * g + 8 * s);
+    // Importance weights of the C-tile rows this lane holds: head 16*ht + 4g + r.
+    float wr[4][4];
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wr[ht][r] = a.w[(size_t)qi * kHI + 16 * ht + 4 * g + r];
+
+    const uint16_t *kb = (const uint16_t *)a.k_idx[b];
+    const int last = nvis > 0 ? nvis - 1 : 0;
+    for (int base = j0 + wave * kEntriesPerWaveStep; base < j1; base += kScoreWaves * kEntriesPerWaveStep) {
+        if (base >= nvis) {  // nothing visible in this step
+            if (g < 2 && base + 16 * g + e < j1) srow[base + 16 * g + e] = -INFINITY;
+            continue;
+        }
+        bf16x8_t kf[2][4];
+#pragma unroll
+        for (int et = 0; et < 2; ++et) {
+            int j = base + 16 * et + e;
+            j = j < nvis ? j : last;  // clamp: loaded but discarded
+            const uint16_t *kr = kb + (size_t)j * kDI + 32 * g;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) kf[et][s] = *(const bf16x8_t *)(kr + 8 * s);
+        }
+        float part[2];
+#pragma unroll
+        for (int et = 0; et < 2; ++et) {
+            f32x4_t acc[4];
+#pragma unroll
+            for (int ht = 0; ht < 4; ++ht) {
+                acc[ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ht][s], kf[et][s], acc[ht], 0, 0, 0);
+            }
+            float p = 0.f;
+#pragma unroll
+            for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float x = acc[ht][r];
+                    p = fmaf(wr[ht][r], a.act == 0 ? fmaxf(x, 0.f) : x, p);
+                }
+            p += __shfl_xor(p, 16);
+            p += __shfl_xor(p, 32);
+            part[et] = p;
+        }
+        // Lanes of group g < 2 store column tile g: 32 consecutive scores.
+        if (g < 2) {
+            const int j = base + 16 * g + e;
+            if (j < j1) srow[j] = j < nvis ? (g == 0 ? part[0] : part[1]) : -INFINITY;
+        }
+    }
+}
+
+hipError_t launch_index_scores(const ScoreArgs &a, int dtype, hipStream_t stream) {
+    const int Q = a.B * a.T;
+    if (dtype == kF32) {
+        dim3 grid((a.n_max + 255) / 256, Q);
+        const size_t lds = sizeof(float) * (size_t)(a.HI * a.DI + a.HI);
+        hipLaunchKernelGGL(index_scores_f32_kernel, grid, dim3(256), lds, stream, a);
+    } else {
+        dim3 grid((a.n_max + a.chunk - 1) / a.chunk, Q);
+        hipLaunchKernelGGL(index_scores_bf16_kernel, grid, dim3(64 * kScoreWaves), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+int score_chunk(int n_max, int n_queries) {
+    // Aim for ~2048 workgroups over the whole launch; multiples of one
+    // workgroup step (4 waves x 32 entries).
+    const int step = kScoreWaves * kEntriesPerWaveStep;
+    long long want = ((long long)n_max * n_queries + 2047) / 2048;
+    long long c = ((want + step - 1) / step) * step;
+    if (c < step) c = step;
+    if (c > 8192) c = 8192;
+    return (int)c;
+}
+
+}  // namespace csa

@@ -189,10 +189,12 @@ def window_span(wl: Workload, seq_len: np.ndarray, q_pos: np.ndarray):
     return pos0, rows
 
 
-def make_case(wl: Workload, with_hca: bool = True) -> Case:
+def make_case(wl: Workload, with_hca: bool = True, seq_lens=None) -> Case:
+    """Draw every tensor of a workload; `seq_lens` overrides the raw lengths."""
     s = wl.seed
     B, T, H, D, HI, DI = wl.batch, wl.q_len, wl.n_heads, wl.head_dim, wl.index_heads, wl.index_dim
-    seq_len = draw_seq_lens(wl)
+    seq_len = draw_seq_lens(wl) if seq_lens is None else np.asarray(seq_lens, dtype=np.int32).copy()
+    assert seq_len.shape == (B,)
     q_pos = query_positions(wl, seq_len)
     n_ent = seq_len // wl.ratio
     pos0, rows = window_span(wl, seq_len, q_pos)

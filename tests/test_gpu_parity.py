@@ -1,0 +1,241 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Rules: top-k computed from the same fp32 scores is bit-exact; top-k from the
+GPU's own scores matches the oracle's set except inside the 1e-3 band around
+the K-th score; attention outputs are within 1e-2 x RMS of the oracle (bf16
+inputs), evaluated on the GPU's own selected set so that legal near-tie swaps
+do not count; scores are within 1e-4 x RMS of the row.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from compressed_sparse_attention_indexer_amd import inputs
+from tests.gpu_helpers import (ATT_TOL_BF16, ATT_TOL_F32, assert_attention_close, assert_scores_close,
+                               assert_topk_band, flash_case, make_case_with_lens, nvis_of, oracle_hca,
+                               oracle_scores, oracle_sparse, say)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import compressed_sparse_attention_indexer_amd as csa  # noqa: E402
+from compressed_sparse_attention_indexer_amd.staging import DeviceCase  # noqa: E402
+
+
+def _np(t):
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy()
+
+
+def run_fused(dc, act=csa.CSA_ACT_RELU):
+    """csa_attention with the intermediate scores and indices exposed."""
+    dims = dc.csa_dims(index_act=act)
+    Q = dims.batch * dims.q_len
+    scores = torch.empty((dims.batch, dims.q_len, dims.max_entries), dtype=torch.float32, device="cuda")
+    idx = torch.empty((dims.batch, dims.q_len, dims.topk), dtype=torch.int32, device="cuda")
+    out, lse = csa.csa_attention(dims, dc.q, dc.q_idx, dc.w, dc.k_idx_p, dc.kv_p, dc.v_p, dc.win_p, dc.win_v_p,
+                                 dc.win_pos0, dc.win_rows, dc.seq_len, dc.q_pos, dc.sink, topk_idx_out=idx,
+                                 scores_out=scores)
+    assert Q == dc.case.q_pos.shape[0]
+    return _np(scores), _np(idx), _np(out), _np(lse)
+
+
+def check_whole_step(case, tol, act=csa.CSA_ACT_RELU):
+    say(f"[case] {case.wl.name} B={case.wl.batch} T={case.wl.q_len} max_entries={case.max_entries}")
+    dc = DeviceCase(case)
+    g_scores, g_idx, g_out, g_lse = run_fused(dc, act)
+    o_scores = oracle_scores(case, act=oracle.ACT_NONE if act == csa.CSA_ACT_NONE else oracle.ACT_RELU)
+    assert_scores_close(g_scores, o_scores, case)
+    o_idx = oracle.topk(o_scores, case.seq_len, case.q_pos, ratio=case.wl.ratio, k=case.wl.topk)
+    n_diff = assert_topk_band(g_idx, o_idx, o_scores, case)
+    # the top-k kernel alone, fed the oracle's scores: bit-exact
+    dims = dc.csa_dims()
+    t_idx = _np(csa.csa_topk_select(dims, torch.from_numpy(o_scores).cuda(), dc.seq_len, dc.q_pos))
+    np.testing.assert_array_equal(t_idx, o_idx)
+    # attention on the GPU's own selection
+    o_out, o_lse = oracle_sparse(case, g_idx)
+    rel = assert_attention_close(g_out, o_out, tol, "out")
+    np.testing.assert_allclose(g_lse, o_lse, atol=1e-3, rtol=0)
+    say(f"  ok: topk band swaps={n_diff} out err/rms={rel:.2e}")
+    return dc
+
+
+# --------------------------------------------------------------------------- fixture (fp32)
+
+def test_fixture_fp32_whole_step():
+    case = inputs.make_case(inputs.WORKLOADS["fixture_b2_l512_fp32"])
+    check_whole_step(case, ATT_TOL_F32)
+
+
+def test_fixture_fp32_no_activation():
+    case = inputs.make_case(inputs.WORKLOADS["fixture_b2_l512_fp32"])
+    check_whole_step(case, ATT_TOL_F32, act=csa.CSA_ACT_NONE)
+
+
+# --------------------------------------------------------------------------- Flash shapes, small
+
+@pytest.mark.parametrize("lens", [
+    [4 * 1000 + 3, 4 * 257, 130],        # several scorer steps, ragged tails
+    [4 * 3000, 4 * 700 + 1],             # n_vis > K: real selection
+    [50, 2, 4 * 128 + 2],                # L < W, p < 3 (nothing compressed), n_vis < K
+])
+def test_flash_whole_step_small(lens):
+    wl, sl = flash_case(f"flash_small_{len(lens)}_{lens[0]}", lens)
+    check_whole_step(make_case_with_lens(wl, sl), ATT_TOL_BF16)
+
+
+def test_flash_no_activation():
+    wl, sl = flash_case("flash_noact", [4 * 2000, 4 * 900])
+    check_whole_step(make_case_with_lens(wl, sl), ATT_TOL_BF16, act=csa.CSA_ACT_NONE)
+
+
+def test_flash_exact_ties_in_scores():
+    """Duplicated index keys give exact score ties across the K-th boundary."""
+    wl, sl = flash_case("flash_ties", [4 * 4096])
+    case = make_case_with_lens(wl, sl)
+    k = case.k_idx[0]
+    k[1::3] = k[0:-1:3][: len(k[1::3])]
+    k[2::3] = k[0:-2:3][: len(k[2::3])]
+    check_whole_step(case, ATT_TOL_BF16)
+
+
+def test_flash_sharp_logits_and_sink():
+    """q scaled so logits spread over several units and a large sink: exercises
+    the running max, the rescaling and the sink merge."""
+    wl, sl = flash_case("flash_sharp", [4 * 3000, 4 * 1500])
+    case = make_case_with_lens(wl, sl)
+    q = inputs.bf16_to_f32(case.q) * np.float32(60.0)
+    case.q = inputs.bf16_bits(q)
+    case.sink = (case.sink * 2 + np.float32(math.log(640))).astype(np.float32)
+    check_whole_step(case, ATT_TOL_BF16)
+
+
+# --------------------------------------------------------------------------- top-k alone (integer work: exact)
+
+def _topk_case(n_vis_list, n_max, K, seed, ties=False):
+    rng = np.random.default_rng(seed)
+    B = len(n_vis_list)
+    scores = np.full((B, 1, n_max), -np.inf, np.float32)
+    for b, nv in enumerate(n_vis_list):
+        s = rng.standard_normal(nv).astype(np.float32)
+        if ties:
+            s = np.round(s * 8) / 8
+        scores[b, 0, :nv] = s
+    seq = np.array([4 * nv for nv in n_vis_list], np.int32)
+    return scores, seq, seq - 1
+
+
+@pytest.mark.parametrize("n_vis,n_max,K,ties", [
+    ([100, 513, 600], 600, 512, False),
+    ([5000, 32768, 20000], 32768, 512, True),
+    ([32768], 32768, 2048, False),
+    ([40000, 33000], 40000, 512, False),
+    ([262144, 200000, 300, 262144], 262144, 512, True),
+    ([262144], 262144, 1, False),
+])
+def test_topk_exact(n_vis, n_max, K, ties):
+    say(f"[case] topk n_vis={n_vis} n_max={n_max} K={K} ties={ties}")
+    scores, seq, pos = _topk_case(n_vis, n_max, K, seed=len(n_vis) * 7 + K, ties=ties)
+    want = oracle.topk(scores, seq, pos, ratio=4, k=K)
+    dims = csa.make_dims(batch=len(n_vis), topk=K, max_entries=n_max)
+    got = _np(csa.csa_topk_select(dims, torch.from_numpy(scores).cuda(), torch.from_numpy(seq).cuda(),
+                                  torch.from_numpy(pos).cuda()))
+    np.testing.assert_array_equal(got, want)
+
+
+def test_topk_all_equal_scores_long_row():
+    """Every score equal: the candidate bin overflows and the exact whole-row
+    fallback must return indices 0..K-1."""
+    n = 100000
+    scores = np.full((1, 1, n), 0.25, np.float32)
+    seq = np.array([4 * n], np.int32)
+    dims = csa.make_dims(batch=1, topk=512, max_entries=n)
+    got = _np(csa.csa_topk_select(dims, torch.from_numpy(scores).cuda(), torch.from_numpy(seq).cuda(),
+                                  torch.from_numpy(seq - 1).cuda()))
+    np.testing.assert_array_equal(got[0, 0], np.arange(512))
+
+
+def test_topk_negative_zero_equals_zero():
+    scores = np.zeros((1, 1, 2000), np.float32)
+    scores[0, 0, ::2] = -0.0
+    scores[0, 0, 1500:] = -1.0
+    seq = np.array([8000], np.int32)
+    dims = csa.make_dims(batch=1, topk=512, max_entries=2000)
+    got = _np(csa.csa_topk_select(dims, torch.from_numpy(scores).cuda(), torch.from_numpy(seq).cuda(),
+                                  torch.from_numpy(seq - 1).cuda()))
+    np.testing.assert_array_equal(got[0, 0], np.arange(512))
+
+
+# --------------------------------------------------------------------------- attention alone
+
+def test_sparse_mqa_many_splits_and_padding():
+    wl, sl = flash_case("flash_attn", [4 * 2000, 4 * 300, 4 * 100 + 3])
+    case = make_case_with_lens(wl, sl)
+    say(f"[case] {wl.name}")
+    dc = DeviceCase(case)
+    o_scores = oracle_scores(case)
+    idx = oracle.topk(o_scores, case.seq_len, case.q_pos, ratio=4, k=512)
+    dims = dc.csa_dims()
+    out, lse = csa.csa_sparse_mqa_decode(dims, dc.q, dc.kv_p, None, torch.from_numpy(idx).cuda(), dc.win_p, None,
+                                         dc.win_pos0, dc.win_rows, dc.seq_len, dc.q_pos, dc.sink)
+    o_out, o_lse = oracle_sparse(case, idx)
+    assert_attention_close(_np(out), o_out, ATT_TOL_BF16, "out")
+    np.testing.assert_allclose(_np(lse), o_lse, atol=1e-3, rtol=0)
+
+
+def test_hca_small():
+    wl, sl = flash_case("hca_small", [128 * 4, 128 * 37 + 5, 100, 128 * 200], hca=128)
+    case = make_case_with_lens(wl, sl)
+    say(f"[case] {wl.name}")
+    dc = DeviceCase(case)
+    out, lse = csa.hca_mqa_decode(dc.hca_dims(), dc.hca_q, dc.hca_kv_p, None, dc.hca_win_p, None, dc.win_pos0,
+                                  dc.win_rows, dc.seq_len, dc.q_pos, dc.hca_sink)
+    o_out, o_lse = oracle_hca(case)
+    assert_attention_close(_np(out), o_out, ATT_TOL_BF16, "hca out")
+    np.testing.assert_allclose(_np(lse), o_lse, atol=1e-3, rtol=0)
+
+
+def test_deterministic_and_no_out_of_bounds_writes():
+    wl, sl = flash_case("flash_det", [4 * 5000, 4 * 1234 + 2])
+    case = make_case_with_lens(wl, sl)
+    dc = DeviceCase(case)
+    dims = dc.csa_dims()
+    guard = 4096
+    res = []
+    for _ in range(2):
+        buf = torch.full((dims.batch * 64 * 512 + 2 * guard,), 7.0, dtype=torch.float32, device="cuda")
+        out = buf[guard:guard + dims.batch * 64 * 512].view(dims.batch, 1, 64, 512)
+        ibuf = torch.full((dims.batch * 512 + 2 * guard,), 12345, dtype=torch.int32, device="cuda")
+        idx = ibuf[guard:guard + dims.batch * 512].view(dims.batch, 1, 512)
+        csa.csa_attention(dims, dc.q, dc.q_idx, dc.w, dc.k_idx_p, dc.kv_p, None, dc.win_p, None, dc.win_pos0,
+                          dc.win_rows, dc.seq_len, dc.q_pos, dc.sink, out=out, topk_idx_out=idx)
+        b, ib = _np(buf), _np(ibuf)
+        assert (b[:guard] == 7.0).all() and (b[-guard:] == 7.0).all()
+        assert (ib[:guard] == 12345).all() and (ib[-guard:] == 12345).all()
+        res.append((b.copy(), ib.copy()))
+    np.testing.assert_array_equal(res[0][0], res[1][0])
+    np.testing.assert_array_equal(res[0][1], res[1][1])
+
+
+# --------------------------------------------------------------------------- full-size workloads
+
+def test_decode_b1_64k_full():
+    check_whole_step(inputs.make_case(inputs.WORKLOADS["decode_b1_64k"]), ATT_TOL_BF16)
+
+
+def test_decode_b32_ragged_full():
+    check_whole_step(inputs.make_case(inputs.WORKLOADS["decode_b32_ragged_64k_128k"]), ATT_TOL_BF16)
+
+
+def test_decode_b4_1m_full_csa_and_hca():
+    case = inputs.make_case(inputs.WORKLOADS["decode_b4_1m"])
+    dc = check_whole_step(case, ATT_TOL_BF16)
+    say("[case] decode_b4_1m HCA layer")
+    out, lse = csa.hca_mqa_decode(dc.hca_dims(), dc.hca_q, dc.hca_kv_p, None, dc.hca_win_p, None, dc.win_pos0,
+                                  dc.win_rows, dc.seq_len, dc.q_pos, dc.hca_sink)
+    o_out, o_lse = oracle_hca(case)
+    assert_attention_close(_np(out), o_out, ATT_TOL_BF16, "hca out")
+    np.testing.assert_allclose(_np(lse), o_lse, atol=1e-3, rtol=0)
