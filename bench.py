@@ -130,7 +130,7 @@ class CsaRunner:
             self.kv_p.append(csa.ptr_array(v2, dev))
 
     def _ws(self, n):
-        return self.t.empty(max(n, 256), dtype=self.t.uint8, device="cuda")
+        return self.t.zeros(max(n, 256), dtype=self.t.uint8, device="cuda")
 
     def scores_call(self, i):
         dc = self.dc
@@ -215,7 +215,7 @@ def bench_hca(torch, csa, case, args):
     Q = d.batch * d.q_len
     out = torch.empty((d.batch, d.q_len, d.n_heads, d.head_dim), dtype=torch.float32, device="cuda")
     lse = torch.empty((d.batch, d.q_len, d.n_heads), dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(256, csa.workspace_size(d, csa._lib.CSA_OP_HCA_MQA)), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(256, csa.workspace_size(d, csa._lib.CSA_OP_HCA_MQA)), dtype=torch.uint8, device="cuda")
     copies = [dc.hca_kv_p]
     keep = []
     for _ in range(args.copies - 1):

@@ -78,7 +78,8 @@ def _ws(dims, op, workspace, device):
     if need == 0:
         return None, 0
     torch = _torch()
-    return torch.empty(need, dtype=torch.uint8, device=device), need
+    # zero-filled: the top-k counters start clean (any contents are still correct, only slower once)
+    return torch.zeros(need, dtype=torch.uint8, device=device), need
 
 
 def csa_index_scores(dims: CsaDims, q_idx, w, k_idx: PtrArg, seq_len, q_pos, scores=None, workspace=None,

@@ -375,11 +375,18 @@ csa_status csa_attention(const csa_dims *d, const void *q, const void *q_idx, co
     float *scores = scores_out ? scores_out : (float *)base;
     int32_t *idx = topk_idx_out ? topk_idx_out : (int32_t *)(base + off_idx);
     hipStream_t st = (hipStream_t)stream;
-    const csa::ScoreArgs sa = score_args(d, q_idx, w, k_idx, seq_len, q_pos, scores);
+    const csa::TopkArgs ta = topk_args(d, scores, seq_len, q_pos, idx, base + off_topk);
+    csa::ScoreArgs sa = score_args(d, q_idx, w, k_idx, seq_len, q_pos, scores);
+    // the bf16 scorer also builds the top-k key histogram while it writes the scores
+    const bool fused_hist = d->dtype == CSA_BF16 && csa::topk_uses_histogram(d->max_entries);
+    if (fused_hist) {
+        sa.hist = ta.hist;
+        sa.ctrl = ta.ctrl;
+        sa.K = d->topk;
+    }
     hipError_t e = csa::launch_index_scores(sa, d->dtype, st);
     if (e != hipSuccess) return hip_status(e, "csa_attention/scores");
-    const csa::TopkArgs ta = topk_args(d, scores, seq_len, q_pos, idx, base + off_topk);
-    e = csa::launch_topk(ta, st);
+    e = csa::launch_topk(ta, st, fused_hist);
     if (e != hipSuccess) return hip_status(e, "csa_attention/topk");
     const csa::MqaArgs ma = mqa_args(d, q, kv, v, idx, win, win_v, win_pos0, win_rows, seq_len, q_pos, sink, out, lse,
                                      base + off_mqa, d->topk + d->window);

@@ -353,12 +353,21 @@ __global__ __launch_bounds__(128) void mqa_combine_kernel(MqaArgs a) {
     if ((tid & 63) == 0) red[tid >> 6] = L;
     __syncthreads();
     L = red[0] + red[1] + exp2f(sink2 - M);
+    // sum of weighted partials; loads issued 8 splits at a time (independent),
+    // splits with zero weight (no rows) are never read
     f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < S; ++s) {
-        const float wgt = sw[s];
-        if (wgt == 0.f) continue;
-        const f32x4_t x = *(const f32x4_t *)&a.part_o[(((size_t)qi * S + s) * a.H + h) * a.D + 4 * tid];
-        acc += wgt * x;
+    const float *src = a.part_o + ((size_t)qi * S * a.H + h) * a.D + 4 * tid;
+    const size_t sstride = (size_t)a.H * a.D;
+    for (int s0 = 0; s0 < S; s0 += 8) {
+        f32x4_t x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int s = s0 + u;
+            x[u] = (s < S && sw[s] != 0.f) ? *(const f32x4_t *)(src + s * sstride) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (s0 + u < S) acc += sw[s0 + u] * x[u];
     }
     const float inv = 1.f / L;
     *(f32x4_t *)&a.out[((size_t)qi * a.H + h) * a.D + 4 * tid] = acc * inv;

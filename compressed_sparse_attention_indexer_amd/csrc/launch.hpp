@@ -19,6 +19,10 @@ struct ScoreArgs {
     float *scores;              // [Q, n_max]
     int B, T, HI, DI, ratio, act, n_max;
     int chunk;                  // entries per workgroup (bf16 kernel)
+    // optional fused top-k histogram (bf16 kernel): null to skip
+    uint32_t *hist;             // [Q, kTopkBins]
+    uint32_t *ctrl;             // [Q, kTopkCtrl]
+    int K;
 };
 
 hipError_t launch_index_scores(const ScoreArgs &a, int dtype, hipStream_t stream);
@@ -31,22 +35,25 @@ struct TopkArgs {
     int32_t *idx;               // [Q, K]
     int B, T, ratio, K, n_max;
     // multi-workgroup path scratch (inside the caller's workspace)
-    uint32_t *hist;             // [Q, kTopkBins]
-    uint32_t *counters;         // [Q, 4]
+    uint32_t *hist;             // [Q, kTopkBins] key histogram (left zero-filled after each call)
+    uint32_t *ctrl;             // [Q, kTopkCtrl] counters (left zero-filled after each call)
     int32_t *sel;               // [Q, K] entries above the threshold bin
     uint32_t *cand_key;         // [Q, kTopkCand]
     int32_t *cand_idx;          // [Q, kTopkCand]
-    int chunk;                  // entries per workgroup (multi-workgroup path)
 };
 
-constexpr int kTopkLdsCap = 32768;   // largest score row kept whole in LDS
+constexpr int kTopkSmallMax = 4096;  // rows up to this length: one workgroup per query, in LDS
 constexpr int kTopkBins = 4096;      // first-level histogram (top 12 key bits)
+constexpr int kTopkCtrl = 8;
 constexpr int kTopkCand = 8192;      // candidates kept for the final in-LDS pass
 constexpr int kTopkMaxK = 2048;
+constexpr int kTopkAuxChunk = 2048;  // scores per workgroup in the histogram and filter kernels
 
 size_t topk_workspace_bytes(int n_queries, int K, int n_max);
 void topk_carve(TopkArgs &a, void *ws, int n_queries);
-hipError_t launch_topk(const TopkArgs &a, hipStream_t stream);
+// hist_done: the scorer already built the histogram and threshold (fused path)
+hipError_t launch_topk(const TopkArgs &a, hipStream_t stream, bool hist_done = false);
+bool topk_uses_histogram(int n_max);
 
 struct MqaArgs {
     const void *q;                  // [Q, H, D]

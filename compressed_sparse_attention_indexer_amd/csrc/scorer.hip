@@ -5,6 +5,7 @@
 // DeepSeek-V4-Flash config: index_n_heads 64, index_head_dim 128).
 #include "common.hpp"
 #include "launch.hpp"
+#include "topk_hist.hpp"
 
 namespace csa {
 
@@ -47,12 +48,14 @@ __global__ __launch_bounds__(256) void index_scores_f32_kernel(ScoreArgs a) {
 // Per wave and step: 32 entries (two 16-entry column tiles) x 64 heads (four
 // 16-head row tiles) x 128 dims (four k-steps of 32) on
 // v_mfma_f32_16x16x32_bf16.  A = index query (heads x dims, resident in
-// registers), B = index keys (dims x entries) loaded straight from HBM.
-// The contraction order over the 128 dims is free, so lane (e, g) of a tile
-// owns dims [32g, 32g+32) of its entry: 64 contiguous bytes, and the query
-// fragments use the same dim permutation.  The C tile gives each lane 4 heads
-// of one entry; the weighted ReLU sum over those heads is done in registers
-// and the 4 lane groups are summed with two cross-lane adds.
+// registers), B = index keys (dims x entries) loaded straight from HBM into
+// registers, one step ahead of the step being computed.  Lane (e, g) of a
+// tile holds dims [32s + 8g, 32s + 8g + 8) of entry e for k-step s, so each
+// load instruction reads 64 contiguous bytes of every entry it touches.  The
+// C tile gives each lane 4 heads of one entry; the weighted ReLU sum over
+// those heads is done in registers and the 4 lane groups are summed with two
+// cross-lane adds.  Optionally the workgroup also histograms the keys of the
+// scores it writes for the multi-workgroup top-k.
 namespace {
 constexpr int kHI = 64;
 constexpr int kDI = 128;
@@ -61,27 +64,35 @@ constexpr int kEntriesPerWaveStep = 32;
 }  // namespace
 
 __global__ __launch_bounds__(64 * kScoreWaves) void index_scores_bf16_kernel(ScoreArgs a) {
+    __shared__ uint32_t lh[kTopkBins];
+    __shared__ int s_flag;
+    __shared__ uint32_t s_wsum[4];
     const int qi = blockIdx.y;
     const int b = qi / a.T;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int e = lane & 15;   // entry (B column) / head row (A row) within a tile
-    const int g = lane >> 4;   // dim group: dims [32g, 32g + 32)
+    const int g = lane >> 4;   // dim group within a k-step
 
     int nvis = visible_entries(a.seq_len[b], a.q_pos[qi], a.ratio);
     nvis = nvis < a.n_max ? nvis : a.n_max;
+    const bool with_hist = a.hist != nullptr && nvis > a.K;  // same for the whole workgroup
+    if (with_hist)
+        for (int i = threadIdx.x; i < kTopkBins; i += 64 * kScoreWaves) lh[i] = 0u;
+    __syncthreads();
     const int j0 = blockIdx.x * a.chunk;
     const int j1 = j0 + a.chunk < a.n_max ? j0 + a.chunk : a.n_max;
+    const int lim = j1 < nvis ? j1 : nvis;
     float *srow = a.scores + (size_t)qi * a.n_max;
 
-    // A fragments: head 16*ht + e, dims 32g + 8s .. +8 for k-step s.
+    // A fragments: head 16*ht + e, dims 32s + 8g .. +8 for k-step s.
     bf16x8_t qa[4][4];
     const uint16_t *qb = (const uint16_t *)a.q_idx + (size_t)qi * kHI * kDI;
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-            qa[ht][s] = *(const bf16x8_t *)(qb + (16 * ht + e) * kDI + 32 * g + 8 * s);
+            qa[ht][s] = *(const bf16x8_t *)(qb + (16 * ht + e) * kDI + 32 * s + 8 * g);
     // Importance weights of the C-tile rows this lane holds: head 16*ht + 4g + r.
     float wr[4][4];
 #pragma unroll
@@ -91,19 +102,21 @@ __global__ __launch_bounds__(64 * kScoreWaves) void index_scores_bf16_kernel(Sco
 
     const uint16_t *kb = (const uint16_t *)a.k_idx[b];
     const int last = nvis > 0 ? nvis - 1 : 0;
-    for (int base = j0 + wave * kEntriesPerWaveStep; base < j1; base += kScoreWaves * kEntriesPerWaveStep) {
-        if (base >= nvis) {  // nothing visible in this step
-            if (g < 2 && base + 16 * g + e < j1) srow[base + 16 * g + e] = -INFINITY;
-            continue;
-        }
-        bf16x8_t kf[2][4];
+    auto load = [&](bf16x8_t (&kf)[2][4], int base) {
 #pragma unroll
         for (int et = 0; et < 2; ++et) {
             int j = base + 16 * et + e;
             j = j < nvis ? j : last;  // clamp: loaded but discarded
-            const uint16_t *kr = kb + (size_t)j * kDI + 32 * g;
+            const uint16_t *kr = kb + (size_t)j * kDI + 8 * g;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) kf[et][s] = *(const bf16x8_t *)(kr + 8 * s);
+            for (int s = 0; s < 4; ++s) kf[et][s] = *(const bf16x8_t *)(kr + 32 * s);
+        }
+    };
+    auto process = [&](const bf16x8_t (&kf)[2][4], int base) {
+        const int j = base + 16 * g + e;  // entry this lane stores (g < 2)
+        if (base >= nvis) {  // nothing visible in this step
+            if (g < 2 && j < j1) srow[j] = -INFINITY;
+            return;
         }
         float part[2];
 #pragma unroll
@@ -129,11 +142,27 @@ __global__ __launch_bounds__(64 * kScoreWaves) void index_scores_bf16_kernel(Sco
             part[et] = p;
         }
         // Lanes of group g < 2 store column tile g: 32 consecutive scores.
-        if (g < 2) {
-            const int j = base + 16 * g + e;
-            if (j < j1) srow[j] = j < nvis ? (g == 0 ? part[0] : part[1]) : -INFINITY;
+        if (g < 2 && j < j1) {
+            const float sv = j < nvis ? (g == 0 ? part[0] : part[1]) : -INFINITY;
+            srow[j] = sv;
+            if (with_hist && j < nvis) atomicAdd(&lh[order_key(sv) >> 20], 1u);
         }
+    };
+
+    constexpr int kStride = kScoreWaves * kEntriesPerWaveStep;
+    bf16x8_t ka[2][4], kc[2][4];
+    int base = j0 + wave * kEntriesPerWaveStep;
+    if (base < lim) load(ka, base);
+    for (; base < j1; base += 2 * kStride) {
+        const int b1 = base + kStride, b2 = base + 2 * kStride;
+        if (b1 < lim) load(kc, b1);
+        process(ka, base);
+        if (b2 < lim) load(ka, b2);
+        if (b1 < j1) process(kc, b1);
     }
+    if (with_hist)
+        hist_publish(lh, a.hist + (size_t)qi * kTopkBins, a.ctrl + (size_t)qi * kTopkCtrl, nvis, a.K, gridDim.x,
+                     &s_flag, s_wsum);
 }
 
 hipError_t launch_index_scores(const ScoreArgs &a, int dtype, hipStream_t stream) {
@@ -150,10 +179,10 @@ hipError_t launch_index_scores(const ScoreArgs &a, int dtype, hipStream_t stream
 }
 
 int score_chunk(int n_max, int n_queries) {
-    // Aim for ~2048 workgroups over the whole launch; multiples of one
-    // workgroup step (4 waves x 32 entries).
-    const int step = kScoreWaves * kEntriesPerWaveStep;
-    long long want = ((long long)n_max * n_queries + 2047) / 2048;
+    // Aim for ~1024 workgroups over the whole launch; multiples of two
+    // workgroup steps (4 waves x 32 entries, double-buffered).
+    const int step = 2 * kScoreWaves * kEntriesPerWaveStep;
+    long long want = ((long long)n_max * n_queries + 1023) / 1024;
     long long c = ((want + step - 1) / step) * step;
     if (c < step) c = step;
     if (c > 8192) c = 8192;

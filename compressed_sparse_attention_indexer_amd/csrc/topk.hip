@@ -8,14 +8,21 @@
 //    the row in LDS, finds the exact K-th key with four 8-bit radix passes,
 //    then writes the selection in index order with an ordered compaction
 //    (wave ballots + cross-wave prefix counts), taking equal keys by index.
-//  * longer rows: many workgroups per query build a 12-bit key histogram,
-//    one small kernel locates the bin holding the K-th key, many workgroups
-//    copy out the entries above that bin and the candidates inside it, and a
-//    final workgroup selects among the candidates by (key, -index) and sorts
-//    the K indices.  If the bin is larger than the candidate buffer, the final
-//    workgroup falls back to the exact one-workgroup scan of the whole row.
+//  * longer rows: many workgroups per query build a 12-bit key histogram (or
+//    the scorer builds it while writing the scores); the last workgroup of
+//    each query locates the bin holding the K-th key.  Many workgroups then
+//    copy out the entries above that bin and the candidates inside it.  One
+//    workgroup per query refines the candidates with a second 12-bit
+//    histogram, breaks the remaining ties by (key, -index), and writes the K
+//    indices in ascending order through an LDS bitmap.  Before using the
+//    candidates it checks that the counts are consistent (entries above the
+//    bin < K <= above + candidates, every candidate kept); otherwise it runs
+//    the exact one-workgroup scan of the whole row.  Correctness therefore
+//    never depends on the workspace's prior contents; the kernels leave the
+//    histogram and counters zero-filled, which makes the next call fast.
 #include "common.hpp"
 #include "launch.hpp"
+#include "topk_hist.hpp"
 
 namespace csa {
 
@@ -149,7 +156,7 @@ __device__ __forceinline__ int query_visible(const TopkArgs &a, int qi) {
 }  // namespace
 
 __global__ __launch_bounds__(kWG) void topk_lds_kernel(TopkArgs a) {
-    __shared__ uint32_t keys[kTopkLdsCap];
+    __shared__ uint32_t keys[kTopkSmallMax];
     __shared__ TopkShared sh;
     const int qi = blockIdx.x;
     topk_row<true>(a.scores + (size_t)qi * a.n_max, query_visible(a, qi), a.K, a.idx + (size_t)qi * a.K,
@@ -159,99 +166,64 @@ __global__ __launch_bounds__(kWG) void topk_lds_kernel(TopkArgs a) {
 // ---------------------------------------------------------------------------
 // Multi-workgroup path.
 
-__global__ __launch_bounds__(kAuxThreads) void topk_clear_kernel(TopkArgs a, int n_queries) {
-    const size_t n_hist = (size_t)n_queries * kTopkBins;
-    const size_t n_cnt = (size_t)n_queries * 4;
-    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n_hist + n_cnt;
-         i += (size_t)gridDim.x * blockDim.x) {
-        if (i < n_hist)
-            a.hist[i] = 0u;
-        else
-            a.counters[i - n_hist] = 0u;
-    }
-}
+namespace {
+constexpr int kPerThread = kTopkAuxChunk / kAuxThreads;  // 8 scores per thread
+constexpr int kSubCap = 1024;                            // second-level tie candidates
+constexpr int kBitmapMaxN = 262144;                      // LDS bitmap ordering up to this row length
+}  // namespace
 
 __global__ __launch_bounds__(kAuxThreads) void topk_hist_kernel(TopkArgs a) {
     __shared__ uint32_t lh[kTopkBins];
+    __shared__ int s_flag;
+    __shared__ uint32_t s_wsum[4];
     const int qi = blockIdx.y;
     const int n = query_visible(a, qi);
-    if (n <= a.K) return;
+    if (n <= a.K) return;  // the same for every workgroup of this query
     for (int i = threadIdx.x; i < kTopkBins; i += kAuxThreads) lh[i] = 0u;
     __syncthreads();
     const float *row = a.scores + (size_t)qi * a.n_max;
-    const int j0 = blockIdx.x * a.chunk;
-    const int j1 = j0 + a.chunk < n ? j0 + a.chunk : n;
-    for (int j = j0 + threadIdx.x; j < j1; j += kAuxThreads) atomicAdd(&lh[order_key(row[j]) >> 20], 1u);
-    __syncthreads();
-    uint32_t *gh = a.hist + (size_t)qi * kTopkBins;
-    for (int i = threadIdx.x; i < kTopkBins; i += kAuxThreads)
-        if (lh[i]) atomicAdd(&gh[i], lh[i]);
+    const int j0 = blockIdx.x * kTopkAuxChunk + kPerThread * threadIdx.x;
+    float v[kPerThread];
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) v[k] = j0 + k < n ? row[j0 + k] : 0.f;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k)
+        if (j0 + k < n) atomicAdd(&lh[order_key(v[k]) >> 20], 1u);
+    hist_publish(lh, a.hist + (size_t)qi * kTopkBins, a.ctrl + (size_t)qi * kTopkCtrl, n, a.K, gridDim.x,
+                 &s_flag, s_wsum);
 }
 
-// counters[q] = {threshold bin, rank needed inside it, #above, #candidates}
-__global__ __launch_bounds__(kAuxThreads) void topk_thresh_kernel(TopkArgs a) {
-    __shared__ uint32_t wsum[kAuxThreads / 64];
-    const int qi = blockIdx.x;
-    const int n = query_visible(a, qi);
-    if (n <= a.K) return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    constexpr int kPer = kTopkBins / kAuxThreads;  // 16 bins per thread
-    const uint32_t *gh = a.hist + (size_t)qi * kTopkBins;
-    uint32_t h[kPer];
-    uint32_t s = 0;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        h[i] = gh[kPer * tid + i];
-        s += h[i];
-    }
-    uint32_t suf = s;  // suffix sum within the wave
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t t = __shfl_down(suf, o);
-        if (lane + o < 64) suf += t;
-    }
-    if (lane == 0) wsum[wave] = suf;
-    __syncthreads();
-    for (int w = wave + 1; w < kAuxThreads / 64; ++w) suf += wsum[w];
-    const uint32_t above = suf - s;
-    const uint32_t need = (uint32_t)a.K;
-    if (above < need && need <= suf) {
-        uint32_t acc = above;
-        for (int i = kPer - 1; i >= 0; --i) {
-            if (acc < need && need <= acc + h[i]) {
-                a.counters[(size_t)qi * 4 + 0] = (uint32_t)(kPer * tid + i);
-                a.counters[(size_t)qi * 4 + 1] = need - acc;
-                break;
-            }
-            acc += h[i];
-        }
-    }
-}
-
+// Entries whose 12-bit key digit is above the threshold bin -> sel[], inside
+// it -> candidates.  Slots are reserved with one atomic per list per
+// workgroup; every write is bounded by its buffer.
 __global__ __launch_bounds__(kAuxThreads) void topk_filter_kernel(TopkArgs a) {
-    constexpr int kMaxChunk = 2048;
-    __shared__ int32_t l_sel[kMaxChunk];
-    __shared__ int32_t l_cidx[kMaxChunk];
-    __shared__ uint32_t l_ckey[kMaxChunk];
+    __shared__ int32_t l_sel[kTopkAuxChunk];
+    __shared__ int32_t l_cidx[kTopkAuxChunk];
+    __shared__ uint32_t l_ckey[kTopkAuxChunk];
     __shared__ int l_cnt[2];
     __shared__ int l_base[2];
     const int qi = blockIdx.y;
     const int n = query_visible(a, qi);
     if (n <= a.K) return;
-    const uint32_t bin = a.counters[(size_t)qi * 4 + 0];
+    uint32_t *ctrl = a.ctrl + (size_t)qi * kTopkCtrl;
+    const uint32_t bin = ctrl[kCtrlBin];
+    if (bin >= (uint32_t)kTopkBins) return;
     if (threadIdx.x < 2) l_cnt[threadIdx.x] = 0;
     __syncthreads();
     const float *row = a.scores + (size_t)qi * a.n_max;
-    const int j0 = blockIdx.x * a.chunk;
-    const int j1 = j0 + a.chunk < n ? j0 + a.chunk : n;
+    const int j0 = blockIdx.x * kTopkAuxChunk + kPerThread * threadIdx.x;
+    float v[kPerThread];
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) v[k] = j0 + k < n ? row[j0 + k] : 0.f;
     const uint64_t lt = lanemask_lt();
     const int lane = threadIdx.x & 63;
-    for (int jb = j0; jb < j1; jb += kAuxThreads) {
-        const int j = jb + threadIdx.x;
-        const uint32_t k = j < j1 ? order_key(row[j]) : 0u;
-        const uint32_t d = k >> 20;
-        const bool gt = j < j1 && d > bin;
-        const bool eq = j < j1 && d == bin;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+        const int j = j0 + k;
+        const uint32_t key = order_key(v[k]);
+        const uint32_t d = key >> 20;
+        const bool gt = j < n && d > bin;
+        const bool eq = j < n && d == bin;
         const uint64_t mg = __ballot(gt), me = __ballot(eq);
         if (mg) {
             int base = 0;
@@ -265,17 +237,16 @@ __global__ __launch_bounds__(kAuxThreads) void topk_filter_kernel(TopkArgs a) {
             base = __shfl(base, 0);
             if (eq) {
                 l_cidx[base + __popcll(me & lt)] = j;
-                l_ckey[base + __popcll(me & lt)] = k;
+                l_ckey[base + __popcll(me & lt)] = key;
             }
         }
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        l_base[0] = l_cnt[0] ? (int)atomicAdd(&a.counters[(size_t)qi * 4 + 2], (uint32_t)l_cnt[0]) : 0;
-        l_base[1] = l_cnt[1] ? (int)atomicAdd(&a.counters[(size_t)qi * 4 + 3], (uint32_t)l_cnt[1]) : 0;
+        l_base[0] = l_cnt[0] ? (int)atomicAdd(&ctrl[kCtrlAbove], (uint32_t)l_cnt[0]) : 0;
+        l_base[1] = l_cnt[1] ? (int)atomicAdd(&ctrl[kCtrlCand], (uint32_t)l_cnt[1]) : 0;
     }
     __syncthreads();
-    // entries above the threshold bin: fewer than K in total
     for (int i = threadIdx.x; i < l_cnt[0]; i += kAuxThreads) {
         const int slot = l_base[0] + i;
         if (slot < a.K) a.sel[(size_t)qi * a.K + slot] = l_sel[i];
@@ -289,100 +260,203 @@ __global__ __launch_bounds__(kAuxThreads) void topk_filter_kernel(TopkArgs a) {
     }
 }
 
+namespace {
+// Block-wide exclusive prefix sum over 1024 threads (one value each).
+__device__ __forceinline__ int block_exclusive_scan(int x, int *s_wave, int *total) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int inc = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(inc, o);
+        if (lane >= o) inc += t;
+    }
+    if (lane == 63) s_wave[wave] = inc;
+    __syncthreads();
+    int before = 0, all = 0;
+    for (int w = 0; w < kWaves; ++w) {
+        const int c = s_wave[w];
+        before += w < wave ? c : 0;
+        all += c;
+    }
+    __syncthreads();
+    *total = all;
+    return before + inc - x;
+}
+}  // namespace
+
+// One workgroup per query: candidates -> exact selection -> ascending output.
 __global__ __launch_bounds__(kWG) void topk_final_kernel(TopkArgs a) {
     __shared__ uint32_t c_key[kTopkCand];
-    __shared__ uint32_t c_nidx[kTopkCand];  // ~index: larger means lower index
+    __shared__ int32_t c_idx[kTopkCand];
+    __shared__ uint32_t bits[kBitmapMaxN / 32];  // also the second-level histogram
+    __shared__ uint32_t sub_key[kSubCap];
+    __shared__ int32_t sub_idx[kSubCap];
     __shared__ int32_t v[kTopkMaxK];
     __shared__ TopkShared sh;
+    __shared__ int s_wave[kWaves];
+    __shared__ int s_cnt[2];
     const int qi = blockIdx.x;
     const int tid = threadIdx.x;
     const int n = query_visible(a, qi);
+    const int K = a.K;
     const float *row = a.scores + (size_t)qi * a.n_max;
-    int32_t *out = a.idx + (size_t)qi * a.K;
-    if (n <= a.K) {
-        for (int i = tid; i < a.K; i += kWG) out[i] = i < n ? i : -1;
+    int32_t *out = a.idx + (size_t)qi * K;
+    if (n <= K) {
+        for (int i = tid; i < K; i += kWG) out[i] = i < n ? i : -1;
         return;
     }
-    const int need0 = (int)a.counters[(size_t)qi * 4 + 1];
-    const int n_above = (int)a.counters[(size_t)qi * 4 + 2];
-    const int n_cand = (int)a.counters[(size_t)qi * 4 + 3];
-    if (n_cand > kTopkCand || n_above + need0 != a.K) {  // bin too large: exact whole-row scan
-        topk_row<false>(row, n, a.K, out, nullptr, sh);
+    uint32_t *ctrl = a.ctrl + (size_t)qi * kTopkCtrl;
+    const uint32_t bin = ctrl[kCtrlBin];
+    const int n_above = (int)ctrl[kCtrlAbove];
+    const int n_cand = (int)ctrl[kCtrlCand];
+    __syncthreads();
+    if (tid == 0) {  // leave the counters zero-filled for the next call
+        ctrl[kCtrlDone] = 0u;
+        ctrl[kCtrlAbove] = 0u;
+        ctrl[kCtrlCand] = 0u;
+    }
+    const int need = K - n_above;
+    const bool fast = bin < (uint32_t)kTopkBins && n_above >= 0 && n_above < K && n_cand <= kTopkCand &&
+                      n_above + n_cand >= K;
+    if (!fast) {
+        topk_row<false>(row, n, K, out, nullptr, sh);
         return;
     }
+    uint32_t *h2 = bits;  // 4096-bin histogram of key bits [19:8]
+    for (int i = tid; i < kTopkBins; i += kWG) h2[i] = 0u;
+    if (tid < 2) s_cnt[tid] = 0;
+    for (int i = tid; i < n_above; i += kWG) v[i] = a.sel[(size_t)qi * K + i];
     for (int i = tid; i < n_cand; i += kWG) {
         c_key[i] = a.cand_key[(size_t)qi * kTopkCand + i];
-        c_nidx[i] = ~(uint32_t)a.cand_idx[(size_t)qi * kTopkCand + i];
+        c_idx[i] = a.cand_idx[(size_t)qi * kTopkCand + i];
     }
-    for (int i = tid; i < n_above; i += kWG) v[i] = a.sel[(size_t)qi * a.K + i];
-    if (tid == 0) sh.count = 0;
     __syncthreads();
-    // need0-th largest composite (key, ~index) among the candidates; composites are unique.
-    uint64_t prefix = 0;
-    int need = need0;
-    for (int pass = 0; pass < 8; ++pass) {
-        const int shift = 56 - 8 * pass;
-        const uint64_t hi_mask = pass == 0 ? 0ull : (~0ull << (shift + 8));
-        if (tid < 256) sh.hist[tid] = 0;
-        __syncthreads();
-        for (int i = tid; i < n_cand; i += kWG) {
-            const uint64_t c = ((uint64_t)c_key[i] << 32) | c_nidx[i];
-            if ((c & hi_mask) == prefix) atomicAdd(&sh.hist[(c >> shift) & 255u], 1u);
-        }
-        __syncthreads();
-        find_bin_256(sh, need);
-        __syncthreads();
-        prefix |= (uint64_t)sh.bcast[0] << shift;
-        need = sh.bcast[1];
-        __syncthreads();
+    for (int i = tid; i < n_cand; i += kWG) atomicAdd(&h2[(c_key[i] >> 8) & 0xFFFu], 1u);
+    __syncthreads();
+    // bin b2 of the need-th largest candidate: 4 bins per thread, suffix sums
+    uint32_t hh[4], s = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        hh[i] = h2[4 * tid + i];
+        s += hh[i];
     }
-    for (int i = tid; i < n_cand; i += kWG) {
-        const uint64_t c = ((uint64_t)c_key[i] << 32) | c_nidx[i];
-        if (c >= prefix) {
-            const int slot = atomicAdd(&sh.count, 1);
-            if (slot < need0) v[n_above + slot] = (int32_t)~c_nidx[i];
-        }
-    }
-    // bitonic sort of the K indices (padded to a power of two)
-    int P = 1;
-    while (P < a.K) P <<= 1;
-    __syncthreads();
-    for (int i = a.K + tid; i < P; i += kWG) v[i] = 0x7FFFFFFF;
-    __syncthreads();
-    for (int size = 2; size <= P; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int t = tid; t < P / 2; t += kWG) {
-                const int i = (t / stride) * stride * 2 + (t % stride);
-                const int j = i + stride;
-                const bool asc = (i & size) == 0;
-                const int32_t x = v[i], y = v[j];
-                if ((x > y) == asc) {
-                    v[i] = y;
-                    v[j] = x;
-                }
+    int tot;
+    const int pre = block_exclusive_scan((int)s, s_wave, &tot);  // bins below this thread
+    const int above_me = tot - pre - (int)s;                       // bins above this thread
+    if (above_me < need && need <= above_me + (int)s) {
+        int acc = above_me;
+        for (int i = 3; i >= 0; --i) {
+            if (acc < need && need <= acc + (int)hh[i]) {
+                sh.bcast[0] = 4 * tid + i;
+                sh.bcast[1] = need - acc;
+                break;
             }
-            __syncthreads();
+            acc += (int)hh[i];
         }
     }
-    for (int i = tid; i < a.K; i += kWG) out[i] = v[i];
+    __syncthreads();
+    const uint32_t b2 = (uint32_t)sh.bcast[0];
+    const int need2 = sh.bcast[1];
+    // above b2: selected; inside b2: ties to resolve by (key, -index)
+    for (int i = tid; i < n_cand; i += kWG) {
+        const uint32_t d2 = (c_key[i] >> 8) & 0xFFFu;
+        if (d2 > b2) {
+            const int slot = n_above + atomicAdd(&s_cnt[0], 1);
+            if (slot < K) v[slot] = c_idx[i];
+        } else if (d2 == b2) {
+            const int slot = atomicAdd(&s_cnt[1], 1);
+            if (slot < kSubCap) {
+                sub_key[slot] = c_key[i];
+                sub_idx[slot] = c_idx[i];
+            }
+        }
+    }
+    __syncthreads();
+    const int n_hi = s_cnt[0], m2 = s_cnt[1];
+    if (m2 > kSubCap || n_above + n_hi + need2 != K) {  // not expected; stay exact
+        __syncthreads();
+        topk_row<false>(row, n, K, out, nullptr, sh);
+        return;
+    }
+    for (int t = tid; t < m2; t += kWG) {
+        const uint64_t mine = ((uint64_t)sub_key[t] << 32) | (uint32_t)~(uint32_t)sub_idx[t];
+        int rank = 0;
+        for (int u = 0; u < m2; ++u) {
+            const uint64_t other = ((uint64_t)sub_key[u] << 32) | (uint32_t)~(uint32_t)sub_idx[u];
+            rank += other > mine;
+        }
+        if (rank < need2) v[n_above + n_hi + rank] = sub_idx[t];
+    }
+    __syncthreads();
+    // ascending order
+    if (n <= kBitmapMaxN) {
+        const int n_words = (n + 31) >> 5;
+        for (int i = tid; i < n_words; i += kWG) bits[i] = 0u;
+        __syncthreads();
+        for (int i = tid; i < K; i += kWG) atomicOr(&bits[v[i] >> 5], 1u << (v[i] & 31));
+        __syncthreads();
+        constexpr int kWordsPerThread = kBitmapMaxN / 32 / kWG;  // 8
+        uint32_t wv[kWordsPerThread];
+        int cnt = 0;
+#pragma unroll
+        for (int k = 0; k < kWordsPerThread; ++k) {
+            const int wi = kWordsPerThread * tid + k;
+            wv[k] = wi < n_words ? bits[wi] : 0u;
+            cnt += __popc(wv[k]);
+        }
+        int pos = block_exclusive_scan(cnt, s_wave, &tot);
+#pragma unroll
+        for (int k = 0; k < kWordsPerThread; ++k) {
+            uint32_t w = wv[k];
+            while (w) {
+                const int b = __ffs(w) - 1;
+                if (pos < K) out[pos] = 32 * (kWordsPerThread * tid + k) + b;
+                ++pos;
+                w &= w - 1u;
+            }
+        }
+    } else {
+        int P = 1;
+        while (P < K) P <<= 1;
+        for (int i = K + tid; i < P; i += kWG) v[i] = 0x7FFFFFFF;
+        __syncthreads();
+        for (int size = 2; size <= P; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                for (int t = tid; t < P / 2; t += kWG) {
+                    const int i = (t / stride) * stride * 2 + (t % stride);
+                    const int j = i + stride;
+                    const bool asc = (i & size) == 0;
+                    const int32_t x = v[i], y = v[j];
+                    if ((x > y) == asc) {
+                        v[i] = y;
+                        v[j] = x;
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        for (int i = tid; i < K; i += kWG) out[i] = v[i];
+    }
 }
 
+bool topk_uses_histogram(int n_max) { return n_max > kTopkSmallMax; }
+
 size_t topk_workspace_bytes(int n_queries, int K, int n_max) {
-    if (n_max <= kTopkLdsCap) return 0;
+    if (!topk_uses_histogram(n_max)) return 0;
     const size_t Q = (size_t)n_queries;
-    return Q * kTopkBins * 4 + Q * 4 * 4 + Q * (size_t)K * 4 + Q * kTopkCand * 8 + 256;
+    return Q * kTopkBins * 4 + Q * kTopkCtrl * 4 + Q * (size_t)K * 4 + Q * kTopkCand * 8 + 256;
 }
 
 static inline char *align256(char *p) { return (char *)(((uintptr_t)p + 255) & ~(uintptr_t)255); }
 
 void topk_carve(TopkArgs &a, void *ws, int n_queries) {
-    if (a.n_max <= kTopkLdsCap) return;
+    if (!topk_uses_histogram(a.n_max)) return;
     const size_t Q = (size_t)n_queries;
     char *p = align256((char *)ws);
     a.hist = (uint32_t *)p;
     p += Q * kTopkBins * 4;
-    a.counters = (uint32_t *)p;
-    p += Q * 4 * 4;
+    a.ctrl = (uint32_t *)p;
+    p += Q * kTopkCtrl * 4;
     a.sel = (int32_t *)p;
     p += Q * (size_t)a.K * 4;
     a.cand_key = (uint32_t *)p;
@@ -390,21 +464,14 @@ void topk_carve(TopkArgs &a, void *ws, int n_queries) {
     a.cand_idx = (int32_t *)p;
 }
 
-hipError_t launch_topk(const TopkArgs &a0, hipStream_t stream) {
-    const int Q = a0.B * a0.T;
-    if (a0.n_max <= kTopkLdsCap) {
-        hipLaunchKernelGGL(topk_lds_kernel, dim3(Q), dim3(kWG), 0, stream, a0);
+hipError_t launch_topk(const TopkArgs &a, hipStream_t stream, bool hist_done) {
+    const int Q = a.B * a.T;
+    if (!topk_uses_histogram(a.n_max)) {
+        hipLaunchKernelGGL(topk_lds_kernel, dim3(Q), dim3(kWG), 0, stream, a);
         return hipGetLastError();
     }
-    TopkArgs a = a0;
-    a.chunk = 2048;
-    const int n_chunks = (a.n_max + a.chunk - 1) / a.chunk;
-    const size_t clear_n = (size_t)Q * (kTopkBins + 4);
-    int clear_blocks = (int)((clear_n + kAuxThreads - 1) / kAuxThreads);
-    clear_blocks = clear_blocks < 4096 ? clear_blocks : 4096;
-    hipLaunchKernelGGL(topk_clear_kernel, dim3(clear_blocks), dim3(kAuxThreads), 0, stream, a, Q);
-    hipLaunchKernelGGL(topk_hist_kernel, dim3(n_chunks, Q), dim3(kAuxThreads), 0, stream, a);
-    hipLaunchKernelGGL(topk_thresh_kernel, dim3(Q), dim3(kAuxThreads), 0, stream, a);
+    const int n_chunks = (a.n_max + kTopkAuxChunk - 1) / kTopkAuxChunk;
+    if (!hist_done) hipLaunchKernelGGL(topk_hist_kernel, dim3(n_chunks, Q), dim3(kAuxThreads), 0, stream, a);
     hipLaunchKernelGGL(topk_filter_kernel, dim3(n_chunks, Q), dim3(kAuxThreads), 0, stream, a);
     hipLaunchKernelGGL(topk_final_kernel, dim3(Q), dim3(kWG), 0, stream, a);
     return hipGetLastError();

@@ -149,8 +149,9 @@ def test_workspace_checks():
 
 
 def test_workspace_sizes():
-    # short rows are selected in LDS: no workspace
-    assert csa.workspace_size(_flash(max_entries=32768), _lib.CSA_OP_TOPK) == 0
+    # short rows are selected by one workgroup in LDS: no workspace
+    assert csa.workspace_size(_flash(max_entries=4096), _lib.CSA_OP_TOPK) == 0
+    assert csa.workspace_size(_flash(max_entries=4097), _lib.CSA_OP_TOPK) > 0
     assert csa.workspace_size(_fixture(), _lib.CSA_OP_ATTENTION) >= 2 * 128 * 4 + 2 * 32 * 4
     big = csa.workspace_size(_flash(max_entries=262144), _lib.CSA_OP_ATTENTION)
     assert big >= 4 * 262144 * 4 + 4 * 512 * 4

@@ -158,6 +158,39 @@ def test_topk_all_equal_scores_long_row():
     np.testing.assert_array_equal(got[0, 0], np.arange(512))
 
 
+@pytest.mark.parametrize("fill", [0xFF, 0x01, None])
+def test_topk_any_workspace_contents_stay_exact(fill):
+    """The multi-workgroup top-k keeps its histogram and counters in the
+    workspace; whatever the workspace holds, results are exact, and the call
+    leaves it clean for the next one."""
+    scores, seq, pos = _topk_case([262144, 50000, 300], 262144, 512, seed=5, ties=True)
+    want = oracle.topk(scores, seq, pos, ratio=4, k=512)
+    dims = csa.make_dims(batch=3, topk=512, max_entries=262144)
+    n = csa.workspace_size(dims, csa._lib.CSA_OP_TOPK)
+    if fill is None:
+        ws = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda")
+    else:
+        ws = torch.full((n,), fill, dtype=torch.uint8, device="cuda")
+    sc, sq, ps = (torch.from_numpy(x).cuda() for x in (scores, seq, pos))
+    for call in range(3):
+        say(f"[case] dirty workspace fill={fill} call={call}")
+        got = _np(csa.csa_topk_select(dims, sc, sq, ps, workspace=ws))
+        np.testing.assert_array_equal(got, want)
+
+
+def test_fused_selection_equals_standalone_topk():
+    wl, sl = flash_case("flash_fused_vs_standalone", [4 * 40000, 4 * 9000, 4 * 20000 + 1])
+    case = make_case_with_lens(wl, sl)
+    say(f"[case] {wl.name}")
+    dc = DeviceCase(case)
+    g_scores, g_idx, _, _ = run_fused(dc)
+    dims = dc.csa_dims()
+    t_idx = _np(csa.csa_topk_select(dims, torch.from_numpy(g_scores).cuda(), dc.seq_len, dc.q_pos))
+    np.testing.assert_array_equal(t_idx, g_idx)
+    want = oracle.topk(g_scores, case.seq_len, case.q_pos, ratio=4, k=512)
+    np.testing.assert_array_equal(g_idx, want)
+
+
 def test_topk_negative_zero_equals_zero():
     scores = np.zeros((1, 1, 2000), np.float32)
     scores[0, 0, ::2] = -0.0
