@@ -77,8 +77,10 @@ __global__ __launch_bounds__(64 * kScoreWaves) void index_scores_bf16_kernel(Sco
     int nvis = visible_entries(a.seq_len[b], a.q_pos[qi], a.ratio);
     nvis = nvis < a.n_max ? nvis : a.n_max;
     const bool with_hist = a.hist != nullptr && nvis > a.K;  // same for the whole workgroup
-    if (with_hist)
+    if (with_hist) {
+        hist_begin(a.ctrl + (size_t)qi * kTopkCtrl);
         for (int i = threadIdx.x; i < kTopkBins; i += 64 * kScoreWaves) lh[i] = 0u;
+    }
     __syncthreads();
     const int j0 = blockIdx.x * a.chunk;
     const int j1 = j0 + a.chunk < a.n_max ? j0 + a.chunk : a.n_max;

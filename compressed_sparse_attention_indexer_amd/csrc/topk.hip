@@ -179,6 +179,7 @@ __global__ __launch_bounds__(kAuxThreads) void topk_hist_kernel(TopkArgs a) {
     const int qi = blockIdx.y;
     const int n = query_visible(a, qi);
     if (n <= a.K) return;  // the same for every workgroup of this query
+    hist_begin(a.ctrl + (size_t)qi * kTopkCtrl);
     for (int i = threadIdx.x; i < kTopkBins; i += kAuxThreads) lh[i] = 0u;
     __syncthreads();
     const float *row = a.scores + (size_t)qi * a.n_max;

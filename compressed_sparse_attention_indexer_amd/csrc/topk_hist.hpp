@@ -10,6 +10,16 @@ namespace csa {
 enum : int { kCtrlDone = 0, kCtrlBin = 1, kCtrlAbove = 3, kCtrlCand = 4 };
 constexpr uint32_t kNoBin = 0xFFFFFFFFu;
 
+// Called by every workgroup that builds the histogram, before anything else:
+// the first workgroup of each query zero-fills the filter's counters, so the
+// filter (a later kernel) always starts from zero whatever the workspace held.
+__device__ __forceinline__ void hist_begin(uint32_t *ctrl) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        ctrl[kCtrlAbove] = 0u;
+        ctrl[kCtrlCand] = 0u;
+    }
+}
+
 // Workgroup-cooperative (256 threads).  Adds the workgroup's LDS histogram
 // `lh` to the query's global histogram; the last of the query's `n_wg`
 // workgroups to finish finds the bin holding the K-th largest key (counting
