@@ -95,7 +95,14 @@ float scale_of(const csa_dims *d) {
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t ws_topk(const csa_dims *d) { return csa::topk_workspace_bytes(n_queries(d), d->topk, d->max_entries); }
+// Histogram windows come from the bf16 scorer in the fused call (one per scorer
+// workgroup) and from the histogram kernel otherwise.
+int win_chunk(const csa_dims *d, bool fused) {
+    return fused && d->dtype == CSA_BF16 ? csa::score_chunk(d->max_entries, n_queries(d)) : csa::kTopkAuxChunk;
+}
+size_t ws_topk(const csa_dims *d, bool fused = false) {
+    return csa::topk_workspace_bytes(n_queries(d), d->topk, d->max_entries, win_chunk(d, fused));
+}
 size_t ws_sparse(const csa_dims *d) {
     return csa::mqa_workspace_bytes(d->dtype, n_queries(d), d->n_heads, d->head_dim, d->topk + d->window);
 }
@@ -108,7 +115,7 @@ size_t ws_attention_parts(const csa_dims *d, size_t *off_idx, size_t *off_topk, 
     const size_t idx = align_up(Q * (size_t)d->topk * 4);
     *off_idx = scores;
     *off_topk = scores + idx;
-    *off_mqa = *off_topk + align_up(ws_topk(d));
+    *off_mqa = *off_topk + align_up(ws_topk(d, true));
     return *off_mqa + align_up(ws_sparse(d)) + 256;
 }
 
@@ -145,7 +152,7 @@ csa::ScoreArgs score_args(const csa_dims *d, const void *q_idx, const float *w, 
 }
 
 csa::TopkArgs topk_args(const csa_dims *d, const float *scores, const int32_t *seq_len, const int32_t *q_pos,
-                        int32_t *idx, void *ws) {
+                        int32_t *idx, void *ws, bool fused = false) {
     csa::TopkArgs a{};
     a.scores = scores;
     a.seq_len = seq_len;
@@ -156,7 +163,7 @@ csa::TopkArgs topk_args(const csa_dims *d, const float *scores, const int32_t *s
     a.ratio = d->ratio;
     a.K = d->topk;
     a.n_max = d->max_entries;
-    csa::topk_carve(a, ws, n_queries(d));
+    csa::topk_carve(a, ws, n_queries(d), win_chunk(d, fused));
     return a;
 }
 
@@ -375,13 +382,13 @@ csa_status csa_attention(const csa_dims *d, const void *q, const void *q_idx, co
     float *scores = scores_out ? scores_out : (float *)base;
     int32_t *idx = topk_idx_out ? topk_idx_out : (int32_t *)(base + off_idx);
     hipStream_t st = (hipStream_t)stream;
-    const csa::TopkArgs ta = topk_args(d, scores, seq_len, q_pos, idx, base + off_topk);
+    const csa::TopkArgs ta = topk_args(d, scores, seq_len, q_pos, idx, base + off_topk, true);
     csa::ScoreArgs sa = score_args(d, q_idx, w, k_idx, seq_len, q_pos, scores);
-    // the bf16 scorer also builds the top-k key histogram while it writes the scores
+    // the bf16 scorer also writes the top-k key-histogram windows while it writes the scores
     const bool fused_hist = d->dtype == CSA_BF16 && csa::topk_uses_histogram(d->max_entries);
     if (fused_hist) {
-        sa.hist = ta.hist;
-        sa.ctrl = ta.ctrl;
+        sa.win_hdr = ta.win_hdr;
+        sa.win_cnt = ta.win_cnt;
         sa.K = d->topk;
     }
     hipError_t e = csa::launch_index_scores(sa, d->dtype, st);

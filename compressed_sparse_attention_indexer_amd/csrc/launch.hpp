@@ -19,14 +19,25 @@ struct ScoreArgs {
     float *scores;              // [Q, n_max]
     int B, T, HI, DI, ratio, act, n_max;
     int chunk;                  // entries per workgroup (bf16 kernel)
-    // optional fused top-k histogram (bf16 kernel): null to skip
-    uint32_t *hist;             // [Q, kTopkBins]
-    uint32_t *ctrl;             // [Q, kTopkCtrl]
+    // optional top-k key-histogram windows written by the bf16 kernel (null: skip)
+    int32_t *win_hdr;           // [Q, n_win]
+    uint32_t *win_cnt;          // [Q, n_win, kTopkWin]
     int K;
 };
 
 hipError_t launch_index_scores(const ScoreArgs &a, int dtype, hipStream_t stream);
 int score_chunk(int n_max, int n_queries);
+
+constexpr int kTopkSmallMax = 4096;       // rows up to this length: one workgroup, row kept in LDS
+constexpr int kTopkOneKernelMax = 65536;  // rows up to this length: threshold+scan+select in one kernel
+constexpr int kTopkBins = 4096;           // key histogram (top 12 key bits)
+constexpr int kTopkWin = 128;             // histogram window kept per workgroup (16 octaves)
+constexpr int kTopkCand = 8192;           // candidates held in LDS by the selecting workgroup
+constexpr int kTopkMaxK = 2048;
+constexpr int kTopkAuxChunk = 2048;       // scores per workgroup in the histogram and filter kernels
+constexpr int kFltAboveCap = 64;          // per filter workgroup: entries above the threshold bin
+constexpr int kFltCandCap = 256;          // per filter workgroup: candidates inside it
+constexpr int kFltRegionWords = 2 + kFltAboveCap + 2 * kFltCandCap;
 
 struct TopkArgs {
     const float *scores;        // [Q, n_max]
@@ -34,24 +45,18 @@ struct TopkArgs {
     const int32_t *q_pos;       // [Q]
     int32_t *idx;               // [Q, K]
     int B, T, ratio, K, n_max;
-    // multi-workgroup path scratch (inside the caller's workspace)
-    uint32_t *hist;             // [Q, kTopkBins] key histogram (left zero-filled after each call)
-    uint32_t *ctrl;             // [Q, kTopkCtrl] counters (left zero-filled after each call)
-    int32_t *sel;               // [Q, K] entries above the threshold bin
-    uint32_t *cand_key;         // [Q, kTopkCand]
-    int32_t *cand_idx;          // [Q, kTopkCand]
+    // scratch inside the caller's workspace (rows longer than kTopkSmallMax)
+    int win_chunk;              // entries per histogram window
+    int n_win;                  // windows per query = ceil(n_max / win_chunk)
+    int32_t *win_hdr;           // [Q, n_win]
+    uint32_t *win_cnt;          // [Q, n_win, kTopkWin]
+    uint32_t *bin;              // [Q] threshold bin (long rows)
+    uint32_t *flt;              // [Q, n_flt, kFltRegionWords] per-filter-workgroup lists (long rows)
 };
 
-constexpr int kTopkSmallMax = 4096;  // rows up to this length: one workgroup per query, in LDS
-constexpr int kTopkBins = 4096;      // first-level histogram (top 12 key bits)
-constexpr int kTopkCtrl = 8;
-constexpr int kTopkCand = 8192;      // candidates kept for the final in-LDS pass
-constexpr int kTopkMaxK = 2048;
-constexpr int kTopkAuxChunk = 2048;  // scores per workgroup in the histogram and filter kernels
-
-size_t topk_workspace_bytes(int n_queries, int K, int n_max);
-void topk_carve(TopkArgs &a, void *ws, int n_queries);
-// hist_done: the scorer already built the histogram and threshold (fused path)
+size_t topk_workspace_bytes(int n_queries, int K, int n_max, int win_chunk);
+void topk_carve(TopkArgs &a, void *ws, int n_queries, int win_chunk);
+// hist_done: the scorer already wrote the histogram windows (fused path)
 hipError_t launch_topk(const TopkArgs &a, hipStream_t stream, bool hist_done = false);
 bool topk_uses_histogram(int n_max);
 

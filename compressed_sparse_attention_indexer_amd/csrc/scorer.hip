@@ -65,8 +65,7 @@ constexpr int kEntriesPerWaveStep = 32;
 
 __global__ __launch_bounds__(64 * kScoreWaves) void index_scores_bf16_kernel(ScoreArgs a) {
     __shared__ uint32_t lh[kTopkBins];
-    __shared__ int s_flag;
-    __shared__ uint32_t s_wsum[4];
+    __shared__ int s_red[4];
     const int qi = blockIdx.y;
     const int b = qi / a.T;
     const int lane = threadIdx.x & 63;
@@ -76,11 +75,9 @@ __global__ __launch_bounds__(64 * kScoreWaves) void index_scores_bf16_kernel(Sco
 
     int nvis = visible_entries(a.seq_len[b], a.q_pos[qi], a.ratio);
     nvis = nvis < a.n_max ? nvis : a.n_max;
-    const bool with_hist = a.hist != nullptr && nvis > a.K;  // same for the whole workgroup
-    if (with_hist) {
-        hist_begin(a.ctrl + (size_t)qi * kTopkCtrl);
+    const bool with_hist = a.win_hdr != nullptr && nvis > a.K;  // same for the whole workgroup
+    if (with_hist)
         for (int i = threadIdx.x; i < kTopkBins; i += 64 * kScoreWaves) lh[i] = 0u;
-    }
     __syncthreads();
     const int j0 = blockIdx.x * a.chunk;
     const int j1 = j0 + a.chunk < a.n_max ? j0 + a.chunk : a.n_max;
@@ -144,11 +141,9 @@ __global__ __launch_bounds__(64 * kScoreWaves) void index_scores_bf16_kernel(Sco
             part[et] = p;
         }
         // Lanes of group g < 2 store column tile g: 32 consecutive scores.
-        if (g < 2 && j < j1) {
-            const float sv = j < nvis ? (g == 0 ? part[0] : part[1]) : -INFINITY;
-            srow[j] = sv;
-            if (with_hist && j < nvis) atomicAdd(&lh[order_key(sv) >> 20], 1u);
-        }
+        const float sv = j < nvis ? (g == 0 ? part[0] : part[1]) : -INFINITY;
+        if (g < 2 && j < j1) srow[j] = sv;
+        if (with_hist) lds_hist_add(lh, order_key(sv) >> 20, g < 2 && j < nvis);
     };
 
     constexpr int kStride = kScoreWaves * kEntriesPerWaveStep;
@@ -162,9 +157,10 @@ __global__ __launch_bounds__(64 * kScoreWaves) void index_scores_bf16_kernel(Sco
         if (b2 < lim) load(ka, b2);
         if (b1 < j1) process(kc, b1);
     }
-    if (with_hist)
-        hist_publish(lh, a.hist + (size_t)qi * kTopkBins, a.ctrl + (size_t)qi * kTopkCtrl, nvis, a.K, gridDim.x,
-                     &s_flag, s_wsum);
+    if (with_hist) {
+        const size_t w = (size_t)qi * gridDim.x + blockIdx.x;
+        hist_window_store(lh, a.win_hdr + w, a.win_cnt + w * kTopkWin, s_red);
+    }
 }
 
 hipError_t launch_index_scores(const ScoreArgs &a, int dtype, hipStream_t stream) {

@@ -3,23 +3,22 @@
 // bullet).  Order is (fp32 score desc, index asc); the K chosen indices are
 // written ascending, padded with -1 when fewer than K entries are visible.
 //
-// Scores become order-preserving uint32 keys.  Two paths:
-//  * rows up to kTopkLdsCap entries: one 1024-thread workgroup per query keeps
-//    the row in LDS, finds the exact K-th key with four 8-bit radix passes,
-//    then writes the selection in index order with an ordered compaction
-//    (wave ballots + cross-wave prefix counts), taking equal keys by index.
-//  * longer rows: many workgroups per query build a 12-bit key histogram (or
-//    the scorer builds it while writing the scores); the last workgroup of
-//    each query locates the bin holding the K-th key.  Many workgroups then
-//    copy out the entries above that bin and the candidates inside it.  One
-//    workgroup per query refines the candidates with a second 12-bit
-//    histogram, breaks the remaining ties by (key, -index), and writes the K
-//    indices in ascending order through an LDS bitmap.  Before using the
-//    candidates it checks that the counts are consistent (entries above the
-//    bin < K <= above + candidates, every candidate kept); otherwise it runs
-//    the exact one-workgroup scan of the whole row.  Correctness therefore
-//    never depends on the workspace's prior contents; the kernels leave the
-//    histogram and counters zero-filled, which makes the next call fast.
+// Scores become order-preserving uint32 keys.  Three row-length regimes:
+//  * up to kTopkSmallMax entries: one 1024-thread workgroup per query keeps
+//    the row in LDS, finds the exact K-th key with four 8-bit radix passes and
+//    writes the selection in index order with an ordered compaction.
+//  * up to kTopkOneKernelMax: the key histogram comes in windows (one per
+//    scorer or histogram workgroup, plain stores); one workgroup per query
+//    merges them into the exact histogram of the top 128 bins (16 octaves
+//    below the largest key), finds the bin holding the K-th key, scans the row
+//    into "above" and "candidate" lists in LDS, selects among the candidates
+//    and writes the indices in order through an LDS bitmap.
+//  * longer rows: the threshold, the scan (many workgroups, each writing its
+//    own lists with plain stores) and the selection run as three kernels.
+// Every shortcut is checked (counts consistent, buffers not overflowed,
+// threshold inside the merged window); otherwise the exact whole-row radix
+// scan runs.  No step uses global atomics, and correctness never depends on
+// the workspace's prior contents.
 #include "common.hpp"
 #include "launch.hpp"
 #include "topk_hist.hpp"
@@ -30,12 +29,14 @@ namespace {
 constexpr int kWG = 1024;
 constexpr int kWaves = kWG / 64;
 constexpr int kAuxThreads = 256;
+constexpr int kPerThread = kTopkAuxChunk / kAuxThreads;  // 8 scores per thread
+constexpr int kSubCap = 1024;                            // candidates sharing the final sub-bin
+constexpr int kBitmapMaxN = 262144;                      // LDS bitmap ordering up to this row length
 
 struct TopkShared {
     uint32_t hist[256];
     uint64_t masks[2][kWaves][2];
     int bcast[2];
-    int count;
 };
 
 // Wave 0 finds the histogram bin that holds the need-th largest element
@@ -94,9 +95,10 @@ __device__ void topk_row(const float *__restrict__ row, int n, int K, int32_t *_
         const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
         if (tid < 256) sh.hist[tid] = 0;
         __syncthreads();
-        for (int i = tid; i < n; i += kWG) {
-            const uint32_t k = key_at(i);
-            if ((k & hi_mask) == prefix) atomicAdd(&sh.hist[(k >> shift) & 255u], 1u);
+        for (int i0 = 0; i0 < n; i0 += kWG) {
+            const int i = i0 + tid;
+            const uint32_t k = i < n ? key_at(i) : 0u;
+            lds_hist_add(sh.hist, (k >> shift) & 255u, i < n && (k & hi_mask) == prefix);
         }
         __syncthreads();
         find_bin_256(sh, need);
@@ -153,116 +155,7 @@ __device__ __forceinline__ int query_visible(const TopkArgs &a, int qi) {
     return n < a.n_max ? n : a.n_max;
 }
 
-}  // namespace
-
-__global__ __launch_bounds__(kWG) void topk_lds_kernel(TopkArgs a) {
-    __shared__ uint32_t keys[kTopkSmallMax];
-    __shared__ TopkShared sh;
-    const int qi = blockIdx.x;
-    topk_row<true>(a.scores + (size_t)qi * a.n_max, query_visible(a, qi), a.K, a.idx + (size_t)qi * a.K,
-                   keys, sh);
-}
-
-// ---------------------------------------------------------------------------
-// Multi-workgroup path.
-
-namespace {
-constexpr int kPerThread = kTopkAuxChunk / kAuxThreads;  // 8 scores per thread
-constexpr int kSubCap = 1024;                            // second-level tie candidates
-constexpr int kBitmapMaxN = 262144;                      // LDS bitmap ordering up to this row length
-}  // namespace
-
-__global__ __launch_bounds__(kAuxThreads) void topk_hist_kernel(TopkArgs a) {
-    __shared__ uint32_t lh[kTopkBins];
-    __shared__ int s_flag;
-    __shared__ uint32_t s_wsum[4];
-    const int qi = blockIdx.y;
-    const int n = query_visible(a, qi);
-    if (n <= a.K) return;  // the same for every workgroup of this query
-    hist_begin(a.ctrl + (size_t)qi * kTopkCtrl);
-    for (int i = threadIdx.x; i < kTopkBins; i += kAuxThreads) lh[i] = 0u;
-    __syncthreads();
-    const float *row = a.scores + (size_t)qi * a.n_max;
-    const int j0 = blockIdx.x * kTopkAuxChunk + kPerThread * threadIdx.x;
-    float v[kPerThread];
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k) v[k] = j0 + k < n ? row[j0 + k] : 0.f;
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k)
-        if (j0 + k < n) atomicAdd(&lh[order_key(v[k]) >> 20], 1u);
-    hist_publish(lh, a.hist + (size_t)qi * kTopkBins, a.ctrl + (size_t)qi * kTopkCtrl, n, a.K, gridDim.x,
-                 &s_flag, s_wsum);
-}
-
-// Entries whose 12-bit key digit is above the threshold bin -> sel[], inside
-// it -> candidates.  Slots are reserved with one atomic per list per
-// workgroup; every write is bounded by its buffer.
-__global__ __launch_bounds__(kAuxThreads) void topk_filter_kernel(TopkArgs a) {
-    __shared__ int32_t l_sel[kTopkAuxChunk];
-    __shared__ int32_t l_cidx[kTopkAuxChunk];
-    __shared__ uint32_t l_ckey[kTopkAuxChunk];
-    __shared__ int l_cnt[2];
-    __shared__ int l_base[2];
-    const int qi = blockIdx.y;
-    const int n = query_visible(a, qi);
-    if (n <= a.K) return;
-    uint32_t *ctrl = a.ctrl + (size_t)qi * kTopkCtrl;
-    const uint32_t bin = ctrl[kCtrlBin];
-    if (bin >= (uint32_t)kTopkBins) return;
-    if (threadIdx.x < 2) l_cnt[threadIdx.x] = 0;
-    __syncthreads();
-    const float *row = a.scores + (size_t)qi * a.n_max;
-    const int j0 = blockIdx.x * kTopkAuxChunk + kPerThread * threadIdx.x;
-    float v[kPerThread];
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k) v[k] = j0 + k < n ? row[j0 + k] : 0.f;
-    const uint64_t lt = lanemask_lt();
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
-        const int j = j0 + k;
-        const uint32_t key = order_key(v[k]);
-        const uint32_t d = key >> 20;
-        const bool gt = j < n && d > bin;
-        const bool eq = j < n && d == bin;
-        const uint64_t mg = __ballot(gt), me = __ballot(eq);
-        if (mg) {
-            int base = 0;
-            if (lane == 0) base = atomicAdd(&l_cnt[0], __popcll(mg));
-            base = __shfl(base, 0);
-            if (gt) l_sel[base + __popcll(mg & lt)] = j;
-        }
-        if (me) {
-            int base = 0;
-            if (lane == 0) base = atomicAdd(&l_cnt[1], __popcll(me));
-            base = __shfl(base, 0);
-            if (eq) {
-                l_cidx[base + __popcll(me & lt)] = j;
-                l_ckey[base + __popcll(me & lt)] = key;
-            }
-        }
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        l_base[0] = l_cnt[0] ? (int)atomicAdd(&ctrl[kCtrlAbove], (uint32_t)l_cnt[0]) : 0;
-        l_base[1] = l_cnt[1] ? (int)atomicAdd(&ctrl[kCtrlCand], (uint32_t)l_cnt[1]) : 0;
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < l_cnt[0]; i += kAuxThreads) {
-        const int slot = l_base[0] + i;
-        if (slot < a.K) a.sel[(size_t)qi * a.K + slot] = l_sel[i];
-    }
-    for (int i = threadIdx.x; i < l_cnt[1]; i += kAuxThreads) {
-        const int slot = l_base[1] + i;
-        if (slot < kTopkCand) {
-            a.cand_idx[(size_t)qi * kTopkCand + slot] = l_cidx[i];
-            a.cand_key[(size_t)qi * kTopkCand + slot] = l_ckey[i];
-        }
-    }
-}
-
-namespace {
-// Block-wide exclusive prefix sum over 1024 threads (one value each).
+// Block-wide exclusive prefix sum over the 1024 threads (one value each).
 __device__ __forceinline__ int block_exclusive_scan(int x, int *s_wave, int *total) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int inc = x;
@@ -283,58 +176,46 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int *s_wave, int *tot
     *total = all;
     return before + inc - x;
 }
-}  // namespace
 
-// One workgroup per query: candidates -> exact selection -> ascending output.
-__global__ __launch_bounds__(kWG) void topk_final_kernel(TopkArgs a) {
-    __shared__ uint32_t c_key[kTopkCand];
-    __shared__ int32_t c_idx[kTopkCand];
-    __shared__ uint32_t bits[kBitmapMaxN / 32];  // also the second-level histogram
-    __shared__ uint32_t sub_key[kSubCap];
-    __shared__ int32_t sub_idx[kSubCap];
-    __shared__ int32_t v[kTopkMaxK];
-    __shared__ TopkShared sh;
-    __shared__ int s_wave[kWaves];
-    __shared__ int s_cnt[2];
-    const int qi = blockIdx.x;
+// Append `valid` lanes to an LDS list: one LDS atomic per wave.  Returns the
+// slot of this lane (meaningless when !valid).
+__device__ __forceinline__ int wave_append(int *count, bool valid) {
+    const uint64_t m = __ballot(valid);
+    int base = 0;
+    if (m) {
+        if (lane_id() == 0) base = atomicAdd(count, __popcll(m));
+        base = __shfl(base, 0);
+    }
+    return base + __popcll(m & lanemask_lt());
+}
+
+struct SelectShared {
+    uint32_t words[kBitmapMaxN / 32];  // second-level histogram, then the output bitmap
+    uint32_t sub_key[kSubCap];
+    int32_t sub_idx[kSubCap];
+    int s_wave[kWaves];
+    int cnt[2];
+    int bcast[2];
+};
+
+// Given v[0..na) = the entries above the threshold bin (na < K) and the
+// candidates inside it (c_key/c_idx[0..nc), na + nc >= K), keep the K - na
+// best candidates by (key desc, index asc) and write all K indices ascending.
+// Returns false (the same in every thread) if a capacity is exceeded; nothing
+// is written to `out` then.
+__device__ bool select_emit(int32_t *v, int na, const uint32_t *c_key, const int32_t *c_idx, int nc, int n, int K,
+                            int32_t *out, SelectShared &ss) {
     const int tid = threadIdx.x;
-    const int n = query_visible(a, qi);
-    const int K = a.K;
-    const float *row = a.scores + (size_t)qi * a.n_max;
-    int32_t *out = a.idx + (size_t)qi * K;
-    if (n <= K) {
-        for (int i = tid; i < K; i += kWG) out[i] = i < n ? i : -1;
-        return;
-    }
-    uint32_t *ctrl = a.ctrl + (size_t)qi * kTopkCtrl;
-    const uint32_t bin = ctrl[kCtrlBin];
-    const int n_above = (int)ctrl[kCtrlAbove];
-    const int n_cand = (int)ctrl[kCtrlCand];
-    __syncthreads();
-    if (tid == 0) {  // leave the counters zero-filled for the next call
-        ctrl[kCtrlDone] = 0u;
-        ctrl[kCtrlAbove] = 0u;
-        ctrl[kCtrlCand] = 0u;
-    }
-    const int need = K - n_above;
-    const bool fast = bin < (uint32_t)kTopkBins && n_above >= 0 && n_above < K && n_cand <= kTopkCand &&
-                      n_above + n_cand >= K;
-    if (!fast) {
-        topk_row<false>(row, n, K, out, nullptr, sh);
-        return;
-    }
-    uint32_t *h2 = bits;  // 4096-bin histogram of key bits [19:8]
+    const int need = K - na;
+    uint32_t *h2 = ss.words;  // 4096-bin histogram of key bits [19:8]
     for (int i = tid; i < kTopkBins; i += kWG) h2[i] = 0u;
-    if (tid < 2) s_cnt[tid] = 0;
-    for (int i = tid; i < n_above; i += kWG) v[i] = a.sel[(size_t)qi * K + i];
-    for (int i = tid; i < n_cand; i += kWG) {
-        c_key[i] = a.cand_key[(size_t)qi * kTopkCand + i];
-        c_idx[i] = a.cand_idx[(size_t)qi * kTopkCand + i];
+    if (tid < 2) ss.cnt[tid] = 0;
+    __syncthreads();
+    for (int i0 = 0; i0 < nc; i0 += kWG) {
+        const int i = i0 + tid;
+        lds_hist_add(h2, i < nc ? (c_key[i] >> 8) & 0xFFFu : 0u, i < nc);
     }
     __syncthreads();
-    for (int i = tid; i < n_cand; i += kWG) atomicAdd(&h2[(c_key[i] >> 8) & 0xFFFu], 1u);
-    __syncthreads();
-    // bin b2 of the need-th largest candidate: 4 bins per thread, suffix sums
     uint32_t hh[4], s = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -342,70 +223,63 @@ __global__ __launch_bounds__(kWG) void topk_final_kernel(TopkArgs a) {
         s += hh[i];
     }
     int tot;
-    const int pre = block_exclusive_scan((int)s, s_wave, &tot);  // bins below this thread
-    const int above_me = tot - pre - (int)s;                       // bins above this thread
+    const int pre = block_exclusive_scan((int)s, ss.s_wave, &tot);
+    const int above_me = tot - pre - (int)s;  // candidates in higher bins
     if (above_me < need && need <= above_me + (int)s) {
         int acc = above_me;
         for (int i = 3; i >= 0; --i) {
             if (acc < need && need <= acc + (int)hh[i]) {
-                sh.bcast[0] = 4 * tid + i;
-                sh.bcast[1] = need - acc;
+                ss.bcast[0] = 4 * tid + i;
+                ss.bcast[1] = need - acc;
                 break;
             }
             acc += (int)hh[i];
         }
     }
     __syncthreads();
-    const uint32_t b2 = (uint32_t)sh.bcast[0];
-    const int need2 = sh.bcast[1];
-    // above b2: selected; inside b2: ties to resolve by (key, -index)
-    for (int i = tid; i < n_cand; i += kWG) {
-        const uint32_t d2 = (c_key[i] >> 8) & 0xFFFu;
-        if (d2 > b2) {
-            const int slot = n_above + atomicAdd(&s_cnt[0], 1);
-            if (slot < K) v[slot] = c_idx[i];
-        } else if (d2 == b2) {
-            const int slot = atomicAdd(&s_cnt[1], 1);
-            if (slot < kSubCap) {
-                sub_key[slot] = c_key[i];
-                sub_idx[slot] = c_idx[i];
-            }
+    const uint32_t b2 = (uint32_t)ss.bcast[0];
+    const int need2 = ss.bcast[1];
+    for (int i0 = 0; i0 < nc; i0 += kWG) {
+        const int i = i0 + tid;
+        const uint32_t d2 = i < nc ? (c_key[i] >> 8) & 0xFFFu : 0u;
+        const bool hi = i < nc && d2 > b2, tie = i < nc && d2 == b2;
+        const int s_hi = wave_append(&ss.cnt[0], hi);
+        const int s_tie = wave_append(&ss.cnt[1], tie);
+        if (hi && na + s_hi < K) v[na + s_hi] = c_idx[i];
+        if (tie && s_tie < kSubCap) {
+            ss.sub_key[s_tie] = c_key[i];
+            ss.sub_idx[s_tie] = c_idx[i];
         }
     }
     __syncthreads();
-    const int n_hi = s_cnt[0], m2 = s_cnt[1];
-    if (m2 > kSubCap || n_above + n_hi + need2 != K) {  // not expected; stay exact
-        __syncthreads();
-        topk_row<false>(row, n, K, out, nullptr, sh);
-        return;
-    }
+    const int n_hi = ss.cnt[0], m2 = ss.cnt[1];
+    if (m2 > kSubCap || na + n_hi + need2 != K) return false;
     for (int t = tid; t < m2; t += kWG) {
-        const uint64_t mine = ((uint64_t)sub_key[t] << 32) | (uint32_t)~(uint32_t)sub_idx[t];
+        const uint64_t mine = ((uint64_t)ss.sub_key[t] << 32) | (uint32_t) ~(uint32_t)ss.sub_idx[t];
         int rank = 0;
         for (int u = 0; u < m2; ++u) {
-            const uint64_t other = ((uint64_t)sub_key[u] << 32) | (uint32_t)~(uint32_t)sub_idx[u];
+            const uint64_t other = ((uint64_t)ss.sub_key[u] << 32) | (uint32_t) ~(uint32_t)ss.sub_idx[u];
             rank += other > mine;
         }
-        if (rank < need2) v[n_above + n_hi + rank] = sub_idx[t];
+        if (rank < need2) v[na + n_hi + rank] = ss.sub_idx[t];
     }
     __syncthreads();
-    // ascending order
-    if (n <= kBitmapMaxN) {
+    if (n <= kBitmapMaxN) {  // ascending order through a bitmap of the row
         const int n_words = (n + 31) >> 5;
-        for (int i = tid; i < n_words; i += kWG) bits[i] = 0u;
+        for (int i = tid; i < n_words; i += kWG) ss.words[i] = 0u;
         __syncthreads();
-        for (int i = tid; i < K; i += kWG) atomicOr(&bits[v[i] >> 5], 1u << (v[i] & 31));
+        for (int i = tid; i < K; i += kWG) atomicOr(&ss.words[v[i] >> 5], 1u << (v[i] & 31));
         __syncthreads();
         constexpr int kWordsPerThread = kBitmapMaxN / 32 / kWG;  // 8
         uint32_t wv[kWordsPerThread];
-        int cnt = 0;
+        int c = 0;
 #pragma unroll
         for (int k = 0; k < kWordsPerThread; ++k) {
             const int wi = kWordsPerThread * tid + k;
-            wv[k] = wi < n_words ? bits[wi] : 0u;
-            cnt += __popc(wv[k]);
+            wv[k] = wi < n_words ? ss.words[wi] : 0u;
+            c += __popc(wv[k]);
         }
-        int pos = block_exclusive_scan(cnt, s_wave, &tot);
+        int pos = block_exclusive_scan(c, ss.s_wave, &tot);
 #pragma unroll
         for (int k = 0; k < kWordsPerThread; ++k) {
             uint32_t w = wv[k];
@@ -416,7 +290,7 @@ __global__ __launch_bounds__(kWG) void topk_final_kernel(TopkArgs a) {
                 w &= w - 1u;
             }
         }
-    } else {
+    } else {  // bitonic sort of the K indices, padded to a power of two
         int P = 1;
         while (P < K) P <<= 1;
         for (int i = K + tid; i < P; i += kWG) v[i] = 0x7FFFFFFF;
@@ -438,31 +312,268 @@ __global__ __launch_bounds__(kWG) void topk_final_kernel(TopkArgs a) {
         }
         for (int i = tid; i < K; i += kWG) out[i] = v[i];
     }
+    return true;
 }
 
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Short rows: whole row in LDS.
+__global__ __launch_bounds__(kWG) void topk_lds_kernel(TopkArgs a) {
+    __shared__ uint32_t keys[kTopkSmallMax];
+    __shared__ TopkShared sh;
+    const int qi = blockIdx.x;
+    topk_row<true>(a.scores + (size_t)qi * a.n_max, query_visible(a, qi), a.K, a.idx + (size_t)qi * a.K,
+                   keys, sh);
+}
+
+// ---------------------------------------------------------------------------
+// Histogram windows of a score row (when the scorer did not write them).
+__global__ __launch_bounds__(kAuxThreads) void topk_hist_kernel(TopkArgs a) {
+    __shared__ uint32_t lh[kTopkBins];
+    __shared__ int s_red[4];
+    const int qi = blockIdx.y;
+    const int n = query_visible(a, qi);
+    if (n <= a.K) return;  // the same for every workgroup of this query
+    for (int i = threadIdx.x; i < kTopkBins; i += kAuxThreads) lh[i] = 0u;
+    __syncthreads();
+    const float *row = a.scores + (size_t)qi * a.n_max;
+    const int j0 = blockIdx.x * a.win_chunk;
+    const int j1 = j0 + a.win_chunk < n ? j0 + a.win_chunk : n;
+    for (int jb = j0; jb < j1; jb += kTopkAuxChunk) {
+        float v[kPerThread];
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k) {
+            const int j = jb + k * kAuxThreads + threadIdx.x;
+            v[k] = j < j1 ? row[j] : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k) {
+            const int j = jb + k * kAuxThreads + threadIdx.x;
+            lds_hist_add(lh, order_key(v[k]) >> 20, j < j1);
+        }
+    }
+    const size_t w = (size_t)qi * a.n_win + blockIdx.x;
+    hist_window_store(lh, a.win_hdr + w, a.win_cnt + w * kTopkWin, s_red);
+}
+
+// ---------------------------------------------------------------------------
+// Rows up to kTopkOneKernelMax: threshold, scan and selection in one workgroup.
+__global__ __launch_bounds__(kWG) void topk_onekernel_kernel(TopkArgs a) {
+    __shared__ int32_t v[kTopkMaxK];
+    __shared__ uint32_t c_key[kTopkCand];
+    __shared__ int32_t c_idx[kTopkCand];
+    __shared__ SelectShared ss;
+    __shared__ TopkShared sh;
+    __shared__ uint32_t s_bins[kTopkWin];
+    __shared__ int s_red[kWaves];
+    __shared__ int s_cnt[2];
+    const int qi = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int n = query_visible(a, qi);
+    const int K = a.K;
+    const float *row = a.scores + (size_t)qi * a.n_max;
+    int32_t *out = a.idx + (size_t)qi * K;
+    if (n <= K) {
+        for (int i = tid; i < K; i += kWG) out[i] = i < n ? i : -1;
+        return;
+    }
+    const uint32_t bin = window_threshold(a.win_hdr + (size_t)qi * a.n_win,
+                                          a.win_cnt + (size_t)qi * a.n_win * kTopkWin, a.n_win, K, s_red, s_bins);
+    bool ok = bin != kNoBin;
+    if (ok) {
+        if (tid < 2) s_cnt[tid] = 0;
+        __syncthreads();
+        for (int j0 = 0; j0 < n; j0 += 4 * kWG) {
+            float x[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int j = j0 + k * kWG + tid;
+                x[k] = j < n ? row[j] : 0.f;
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int j = j0 + k * kWG + tid;
+                const uint32_t key = order_key(x[k]);
+                const uint32_t d = key >> 20;
+                const bool gt = j < n && d > bin, eq = j < n && d == bin;
+                const int sa = wave_append(&s_cnt[0], gt);
+                const int sc = wave_append(&s_cnt[1], eq);
+                if (gt && sa < K) v[sa] = j;
+                if (eq && sc < kTopkCand) {
+                    c_key[sc] = key;
+                    c_idx[sc] = j;
+                }
+            }
+        }
+        __syncthreads();
+        const int na = s_cnt[0], nc = s_cnt[1];
+        ok = na < K && nc <= kTopkCand && na + nc >= K;
+        __syncthreads();
+        if (ok) ok = select_emit(v, na, c_key, c_idx, nc, n, K, out, ss);
+    }
+    if (!ok) {
+        __syncthreads();
+        topk_row<false>(row, n, K, out, nullptr, sh);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Long rows: threshold kernel, many-workgroup scan, selection kernel.
+__global__ __launch_bounds__(kAuxThreads) void topk_thresh_kernel(TopkArgs a) {
+    __shared__ uint32_t s_bins[kTopkWin];
+    __shared__ int s_red[4];
+    const int qi = blockIdx.x;
+    if (query_visible(a, qi) <= a.K) return;
+    const uint32_t bin = window_threshold(a.win_hdr + (size_t)qi * a.n_win,
+                                          a.win_cnt + (size_t)qi * a.n_win * kTopkWin, a.n_win, a.K, s_red, s_bins);
+    if (threadIdx.x == 0) a.bin[qi] = bin;
+}
+
+// Each workgroup writes its own region: [0] above count (0xFFFFFFFF when a
+// list overflowed), [1] candidate count, then the above list, candidate keys
+// and candidate indices.
+__global__ __launch_bounds__(kAuxThreads) void topk_filter_kernel(TopkArgs a) {
+    __shared__ int32_t l_above[kFltAboveCap];
+    __shared__ uint32_t l_ckey[kFltCandCap];
+    __shared__ int32_t l_cidx[kFltCandCap];
+    __shared__ int l_cnt[2];
+    const int qi = blockIdx.y;
+    const int n = query_visible(a, qi);
+    if (n <= a.K) return;
+    const uint32_t bin = a.bin[qi];
+    uint32_t *reg = a.flt + ((size_t)qi * gridDim.x + blockIdx.x) * kFltRegionWords;
+    if (bin == kNoBin) return;
+    if (threadIdx.x < 2) l_cnt[threadIdx.x] = 0;
+    __syncthreads();
+    const float *row = a.scores + (size_t)qi * a.n_max;
+    const int j0 = blockIdx.x * kTopkAuxChunk;
+    float x[kPerThread];
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+        const int j = j0 + k * kAuxThreads + threadIdx.x;
+        x[k] = j < n ? row[j] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+        const int j = j0 + k * kAuxThreads + threadIdx.x;
+        const uint32_t key = order_key(x[k]);
+        const uint32_t d = key >> 20;
+        const bool gt = j < n && d > bin, eq = j < n && d == bin;
+        const int sa = wave_append(&l_cnt[0], gt);
+        const int sc = wave_append(&l_cnt[1], eq);
+        if (gt && sa < kFltAboveCap) l_above[sa] = j;
+        if (eq && sc < kFltCandCap) {
+            l_ckey[sc] = key;
+            l_cidx[sc] = j;
+        }
+    }
+    __syncthreads();
+    const int na = l_cnt[0], nc = l_cnt[1];
+    const bool over = na > kFltAboveCap || nc > kFltCandCap;
+    if (threadIdx.x == 0) {
+        reg[0] = over ? 0xFFFFFFFFu : (uint32_t)na;
+        reg[1] = (uint32_t)nc;
+    }
+    if (over) return;
+    for (int i = threadIdx.x; i < na; i += kAuxThreads) reg[2 + i] = (uint32_t)l_above[i];
+    for (int i = threadIdx.x; i < nc; i += kAuxThreads) {
+        reg[2 + kFltAboveCap + i] = l_ckey[i];
+        reg[2 + kFltAboveCap + kFltCandCap + i] = (uint32_t)l_cidx[i];
+    }
+}
+
+__global__ __launch_bounds__(kWG) void topk_final_kernel(TopkArgs a, int n_flt) {
+    __shared__ int32_t v[kTopkMaxK];
+    __shared__ uint32_t c_key[kTopkCand];
+    __shared__ int32_t c_idx[kTopkCand];
+    __shared__ SelectShared ss;
+    __shared__ TopkShared sh;
+    __shared__ int s_bad;
+    const int qi = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int n = query_visible(a, qi);
+    const int K = a.K;
+    const float *row = a.scores + (size_t)qi * a.n_max;
+    int32_t *out = a.idx + (size_t)qi * K;
+    if (n <= K) {
+        for (int i = tid; i < K; i += kWG) out[i] = i < n ? i : -1;
+        return;
+    }
+    bool ok = a.bin[qi] != kNoBin;
+    if (tid == 0) s_bad = 0;
+    __syncthreads();
+    // gather the filter lists of the workgroups that covered visible entries
+    const int n_reg = (n + kTopkAuxChunk - 1) / kTopkAuxChunk;
+    const uint32_t *reg0 = a.flt + (size_t)qi * n_flt * kFltRegionWords;
+    int na_tot = 0, nc_tot = 0;
+    for (int r0 = 0; ok && r0 < n_reg; r0 += kWG) {
+        const int r = r0 + tid;
+        uint32_t na = 0, nc = 0;
+        if (r < n_reg) {
+            na = reg0[(size_t)r * kFltRegionWords + 0];
+            nc = reg0[(size_t)r * kFltRegionWords + 1];
+            if (na > (uint32_t)kFltAboveCap || nc > (uint32_t)kFltCandCap) {
+                s_bad = 1;
+                na = nc = 0;
+            }
+        }
+        int ta, tc;
+        const int pa = block_exclusive_scan((int)na, ss.s_wave, &ta) + na_tot;
+        const int pc = block_exclusive_scan((int)nc, ss.s_wave, &tc) + nc_tot;
+        if (r < n_reg) {
+            const uint32_t *reg = reg0 + (size_t)r * kFltRegionWords;
+            for (uint32_t i = 0; i < na; ++i)
+                if (pa + (int)i < K) v[pa + i] = (int32_t)reg[2 + i];
+            for (uint32_t i = 0; i < nc; ++i)
+                if (pc + (int)i < kTopkCand) {
+                    c_key[pc + i] = reg[2 + kFltAboveCap + i];
+                    c_idx[pc + i] = (int32_t)reg[2 + kFltAboveCap + kFltCandCap + i];
+                }
+        }
+        na_tot += ta;
+        nc_tot += tc;
+    }
+    __syncthreads();
+    ok = ok && !s_bad && na_tot < K && nc_tot <= kTopkCand && na_tot + nc_tot >= K;
+    if (ok) ok = select_emit(v, na_tot, c_key, c_idx, nc_tot, n, K, out, ss);
+    if (!ok) {
+        __syncthreads();
+        topk_row<false>(row, n, K, out, nullptr, sh);
+    }
+}
+
+// ---------------------------------------------------------------------------
 bool topk_uses_histogram(int n_max) { return n_max > kTopkSmallMax; }
 
-size_t topk_workspace_bytes(int n_queries, int K, int n_max) {
+static int n_windows(int n_max, int win_chunk) { return (n_max + win_chunk - 1) / win_chunk; }
+static int n_filters(int n_max) { return (n_max + kTopkAuxChunk - 1) / kTopkAuxChunk; }
+
+size_t topk_workspace_bytes(int n_queries, int K, int n_max, int win_chunk) {
+    (void)K;
     if (!topk_uses_histogram(n_max)) return 0;
     const size_t Q = (size_t)n_queries;
-    return Q * kTopkBins * 4 + Q * kTopkCtrl * 4 + Q * (size_t)K * 4 + Q * kTopkCand * 8 + 256;
+    const size_t nw = (size_t)n_windows(n_max, win_chunk);
+    size_t b = Q * nw * 4 + Q * nw * kTopkWin * 4 + Q * 4 + 4 * 256;
+    if (n_max > kTopkOneKernelMax) b += Q * (size_t)n_filters(n_max) * kFltRegionWords * 4;
+    return b;
 }
 
 static inline char *align256(char *p) { return (char *)(((uintptr_t)p + 255) & ~(uintptr_t)255); }
 
-void topk_carve(TopkArgs &a, void *ws, int n_queries) {
+void topk_carve(TopkArgs &a, void *ws, int n_queries, int win_chunk) {
+    a.win_chunk = win_chunk;
+    a.n_win = n_windows(a.n_max, win_chunk);
     if (!topk_uses_histogram(a.n_max)) return;
     const size_t Q = (size_t)n_queries;
     char *p = align256((char *)ws);
-    a.hist = (uint32_t *)p;
-    p += Q * kTopkBins * 4;
-    a.ctrl = (uint32_t *)p;
-    p += Q * kTopkCtrl * 4;
-    a.sel = (int32_t *)p;
-    p += Q * (size_t)a.K * 4;
-    a.cand_key = (uint32_t *)p;
-    p += Q * kTopkCand * 4;
-    a.cand_idx = (int32_t *)p;
+    a.win_hdr = (int32_t *)p;
+    p = align256(p + Q * a.n_win * 4);
+    a.win_cnt = (uint32_t *)p;
+    p = align256(p + Q * a.n_win * kTopkWin * 4);
+    a.bin = (uint32_t *)p;
+    p = align256(p + Q * 4);
+    a.flt = (uint32_t *)p;
 }
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t stream, bool hist_done) {
@@ -471,10 +582,15 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t stream, bool hist_done) {
         hipLaunchKernelGGL(topk_lds_kernel, dim3(Q), dim3(kWG), 0, stream, a);
         return hipGetLastError();
     }
-    const int n_chunks = (a.n_max + kTopkAuxChunk - 1) / kTopkAuxChunk;
-    if (!hist_done) hipLaunchKernelGGL(topk_hist_kernel, dim3(n_chunks, Q), dim3(kAuxThreads), 0, stream, a);
-    hipLaunchKernelGGL(topk_filter_kernel, dim3(n_chunks, Q), dim3(kAuxThreads), 0, stream, a);
-    hipLaunchKernelGGL(topk_final_kernel, dim3(Q), dim3(kWG), 0, stream, a);
+    if (!hist_done) hipLaunchKernelGGL(topk_hist_kernel, dim3(a.n_win, Q), dim3(kAuxThreads), 0, stream, a);
+    if (a.n_max <= kTopkOneKernelMax) {
+        hipLaunchKernelGGL(topk_onekernel_kernel, dim3(Q), dim3(kWG), 0, stream, a);
+        return hipGetLastError();
+    }
+    const int nf = n_filters(a.n_max);
+    hipLaunchKernelGGL(topk_thresh_kernel, dim3(Q), dim3(kAuxThreads), 0, stream, a);
+    hipLaunchKernelGGL(topk_filter_kernel, dim3(nf, Q), dim3(kAuxThreads), 0, stream, a);
+    hipLaunchKernelGGL(topk_final_kernel, dim3(Q), dim3(kWG), 0, stream, a, nf);
     return hipGetLastError();
 }
 

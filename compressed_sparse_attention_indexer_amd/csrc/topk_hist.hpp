@@ -1,5 +1,7 @@
-// First-level key histogram of the multi-workgroup top-k, shared by the
-// histogram kernel and the scorer (which builds it while writing scores).
+// Key histograms of the multi-workgroup top-k, shared by the histogram
+// kernel, the scorer (which builds them while writing scores) and the
+// selection kernels.  No global atomics: every workgroup stores a window of
+// its own histogram with plain stores, and the consumer merges the windows.
 #pragma once
 
 #include "common.hpp"
@@ -7,74 +9,98 @@
 
 namespace csa {
 
-enum : int { kCtrlDone = 0, kCtrlBin = 1, kCtrlAbove = 3, kCtrlCand = 4 };
 constexpr uint32_t kNoBin = 0xFFFFFFFFu;
 
-// Called by every workgroup that builds the histogram, before anything else:
-// the first workgroup of each query zero-fills the filter's counters, so the
-// filter (a later kernel) always starts from zero whatever the workspace held.
-__device__ __forceinline__ void hist_begin(uint32_t *ctrl) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        ctrl[kCtrlAbove] = 0u;
-        ctrl[kCtrlCand] = 0u;
+// Wave-aggregated LDS histogram add: lanes holding the same bin are counted by
+// one atomic (scores crowd into few bins, so per-lane atomics would serialize).
+__device__ __forceinline__ void lds_hist_add(uint32_t *h, uint32_t bin, bool valid) {
+    uint64_t rem = __ballot(valid);
+    while (rem) {
+        const int leader = __builtin_ctzll(rem);
+        const uint32_t lb = __shfl(bin, leader);
+        const uint64_t m = __ballot(valid && bin == lb) & rem;
+        if (lane_id() == leader) atomicAdd(&h[lb], (uint32_t)__popcll(m));
+        rem &= ~m;
     }
 }
 
-// Workgroup-cooperative (256 threads).  Adds the workgroup's LDS histogram
-// `lh` to the query's global histogram; the last of the query's `n_wg`
-// workgroups to finish finds the bin holding the K-th largest key (counting
-// from the top bin down), stores it in ctrl[kCtrlBin] (kNoBin if the
-// histogram does not add up to n, e.g. a workspace that was not clean), and
-// zero-fills the histogram and the done counter for the next call.
-__device__ __forceinline__ void hist_publish(const uint32_t *lh, uint32_t *gh, uint32_t *ctrl, int n, int K,
-                                             int n_wg, int *s_flag, uint32_t *s_wsum) {
+// Workgroup of 256 threads: store the window of its 4096-bin LDS histogram `lh`
+// that ends at its highest non-empty bin M: cnt[t] = lh[M - 127 + t] (0 below
+// bin 0), hdr = M (or -1 when empty).  Bins within 128 of the global highest
+// bin are then exactly known from all windows together.
+__device__ __forceinline__ void hist_window_store(const uint32_t *lh, int32_t *hdr, uint32_t *cnt, int *s_red) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     __syncthreads();
-    for (int i = tid; i < kTopkBins; i += 256) {
-        const uint32_t c = lh[i];
-        if (c) atomicAdd(&gh[i], c);
-    }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) *s_flag = atomicAdd(&ctrl[kCtrlDone], 1u) == (uint32_t)n_wg - 1u;
-    __syncthreads();
-    if (!*s_flag) return;
-    __threadfence();
     constexpr int kPer = kTopkBins / 256;
-    uint32_t h[kPer];
-    uint32_t s = 0;
+    int mb = -1;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        h[i] = __hip_atomic_load(&gh[kPer * tid + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s += h[i];
-    }
-    uint32_t suf = s;  // sum over this lane and the lanes above it
+    for (int i = kPer - 1; i >= 0; --i)
+        if (mb < 0 && lh[kPer * tid + i]) mb = kPer * tid + i;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t t = __shfl_down(suf, o);
-        if (lane + o < 64) suf += t;
-    }
-    if (lane == 0) s_wsum[wave] = suf;
+    for (int o = 32; o > 0; o >>= 1) mb = max(mb, __shfl_xor(mb, o));
+    if (lane == 0) s_red[wave] = mb;
     __syncthreads();
-    const uint32_t total = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
-    for (int w = wave + 1; w < 4; ++w) suf += s_wsum[w];
-    const uint32_t above = suf - s;
-    const uint32_t need = (uint32_t)K;
-    if (total != (uint32_t)n) {
-        if (tid == 0) ctrl[kCtrlBin] = kNoBin;
-    } else if (above < need && need <= suf) {
-        uint32_t acc = above;
-        for (int i = kPer - 1; i >= 0; --i) {
-            if (acc < need && need <= acc + h[i]) {
-                ctrl[kCtrlBin] = (uint32_t)(kPer * tid + i);
+    const int M = max(max(s_red[0], s_red[1]), max(s_red[2], s_red[3]));
+    if (tid < kTopkWin) {
+        const int b = M - (kTopkWin - 1) + tid;
+        cnt[tid] = (M >= 0 && b >= 0) ? lh[b] : 0u;
+    }
+    if (tid == 0) *hdr = M;
+}
+
+// Merge n_win windows (hdr[w], cnt[w][kTopkWin]) into the exact histogram of
+// the top kTopkWin bins below the global highest bin, and return the bin that
+// holds the K-th largest key (kNoBin if it lies below that range or there is
+// nothing).  Any block size that is a multiple of 64 and >= kTopkWin.
+__device__ __forceinline__ uint32_t window_threshold(const int32_t *hdr, const uint32_t *cnt, int n_win, int K,
+                                                     int *s_red, uint32_t *s_bins) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nwaves = blockDim.x >> 6;
+    int m = -1;
+    for (int w = tid; w < n_win; w += blockDim.x) m = max(m, hdr[w]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = max(m, __shfl_xor(m, o));
+    if (lane == 0) s_red[wave] = m;
+    __syncthreads();
+    int M = -1;
+    for (int w = 0; w < nwaves; ++w) M = max(M, s_red[w]);
+    __syncthreads();
+    if (M < 0) return kNoBin;
+    if (tid < kTopkWin) {
+        const int b = M - (kTopkWin - 1) + tid;
+        uint32_t c = 0;
+        for (int w0 = 0; w0 < n_win; w0 += 8) {  // independent loads, 8 windows at a time
+            uint32_t x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int w = w0 + u;
+                const int mw = w < n_win ? hdr[w] : -1;
+                const int off = b - (mw - (kTopkWin - 1));
+                x[u] = (mw >= 0 && off >= 0 && off < kTopkWin) ? cnt[(size_t)w * kTopkWin + off] : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) c += x[u];
+        }
+        s_bins[tid] = c;
+    }
+    __syncthreads();
+    uint32_t result = kNoBin;
+    if (tid == 0) {
+        uint32_t acc = 0;
+        for (int t = kTopkWin - 1; t >= 0; --t) {
+            acc += s_bins[t];
+            const int b = M - (kTopkWin - 1) + t;
+            if (acc >= (uint32_t)K) {
+                result = b >= 0 ? (uint32_t)b : kNoBin;
                 break;
             }
-            acc += h[i];
         }
+        s_red[0] = (int)result;
     }
     __syncthreads();
-    for (int i = tid; i < kTopkBins; i += 256) gh[i] = 0u;
-    if (tid == 0) ctrl[kCtrlDone] = 0u;
+    result = (uint32_t)s_red[0];
+    __syncthreads();
+    return result;
 }
 
 }  // namespace csa

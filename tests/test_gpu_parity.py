@@ -191,6 +191,27 @@ def test_fused_selection_equals_standalone_topk():
     np.testing.assert_array_equal(g_idx, want)
 
 
+@pytest.mark.parametrize("n", [40000, 262144])
+def test_topk_extreme_range_and_clustered_tops(n):
+    """Shortcut guards: (a) one huge score puts the K-th key far below the
+    16-octave histogram window of the largest key; (b) every top score sits in
+    one contiguous block, overflowing per-workgroup lists.  Both must stay
+    exact."""
+    rng = np.random.default_rng(n)
+    s1 = rng.standard_normal(n).astype(np.float32) + 3.0
+    s1[n // 3] = 1e30
+    s2 = rng.random(n).astype(np.float32)
+    s2[n // 2:n // 2 + 3000] += 10.0
+    scores = np.stack([s1, s2])[:, None, :]
+    seq = np.array([4 * n, 4 * n], np.int32)
+    want = oracle.topk(scores, seq, seq - 1, ratio=4, k=512)
+    dims = csa.make_dims(batch=2, topk=512, max_entries=n)
+    say(f"[case] topk guards n={n}")
+    got = _np(csa.csa_topk_select(dims, torch.from_numpy(scores).cuda(), torch.from_numpy(seq).cuda(),
+                                  torch.from_numpy(seq - 1).cuda()))
+    np.testing.assert_array_equal(got, want)
+
+
 def test_topk_negative_zero_equals_zero():
     scores = np.zeros((1, 1, 2000), np.float32)
     scores[0, 0, ::2] = -0.0
