@@ -184,7 +184,7 @@ __device__ __forceinline__ int wave_append(int *count, bool valid) {
     int base = 0;
     if (m) {
         if (lane_id() == 0) base = atomicAdd(count, __popcll(m));
-        base = __shfl(base, 0);
+        base = __builtin_amdgcn_readlane(base, 0);
     }
     return base + __popcll(m & lanemask_lt());
 }
@@ -365,7 +365,7 @@ __global__ __launch_bounds__(kWG) void topk_onekernel_kernel(TopkArgs a) {
     __shared__ int32_t c_idx[kTopkCand];
     __shared__ SelectShared ss;
     __shared__ TopkShared sh;
-    __shared__ uint32_t s_bins[kTopkWin];
+    __shared__ uint32_t s_hist[kTopkWin];
     __shared__ int s_red[kWaves];
     __shared__ int s_cnt[2];
     const int qi = blockIdx.x;
@@ -379,20 +379,21 @@ __global__ __launch_bounds__(kWG) void topk_onekernel_kernel(TopkArgs a) {
         return;
     }
     const uint32_t bin = window_threshold(a.win_hdr + (size_t)qi * a.n_win,
-                                          a.win_cnt + (size_t)qi * a.n_win * kTopkWin, a.n_win, K, s_red, s_bins);
+                                          a.win_cnt + (size_t)qi * a.n_win * kTopkWin, a.n_win, K, s_red, s_hist);
     bool ok = bin != kNoBin;
     if (ok) {
         if (tid < 2) s_cnt[tid] = 0;
         __syncthreads();
-        for (int j0 = 0; j0 < n; j0 += 4 * kWG) {
-            float x[4];
+        constexpr int kRound = 16;  // scores per thread per round, all loads in flight together
+        for (int j0 = 0; j0 < n; j0 += kRound * kWG) {
+            float x[kRound];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
+            for (int k = 0; k < kRound; ++k) {
                 const int j = j0 + k * kWG + tid;
                 x[k] = j < n ? row[j] : 0.f;
             }
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
+            for (int k = 0; k < kRound; ++k) {
                 const int j = j0 + k * kWG + tid;
                 const uint32_t key = order_key(x[k]);
                 const uint32_t d = key >> 20;
@@ -420,13 +421,13 @@ __global__ __launch_bounds__(kWG) void topk_onekernel_kernel(TopkArgs a) {
 
 // ---------------------------------------------------------------------------
 // Long rows: threshold kernel, many-workgroup scan, selection kernel.
-__global__ __launch_bounds__(kAuxThreads) void topk_thresh_kernel(TopkArgs a) {
-    __shared__ uint32_t s_bins[kTopkWin];
-    __shared__ int s_red[4];
+__global__ __launch_bounds__(kWG) void topk_thresh_kernel(TopkArgs a) {
+    __shared__ uint32_t s_hist[kTopkWin];
+    __shared__ int s_red[kWaves];
     const int qi = blockIdx.x;
     if (query_visible(a, qi) <= a.K) return;
     const uint32_t bin = window_threshold(a.win_hdr + (size_t)qi * a.n_win,
-                                          a.win_cnt + (size_t)qi * a.n_win * kTopkWin, a.n_win, a.K, s_red, s_bins);
+                                          a.win_cnt + (size_t)qi * a.n_win * kTopkWin, a.n_win, a.K, s_red, s_hist);
     if (threadIdx.x == 0) a.bin[qi] = bin;
 }
 
@@ -490,6 +491,8 @@ __global__ __launch_bounds__(kWG) void topk_final_kernel(TopkArgs a, int n_flt) 
     __shared__ SelectShared ss;
     __shared__ TopkShared sh;
     __shared__ int s_bad;
+    __shared__ int s_pa[kWG];
+    __shared__ int s_pc[kWG];
     const int qi = blockIdx.x;
     const int tid = threadIdx.x;
     const int n = query_visible(a, qi);
@@ -503,12 +506,14 @@ __global__ __launch_bounds__(kWG) void topk_final_kernel(TopkArgs a, int n_flt) 
     bool ok = a.bin[qi] != kNoBin;
     if (tid == 0) s_bad = 0;
     __syncthreads();
-    // gather the filter lists of the workgroups that covered visible entries
+    // gather the filter lists of the workgroups that covered visible entries:
+    // headers first (one round), then a flattened copy (one more round)
     const int n_reg = (n + kTopkAuxChunk - 1) / kTopkAuxChunk;
     const uint32_t *reg0 = a.flt + (size_t)qi * n_flt * kFltRegionWords;
     int na_tot = 0, nc_tot = 0;
     for (int r0 = 0; ok && r0 < n_reg; r0 += kWG) {
         const int r = r0 + tid;
+        const int nr = n_reg - r0 < kWG ? n_reg - r0 : kWG;
         uint32_t na = 0, nc = 0;
         if (r < n_reg) {
             na = reg0[(size_t)r * kFltRegionWords + 0];
@@ -519,20 +524,37 @@ __global__ __launch_bounds__(kWG) void topk_final_kernel(TopkArgs a, int n_flt) 
             }
         }
         int ta, tc;
-        const int pa = block_exclusive_scan((int)na, ss.s_wave, &ta) + na_tot;
-        const int pc = block_exclusive_scan((int)nc, ss.s_wave, &tc) + nc_tot;
-        if (r < n_reg) {
-            const uint32_t *reg = reg0 + (size_t)r * kFltRegionWords;
-            for (uint32_t i = 0; i < na; ++i)
-                if (pa + (int)i < K) v[pa + i] = (int32_t)reg[2 + i];
-            for (uint32_t i = 0; i < nc; ++i)
-                if (pc + (int)i < kTopkCand) {
-                    c_key[pc + i] = reg[2 + kFltAboveCap + i];
-                    c_idx[pc + i] = (int32_t)reg[2 + kFltAboveCap + kFltCandCap + i];
-                }
+        const int pa = block_exclusive_scan((int)na, ss.s_wave, &ta);
+        const int pc = block_exclusive_scan((int)nc, ss.s_wave, &tc);
+        s_pa[tid] = pa;  // exclusive prefix of this block of regions
+        s_pc[tid] = pc;
+        __syncthreads();
+        // entry f of the block's above-lists lives in region r with s_pa[r] <= f < s_pa[r+1]
+        for (int f = tid; f < ta; f += kWG) {
+            int lo = 0, hi = nr - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_pa[mid] <= f) lo = mid; else hi = mid - 1;
+            }
+            const uint32_t *reg = reg0 + (size_t)(r0 + lo) * kFltRegionWords;
+            if (na_tot + f < K) v[na_tot + f] = (int32_t)reg[2 + (f - s_pa[lo])];
+        }
+        for (int f = tid; f < tc; f += kWG) {
+            int lo = 0, hi = nr - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_pc[mid] <= f) lo = mid; else hi = mid - 1;
+            }
+            const uint32_t *reg = reg0 + (size_t)(r0 + lo) * kFltRegionWords;
+            const int i = f - s_pc[lo];
+            if (nc_tot + f < kTopkCand) {
+                c_key[nc_tot + f] = reg[2 + kFltAboveCap + i];
+                c_idx[nc_tot + f] = (int32_t)reg[2 + kFltAboveCap + kFltCandCap + i];
+            }
         }
         na_tot += ta;
         nc_tot += tc;
+        __syncthreads();
     }
     __syncthreads();
     ok = ok && !s_bad && na_tot < K && nc_tot <= kTopkCand && na_tot + nc_tot >= K;
@@ -588,7 +610,7 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t stream, bool hist_done) {
         return hipGetLastError();
     }
     const int nf = n_filters(a.n_max);
-    hipLaunchKernelGGL(topk_thresh_kernel, dim3(Q), dim3(kAuxThreads), 0, stream, a);
+    hipLaunchKernelGGL(topk_thresh_kernel, dim3(Q), dim3(kWG), 0, stream, a);
     hipLaunchKernelGGL(topk_filter_kernel, dim3(nf, Q), dim3(kAuxThreads), 0, stream, a);
     hipLaunchKernelGGL(topk_final_kernel, dim3(Q), dim3(kWG), 0, stream, a, nf);
     return hipGetLastError();

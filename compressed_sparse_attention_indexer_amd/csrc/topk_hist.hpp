@@ -17,7 +17,7 @@ __device__ __forceinline__ void lds_hist_add(uint32_t *h, uint32_t bin, bool val
     uint64_t rem = __ballot(valid);
     while (rem) {
         const int leader = __builtin_ctzll(rem);
-        const uint32_t lb = __shfl(bin, leader);
+        const uint32_t lb = __builtin_amdgcn_readlane(bin, leader);
         const uint64_t m = __ballot(valid && bin == lb) & rem;
         if (lane_id() == leader) atomicAdd(&h[lb], (uint32_t)__popcll(m));
         rem &= ~m;
@@ -49,48 +49,54 @@ __device__ __forceinline__ void hist_window_store(const uint32_t *lh, int32_t *h
 }
 
 // Merge n_win windows (hdr[w], cnt[w][kTopkWin]) into the exact histogram of
-// the top kTopkWin bins below the global highest bin, and return the bin that
-// holds the K-th largest key (kNoBin if it lies below that range or there is
-// nothing).  Any block size that is a multiple of 64 and >= kTopkWin.
+// the top kTopkWin bins below the global highest bin M, and return the bin
+// holding the K-th largest key (kNoBin if it lies below that range or there is
+// nothing).  Block of 1024 threads.  Loads are issued in two rounds (headers,
+// then up to 256 windows at a time) so latency is paid a few times, not per
+// window.  s_hist needs kTopkWin words, s_red 16.
 __device__ __forceinline__ uint32_t window_threshold(const int32_t *hdr, const uint32_t *cnt, int n_win, int K,
-                                                     int *s_red, uint32_t *s_bins) {
+                                                     int *s_red, uint32_t *s_hist) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nwaves = blockDim.x >> 6;
     int m = -1;
-    for (int w = tid; w < n_win; w += blockDim.x) m = max(m, hdr[w]);
+    for (int w = tid; w < n_win; w += 1024) m = max(m, hdr[w]);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) m = max(m, __shfl_xor(m, o));
     if (lane == 0) s_red[wave] = m;
+    if (tid < kTopkWin) s_hist[tid] = 0u;
     __syncthreads();
     int M = -1;
-    for (int w = 0; w < nwaves; ++w) M = max(M, s_red[w]);
-    __syncthreads();
-    if (M < 0) return kNoBin;
-    if (tid < kTopkWin) {
-        const int b = M - (kTopkWin - 1) + tid;
-        uint32_t c = 0;
-        for (int w0 = 0; w0 < n_win; w0 += 8) {  // independent loads, 8 windows at a time
-            uint32_t x[8];
+    for (int w = 0; w < 16; ++w) M = max(M, s_red[w]);
+    if (M < 0) return kNoBin;  // the same in every thread
+    // 4 threads per window, 32 bins (8 x 16 bytes) each
+    const int seg = tid & 3;
+    for (int w0 = 0; w0 < n_win; w0 += 256) {
+        const int w = w0 + (tid >> 2);
+        int mw = -1;
+        u32x4_t x[8];
+        if (w < n_win) {
+            mw = hdr[w];
+            const u32x4_t *src = (const u32x4_t *)(cnt + (size_t)w * kTopkWin + 32 * seg);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int w = w0 + u;
-                const int mw = w < n_win ? hdr[w] : -1;
-                const int off = b - (mw - (kTopkWin - 1));
-                x[u] = (mw >= 0 && off >= 0 && off < kTopkWin) ? cnt[(size_t)w * kTopkWin + off] : 0u;
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) c += x[u];
+            for (int i = 0; i < 8; ++i) x[i] = src[i];
         }
-        s_bins[tid] = c;
+        if (mw >= 0) {
+            const int off = mw - M + 32 * seg;  // global-window bin of this thread's first count
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int b = off + 4 * i + c;
+                    if (x[i][c] && b >= 0 && b < kTopkWin) atomicAdd(&s_hist[b], x[i][c]);
+                }
+        }
     }
     __syncthreads();
-    uint32_t result = kNoBin;
     if (tid == 0) {
-        uint32_t acc = 0;
+        uint32_t result = kNoBin, acc = 0;
         for (int t = kTopkWin - 1; t >= 0; --t) {
-            acc += s_bins[t];
-            const int b = M - (kTopkWin - 1) + t;
+            acc += s_hist[t];
             if (acc >= (uint32_t)K) {
+                const int b = M - (kTopkWin - 1) + t;
                 result = b >= 0 ? (uint32_t)b : kNoBin;
                 break;
             }
@@ -98,7 +104,7 @@ __device__ __forceinline__ uint32_t window_threshold(const int32_t *hdr, const u
         s_red[0] = (int)result;
     }
     __syncthreads();
-    result = (uint32_t)s_red[0];
+    const uint32_t result = (uint32_t)s_red[0];
     __syncthreads();
     return result;
 }
