@@ -211,10 +211,7 @@ __device__ bool select_emit(int32_t *v, int na, const uint32_t *c_key, const int
     for (int i = tid; i < kTopkBins; i += kWG) h2[i] = 0u;
     if (tid < 2) ss.cnt[tid] = 0;
     __syncthreads();
-    for (int i0 = 0; i0 < nc; i0 += kWG) {
-        const int i = i0 + tid;
-        lds_hist_add(h2, i < nc ? (c_key[i] >> 8) & 0xFFFu : 0u, i < nc);
-    }
+    for (int i = tid; i < nc; i += kWG) atomicAdd(&h2[(c_key[i] >> 8) & 0xFFFu], 1u);  // spread bins
     __syncthreads();
     uint32_t hh[4], s = 0;
 #pragma unroll

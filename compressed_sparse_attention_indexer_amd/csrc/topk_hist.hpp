@@ -11,17 +11,18 @@ namespace csa {
 
 constexpr uint32_t kNoBin = 0xFFFFFFFFu;
 
-// Wave-aggregated LDS histogram add: lanes holding the same bin are counted by
-// one atomic (scores crowd into few bins, so per-lane atomics would serialize).
+// LDS histogram add.  Scores often crowd into one bin, and same-address LDS
+// atomics serialize lane by lane, so lanes that share the first active lane's
+// bin are counted with one atomic; the other lanes add on their own.
 __device__ __forceinline__ void lds_hist_add(uint32_t *h, uint32_t bin, bool valid) {
-    uint64_t rem = __ballot(valid);
-    while (rem) {
-        const int leader = __builtin_ctzll(rem);
-        const uint32_t lb = __builtin_amdgcn_readlane(bin, leader);
-        const uint64_t m = __ballot(valid && bin == lb) & rem;
-        if (lane_id() == leader) atomicAdd(&h[lb], (uint32_t)__popcll(m));
-        rem &= ~m;
-    }
+    const uint64_t act = __ballot(valid);
+    if (!act) return;
+    const int leader = __builtin_ctzll(act);
+    const uint32_t lb = __builtin_amdgcn_readlane(bin, leader);
+    const bool same = valid && bin == lb;
+    const uint64_t m = __ballot(same);
+    if (lane_id() == leader) atomicAdd(&h[lb], (uint32_t)__popcll(m));
+    if (valid && !same) atomicAdd(&h[bin], 1u);
 }
 
 // Workgroup of 256 threads: store the window of its 4096-bin LDS histogram `lh`
