@@ -96,12 +96,12 @@ float scale_of(const csa_dims *d) {
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Histogram windows come from the bf16 scorer in the fused call (one per scorer
-// workgroup) and from the histogram kernel otherwise.
-int win_chunk(const csa_dims *d, bool fused) {
-    return fused && d->dtype == CSA_BF16 ? csa::score_chunk(d->max_entries, n_queries(d)) : csa::kTopkAuxChunk;
+// workgroup) and from the top-k's own histogram kernel otherwise.
+int win_count(const csa_dims *d, bool fused) {
+    return fused && d->dtype == CSA_BF16 ? csa::score_workgroups(d->max_entries, n_queries(d)) : 0;
 }
 size_t ws_topk(const csa_dims *d, bool fused = false) {
-    return csa::topk_workspace_bytes(n_queries(d), d->topk, d->max_entries, win_chunk(d, fused));
+    return csa::topk_workspace_bytes(n_queries(d), d->topk, d->max_entries, win_count(d, fused));
 }
 size_t ws_sparse(const csa_dims *d) {
     return csa::mqa_workspace_bytes(d->dtype, n_queries(d), d->n_heads, d->head_dim, d->topk + d->window);
@@ -147,7 +147,6 @@ csa::ScoreArgs score_args(const csa_dims *d, const void *q_idx, const float *w, 
     a.ratio = d->ratio;
     a.act = d->index_act;
     a.n_max = d->max_entries;
-    a.chunk = csa::score_chunk(d->max_entries, n_queries(d));
     return a;
 }
 
@@ -163,7 +162,7 @@ csa::TopkArgs topk_args(const csa_dims *d, const float *scores, const int32_t *s
     a.ratio = d->ratio;
     a.K = d->topk;
     a.n_max = d->max_entries;
-    csa::topk_carve(a, ws, n_queries(d), win_chunk(d, fused));
+    csa::topk_carve(a, ws, n_queries(d), win_count(d, fused));
     return a;
 }
 

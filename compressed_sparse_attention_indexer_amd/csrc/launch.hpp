@@ -18,15 +18,15 @@ struct ScoreArgs {
     const int32_t *q_pos;       // [Q]
     float *scores;              // [Q, n_max]
     int B, T, HI, DI, ratio, act, n_max;
-    int chunk;                  // entries per workgroup (bf16 kernel)
-    // optional top-k key-histogram windows written by the bf16 kernel (null: skip)
+    // optional top-k key-histogram windows written by the bf16 kernel (null: skip),
+    // one window per scorer workgroup of a query
     int32_t *win_hdr;           // [Q, n_win]
     uint32_t *win_cnt;          // [Q, n_win, kTopkWin]
     int K;
 };
 
 hipError_t launch_index_scores(const ScoreArgs &a, int dtype, hipStream_t stream);
-int score_chunk(int n_max, int n_queries);
+int score_workgroups(int n_max, int n_queries);  // bf16 scorer workgroups per query
 
 constexpr int kTopkSmallMax = 4096;       // rows up to this length: one workgroup, row kept in LDS
 constexpr int kTopkOneKernelMax = 65536;  // rows up to this length: threshold+scan+select in one kernel
@@ -46,16 +46,16 @@ struct TopkArgs {
     int32_t *idx;               // [Q, K]
     int B, T, ratio, K, n_max;
     // scratch inside the caller's workspace (rows longer than kTopkSmallMax)
-    int win_chunk;              // entries per histogram window
-    int n_win;                  // windows per query = ceil(n_max / win_chunk)
+    int n_win;                  // histogram windows per query
     int32_t *win_hdr;           // [Q, n_win]
     uint32_t *win_cnt;          // [Q, n_win, kTopkWin]
     uint32_t *bin;              // [Q] threshold bin (long rows)
     uint32_t *flt;              // [Q, n_flt, kFltRegionWords] per-filter-workgroup lists (long rows)
 };
 
-size_t topk_workspace_bytes(int n_queries, int K, int n_max, int win_chunk);
-void topk_carve(TopkArgs &a, void *ws, int n_queries, int win_chunk);
+// n_win: windows per query (scorer workgroups per query in the fused path, else 0 = own histogram kernel)
+size_t topk_workspace_bytes(int n_queries, int K, int n_max, int n_win);
+void topk_carve(TopkArgs &a, void *ws, int n_queries, int n_win);
 // hist_done: the scorer already wrote the histogram windows (fused path)
 hipError_t launch_topk(const TopkArgs &a, hipStream_t stream, bool hist_done = false);
 bool topk_uses_histogram(int n_max);

@@ -49,22 +49,31 @@ __global__ __launch_bounds__(256) void index_scores_f32_kernel(ScoreArgs a) {
 // 16-head row tiles) x 128 dims (four k-steps of 32) on
 // v_mfma_f32_16x16x32_bf16.  A = index query (heads x dims, resident in
 // registers), B = index keys (dims x entries) loaded straight from HBM into
-// registers, one step ahead of the step being computed.  Lane (e, g) of a
-// tile holds dims [32s + 8g, 32s + 8g + 8) of entry e for k-step s, so each
-// load instruction reads 64 contiguous bytes of every entry it touches.  The
-// C tile gives each lane 4 heads of one entry; the weighted ReLU sum over
-// those heads is done in registers and the 4 lane groups are summed with two
-// cross-lane adds.  Optionally the workgroup also histograms the keys of the
-// scores it writes for the multi-workgroup top-k.
+// registers with nontemporal loads, two steps ahead of the step being
+// computed.  Lane (e, g) of a tile holds dims [32s + 8g, 32s + 8g + 8) of
+// entry e for k-step s, so each load instruction reads 64 contiguous bytes of
+// every entry it touches.  The C tile gives each lane 4 heads of one entry;
+// the weighted activation sum over those heads is done in registers and the 4
+// lane groups are summed with two cross-lane adds.
+//
+// Launch shape: about one 4-wave workgroup per CU.  A workgroup-step covers
+// 128 entries (32 KiB of keys); the steps of a query are dealt round-robin to
+// its workgroups, so the workgroups in flight read neighbouring memory (the
+// pattern that streams HBM fastest on this part).  Optionally each workgroup
+// also histograms the keys of the scores it writes, for the top-k.
 namespace {
 constexpr int kHI = 64;
 constexpr int kDI = 128;
 constexpr int kScoreWaves = 4;
-constexpr int kEntriesPerWaveStep = 32;
+constexpr int kWaveStep = 32;                         // entries per wave and step
+constexpr int kWgStep = kScoreWaves * kWaveStep;      // entries per workgroup step
+constexpr int kTargetWgs = 256;                       // about one workgroup per CU
+typedef bf16x8_t KeyFrag[2][4];
 }  // namespace
 
-__global__ __launch_bounds__(64 * kScoreWaves) void index_scores_bf16_kernel(ScoreArgs a) {
-    __shared__ uint32_t lh[kTopkBins];
+template <int kAct, bool kHist>
+__global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(ScoreArgs a) {
+    __shared__ uint32_t lh[kHist ? kTopkBins : 1];
     __shared__ int s_red[4];
     const int qi = blockIdx.y;
     const int b = qi / a.T;
@@ -75,13 +84,11 @@ __global__ __launch_bounds__(64 * kScoreWaves) void index_scores_bf16_kernel(Sco
 
     int nvis = visible_entries(a.seq_len[b], a.q_pos[qi], a.ratio);
     nvis = nvis < a.n_max ? nvis : a.n_max;
-    const bool with_hist = a.win_hdr != nullptr && nvis > a.K;  // same for the whole workgroup
-    if (with_hist)
+    const bool with_hist = kHist && nvis > a.K;  // same for the whole workgroup
+    if (with_hist) {
         for (int i = threadIdx.x; i < kTopkBins; i += 64 * kScoreWaves) lh[i] = 0u;
-    __syncthreads();
-    const int j0 = blockIdx.x * a.chunk;
-    const int j1 = j0 + a.chunk < a.n_max ? j0 + a.chunk : a.n_max;
-    const int lim = j1 < nvis ? j1 : nvis;
+        __syncthreads();
+    }
     float *srow = a.scores + (size_t)qi * a.n_max;
 
     // A fragments: head 16*ht + e, dims 32s + 8g .. +8 for k-step s.
@@ -101,20 +108,26 @@ __global__ __launch_bounds__(64 * kScoreWaves) void index_scores_bf16_kernel(Sco
 
     const uint16_t *kb = (const uint16_t *)a.k_idx[b];
     const int last = nvis > 0 ? nvis - 1 : 0;
-    auto load = [&](bf16x8_t (&kf)[2][4], int base) {
+    // step k of this wave starts at entry base(k)
+    const int stride = gridDim.x * kWgStep;
+    const int base0 = blockIdx.x * kWgStep + wave * kWaveStep;
+
+    auto load = [&](KeyFrag &kf, int base) {
+        if (base >= nvis) return;  // nothing visible: not loaded, not used
+        const bool full = base + kWaveStep <= nvis;
 #pragma unroll
         for (int et = 0; et < 2; ++et) {
             int j = base + 16 * et + e;
-            j = j < nvis ? j : last;  // clamp: loaded but discarded
-            const uint16_t *kr = kb + (size_t)j * kDI + 8 * g;
+            if (!full) j = j < nvis ? j : last;  // clamp: loaded but discarded
+            const bf16x8_t *kr = (const bf16x8_t *)(kb + (size_t)j * kDI + 8 * g);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) kf[et][s] = *(const bf16x8_t *)(kr + 32 * s);
+            for (int s = 0; s < 4; ++s) kf[et][s] = __builtin_nontemporal_load(kr + 4 * s);
         }
     };
-    auto process = [&](const bf16x8_t (&kf)[2][4], int base) {
+    auto process = [&](const KeyFrag &kf, int base) {
         const int j = base + 16 * g + e;  // entry this lane stores (g < 2)
-        if (base >= nvis) {  // nothing visible in this step
-            if (g < 2 && j < j1) srow[j] = -INFINITY;
+        if (base >= nvis) {               // nothing visible in this step
+            if (g < 2 && j < a.n_max) srow[j] = -INFINITY;
             return;
         }
         float part[2];
@@ -134,7 +147,7 @@ __global__ __launch_bounds__(64 * kScoreWaves) void index_scores_bf16_kernel(Sco
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float x = acc[ht][r];
-                    p = fmaf(wr[ht][r], a.act == 0 ? fmaxf(x, 0.f) : x, p);
+                    p = fmaf(wr[ht][r], kAct == 0 ? fmaxf(x, 0.f) : x, p);
                 }
             p += __shfl_xor(p, 16);
             p += __shfl_xor(p, 32);
@@ -142,20 +155,23 @@ __global__ __launch_bounds__(64 * kScoreWaves) void index_scores_bf16_kernel(Sco
         }
         // Lanes of group g < 2 store column tile g: 32 consecutive scores.
         const float sv = j < nvis ? (g == 0 ? part[0] : part[1]) : -INFINITY;
-        if (g < 2 && j < j1) srow[j] = sv;
+        if (g < 2 && j < a.n_max) srow[j] = sv;
         if (with_hist) lds_hist_add(lh, order_key(sv) >> 20, g < 2 && j < nvis);
     };
 
-    constexpr int kStride = kScoreWaves * kEntriesPerWaveStep;
-    bf16x8_t ka[2][4], kc[2][4];
-    int base = j0 + wave * kEntriesPerWaveStep;
-    if (base < lim) load(ka, base);
-    for (; base < j1; base += 2 * kStride) {
-        const int b1 = base + kStride, b2 = base + 2 * kStride;
-        if (b1 < lim) load(kc, b1);
-        process(ka, base);
-        if (b2 < lim) load(ka, b2);
-        if (b1 < j1) process(kc, b1);
+    // three register buffers: keys of steps k, k+1, k+2 in flight
+    KeyFrag k0, k1, k2;
+    load(k0, base0);
+    load(k1, base0 + stride);
+    for (int base = base0; base < a.n_max; base += 3 * stride) {
+        load(k2, base + 2 * stride);
+        process(k0, base);
+        if (base + stride >= a.n_max) break;
+        load(k0, base + 3 * stride);
+        process(k1, base + stride);
+        if (base + 2 * stride >= a.n_max) break;
+        load(k1, base + 4 * stride);
+        process(k2, base + 2 * stride);
     }
     if (with_hist) {
         const size_t w = (size_t)qi * gridDim.x + blockIdx.x;
@@ -169,22 +185,31 @@ hipError_t launch_index_scores(const ScoreArgs &a, int dtype, hipStream_t stream
         dim3 grid((a.n_max + 255) / 256, Q);
         const size_t lds = sizeof(float) * (size_t)(a.HI * a.DI + a.HI);
         hipLaunchKernelGGL(index_scores_f32_kernel, grid, dim3(256), lds, stream, a);
+        return hipGetLastError();
+    }
+    dim3 grid(score_workgroups(a.n_max, Q), Q);
+    dim3 block(64 * kScoreWaves);
+    const bool hist = a.win_hdr != nullptr;
+    if (a.act == 0) {
+        if (hist)
+            hipLaunchKernelGGL((index_scores_bf16_kernel<0, true>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((index_scores_bf16_kernel<0, false>), grid, block, 0, stream, a);
     } else {
-        dim3 grid((a.n_max + a.chunk - 1) / a.chunk, Q);
-        hipLaunchKernelGGL(index_scores_bf16_kernel, grid, dim3(64 * kScoreWaves), 0, stream, a);
+        if (hist)
+            hipLaunchKernelGGL((index_scores_bf16_kernel<1, true>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((index_scores_bf16_kernel<1, false>), grid, block, 0, stream, a);
     }
     return hipGetLastError();
 }
 
-int score_chunk(int n_max, int n_queries) {
-    // Aim for ~1024 workgroups over the whole launch; multiples of two
-    // workgroup steps (4 waves x 32 entries, double-buffered).
-    const int step = 2 * kScoreWaves * kEntriesPerWaveStep;
-    long long want = ((long long)n_max * n_queries + 1023) / 1024;
-    long long c = ((want + step - 1) / step) * step;
-    if (c < step) c = step;
-    if (c > 8192) c = 8192;
-    return (int)c;
+int score_workgroups(int n_max, int n_queries) {
+    // about one workgroup per CU over the launch, at most one per workgroup step
+    int per_query = (kTargetWgs + n_queries - 1) / n_queries;
+    const int steps = (n_max + kWgStep - 1) / kWgStep;
+    if (per_query > steps) per_query = steps;
+    return per_query < 1 ? 1 : per_query;
 }
 
 }  // namespace csa

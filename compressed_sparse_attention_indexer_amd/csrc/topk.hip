@@ -335,8 +335,8 @@ __global__ __launch_bounds__(kAuxThreads) void topk_hist_kernel(TopkArgs a) {
     for (int i = threadIdx.x; i < kTopkBins; i += kAuxThreads) lh[i] = 0u;
     __syncthreads();
     const float *row = a.scores + (size_t)qi * a.n_max;
-    const int j0 = blockIdx.x * a.win_chunk;
-    const int j1 = j0 + a.win_chunk < n ? j0 + a.win_chunk : n;
+    const int j0 = blockIdx.x * kTopkAuxChunk;
+    const int j1 = j0 + kTopkAuxChunk < n ? j0 + kTopkAuxChunk : n;
     for (int jb = j0; jb < j1; jb += kTopkAuxChunk) {
         float v[kPerThread];
 #pragma unroll
@@ -565,14 +565,14 @@ __global__ __launch_bounds__(kWG) void topk_final_kernel(TopkArgs a, int n_flt) 
 // ---------------------------------------------------------------------------
 bool topk_uses_histogram(int n_max) { return n_max > kTopkSmallMax; }
 
-static int n_windows(int n_max, int win_chunk) { return (n_max + win_chunk - 1) / win_chunk; }
 static int n_filters(int n_max) { return (n_max + kTopkAuxChunk - 1) / kTopkAuxChunk; }
+static int n_windows(int n_max, int n_win) { return n_win > 0 ? n_win : n_filters(n_max); }
 
-size_t topk_workspace_bytes(int n_queries, int K, int n_max, int win_chunk) {
+size_t topk_workspace_bytes(int n_queries, int K, int n_max, int n_win) {
     (void)K;
     if (!topk_uses_histogram(n_max)) return 0;
     const size_t Q = (size_t)n_queries;
-    const size_t nw = (size_t)n_windows(n_max, win_chunk);
+    const size_t nw = (size_t)n_windows(n_max, n_win);
     size_t b = Q * nw * 4 + Q * nw * kTopkWin * 4 + Q * 4 + 4 * 256;
     if (n_max > kTopkOneKernelMax) b += Q * (size_t)n_filters(n_max) * kFltRegionWords * 4;
     return b;
@@ -580,9 +580,8 @@ size_t topk_workspace_bytes(int n_queries, int K, int n_max, int win_chunk) {
 
 static inline char *align256(char *p) { return (char *)(((uintptr_t)p + 255) & ~(uintptr_t)255); }
 
-void topk_carve(TopkArgs &a, void *ws, int n_queries, int win_chunk) {
-    a.win_chunk = win_chunk;
-    a.n_win = n_windows(a.n_max, win_chunk);
+void topk_carve(TopkArgs &a, void *ws, int n_queries, int n_win) {
+    a.n_win = n_windows(a.n_max, n_win);
     if (!topk_uses_histogram(a.n_max)) return;
     const size_t Q = (size_t)n_queries;
     char *p = align256((char *)ws);
