@@ -16,6 +16,17 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
+// Pointers read out of device pointer arrays are generic; loads through them
+// compile to flat loads, which also count against the LDS wait counter.
+// Reading through an explicit global (address space 1) pointer keeps them
+// global loads, so LDS waits do not drain the memory pipeline.
+template <typename T>
+using gptr = const __attribute__((address_space(1))) T *;
+template <typename T>
+__device__ __forceinline__ gptr<T> as_global(const void *p) {
+    return (gptr<T>)p;
+}
+
 // Number of compressed entries a query at raw position p sees: entry j covers
 // raw tokens [r*j, r*j+r-1] and is visible iff r*j+r-1 <= p and j < L/r.
 __device__ __forceinline__ int visible_entries(int64_t seq_len, int64_t pos, int ratio) {

@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) void index_scores_f32_kernel(ScoreArgs a) {
 // 16-head row tiles) x 128 dims (four k-steps of 32) on
 // v_mfma_f32_16x16x32_bf16.  A = index query (heads x dims, resident in
 // registers), B = index keys (dims x entries) loaded straight from HBM into
-// registers with nontemporal loads, two steps ahead of the step being
+// registers with nontemporal loads, one step ahead of the step being
 // computed.  Lane (e, g) of a tile holds dims [32s + 8g, 32s + 8g + 8) of
 // entry e for k-step s, so each load instruction reads 64 contiguous bytes of
 // every entry it touches.  The C tile gives each lane 4 heads of one entry;
@@ -68,10 +68,11 @@ constexpr int kScoreWaves = 4;
 constexpr int kWaveStep = 32;                         // entries per wave and step
 constexpr int kWgStep = kScoreWaves * kWaveStep;      // entries per workgroup step
 constexpr int kTargetWgs = 256;                       // about one workgroup per CU
+constexpr int kScoreDepth = 2;                        // key steps in flight per wave
 typedef bf16x8_t KeyFrag[2][4];
 }  // namespace
 
-template <int kAct, bool kHist>
+template <int kAct, bool kHist, int kDepth>
 __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(ScoreArgs a) {
     __shared__ uint32_t lh[kHist ? kTopkBins : 1];
     __shared__ int s_red[4];
@@ -108,28 +109,29 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(
 
     const uint16_t *kb = (const uint16_t *)a.k_idx[b];
     const int last = nvis > 0 ? nvis - 1 : 0;
-    // step k of this wave starts at entry base(k)
+    // step k of this wave starts at entry base0 + k * stride
     const int stride = gridDim.x * kWgStep;
     const int base0 = blockIdx.x * kWgStep + wave * kWaveStep;
+    const int n_steps = base0 < a.n_max ? (a.n_max - base0 + stride - 1) / stride : 0;
+    // steps that hold a visible entry come first: 0 .. n_load-1
+    const int n_load = base0 < nvis ? (nvis - base0 + stride - 1) / stride : 0;
 
+    // Every load is unconditional (indices clamped into the visible rows) so
+    // the loop body is straight-line code and the compiler can wait for one
+    // step's loads while the next step's are still in flight.
     auto load = [&](KeyFrag &kf, int base) {
-        if (base >= nvis) return;  // nothing visible: not loaded, not used
-        const bool full = base + kWaveStep <= nvis;
 #pragma unroll
         for (int et = 0; et < 2; ++et) {
             int j = base + 16 * et + e;
-            if (!full) j = j < nvis ? j : last;  // clamp: loaded but discarded
-            const bf16x8_t *kr = (const bf16x8_t *)(kb + (size_t)j * kDI + 8 * g);
+            j = j < nvis ? j : last;
+            const gptr<bf16x8_t> kr = as_global<bf16x8_t>(kb + (size_t)j * kDI + 8 * g);
 #pragma unroll
             for (int s = 0; s < 4; ++s) kf[et][s] = __builtin_nontemporal_load(kr + 4 * s);
         }
     };
-    auto process = [&](const KeyFrag &kf, int base) {
+    // `live`: the step exists (a clamped re-run of the last step stores nothing)
+    auto process = [&](const KeyFrag &kf, int base, bool live) {
         const int j = base + 16 * g + e;  // entry this lane stores (g < 2)
-        if (base >= nvis) {               // nothing visible in this step
-            if (g < 2 && j < a.n_max) srow[j] = -INFINITY;
-            return;
-        }
         float part[2];
 #pragma unroll
         for (int et = 0; et < 2; ++et) {
@@ -155,23 +157,30 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(
         }
         // Lanes of group g < 2 store column tile g: 32 consecutive scores.
         const float sv = j < nvis ? (g == 0 ? part[0] : part[1]) : -INFINITY;
-        if (g < 2 && j < a.n_max) srow[j] = sv;
-        if (with_hist) lds_hist_add(lh, order_key(sv) >> 20, g < 2 && j < nvis);
+        if (live && g < 2 && j < a.n_max) srow[j] = sv;
+        if (with_hist) lds_hist_add(lh, order_key(sv) >> 20, live && g < 2 && j < nvis);
     };
 
-    // three register buffers: keys of steps k, k+1, k+2 in flight
-    KeyFrag k0, k1, k2;
-    load(k0, base0);
-    load(k1, base0 + stride);
-    for (int base = base0; base < a.n_max; base += 3 * stride) {
-        load(k2, base + 2 * stride);
-        process(k0, base);
-        if (base + stride >= a.n_max) break;
-        load(k0, base + 3 * stride);
-        process(k1, base + stride);
-        if (base + 2 * stride >= a.n_max) break;
-        load(k1, base + 4 * stride);
-        process(k2, base + 2 * stride);
+    if (n_load > 0) {
+        // Software pipeline kDepth steps deep, unrolled by kDepth so that no
+        // load sits behind a branch: while step k computes, the loads of steps
+        // k+1 .. k+kDepth-1 are in flight.  Steps past the last one reload the
+        // last step and store nothing.
+        KeyFrag kbuf[kDepth];
+        auto step = [&](int k) { return base0 + (k < n_load ? k : n_load - 1) * stride; };
+#pragma unroll
+        for (int i = 0; i < kDepth; ++i) load(kbuf[i], step(i));
+        for (int k = 0; k < n_load; k += kDepth) {
+#pragma unroll
+            for (int i = 0; i < kDepth; ++i) {
+                process(kbuf[i], step(k + i), k + i < n_load);
+                load(kbuf[i], step(k + i + kDepth));
+            }
+        }
+    }
+    for (int k = n_load; k < n_steps; ++k) {  // steps past the visible entries: -inf
+        const int j = base0 + k * stride + 16 * g + e;
+        if (g < 2 && j < a.n_max) srow[j] = -INFINITY;
     }
     if (with_hist) {
         const size_t w = (size_t)qi * gridDim.x + blockIdx.x;
@@ -192,14 +201,14 @@ hipError_t launch_index_scores(const ScoreArgs &a, int dtype, hipStream_t stream
     const bool hist = a.win_hdr != nullptr;
     if (a.act == 0) {
         if (hist)
-            hipLaunchKernelGGL((index_scores_bf16_kernel<0, true>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((index_scores_bf16_kernel<0, true, kScoreDepth>), grid, block, 0, stream, a);
         else
-            hipLaunchKernelGGL((index_scores_bf16_kernel<0, false>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((index_scores_bf16_kernel<0, false, kScoreDepth>), grid, block, 0, stream, a);
     } else {
         if (hist)
-            hipLaunchKernelGGL((index_scores_bf16_kernel<1, true>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((index_scores_bf16_kernel<1, true, kScoreDepth>), grid, block, 0, stream, a);
         else
-            hipLaunchKernelGGL((index_scores_bf16_kernel<1, false>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((index_scores_bf16_kernel<1, false, kScoreDepth>), grid, block, 0, stream, a);
     }
     return hipGetLastError();
 }
