@@ -13,8 +13,9 @@
 //    below the largest key), finds the bin holding the K-th key, scans the row
 //    into "above" and "candidate" lists in LDS, selects among the candidates
 //    and writes the indices in order through an LDS bitmap.
-//  * longer rows: the threshold, the scan (many workgroups, each writing its
-//    own lists with plain stores) and the selection run as three kernels.
+//  * longer rows: many workgroups each merge the windows into the threshold
+//    and scan a slice of the row, writing their own lists with plain stores;
+//    one workgroup per query then gathers the lists and selects.
 // Every shortcut is checked (counts consistent, buffers not overflowed,
 // threshold inside the merged window); otherwise the exact whole-row radix
 // scan runs.  No step uses global atomics, and correctness never depends on
@@ -417,41 +418,40 @@ __global__ __launch_bounds__(kWG) void topk_onekernel_kernel(TopkArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Long rows: threshold kernel, many-workgroup scan, selection kernel.
-__global__ __launch_bounds__(kWG) void topk_thresh_kernel(TopkArgs a) {
-    __shared__ uint32_t s_hist[kTopkWin];
-    __shared__ int s_red[kWaves];
-    const int qi = blockIdx.x;
-    if (query_visible(a, qi) <= a.K) return;
-    const uint32_t bin = window_threshold(a.win_hdr + (size_t)qi * a.n_win,
-                                          a.win_cnt + (size_t)qi * a.n_win * kTopkWin, a.n_win, a.K, s_red, s_hist);
-    if (threadIdx.x == 0) a.bin[qi] = bin;
-}
-
-// Each workgroup writes its own region: [0] above count (0xFFFFFFFF when a
-// list overflowed), [1] candidate count, then the above list, candidate keys
-// and candidate indices.
+// Long rows: many-workgroup scan (with its own threshold merge), then selection.
+// Each filter workgroup first merges the query's histogram windows into the
+// threshold bin (the same result in every workgroup; its loads go out in the
+// same round as the workgroup's scores), then writes its own region:
+// [0] above count (0xFFFFFFFF when a list overflowed or there is no usable
+// threshold), [1] candidate count, then the above list, candidate keys and
+// candidate indices.
 __global__ __launch_bounds__(kAuxThreads) void topk_filter_kernel(TopkArgs a) {
     __shared__ int32_t l_above[kFltAboveCap];
     __shared__ uint32_t l_ckey[kFltCandCap];
     __shared__ int32_t l_cidx[kFltCandCap];
     __shared__ int l_cnt[2];
+    __shared__ uint32_t s_hist[kTopkWin];
+    __shared__ int s_red[4];
     const int qi = blockIdx.y;
     const int n = query_visible(a, qi);
-    if (n <= a.K) return;
-    const uint32_t bin = a.bin[qi];
-    uint32_t *reg = a.flt + ((size_t)qi * gridDim.x + blockIdx.x) * kFltRegionWords;
-    if (bin == kNoBin) return;
-    if (threadIdx.x < 2) l_cnt[threadIdx.x] = 0;
-    __syncthreads();
-    const float *row = a.scores + (size_t)qi * a.n_max;
     const int j0 = blockIdx.x * kTopkAuxChunk;
+    if (n <= a.K || j0 >= n) return;  // the selection reads regions below n only
+    uint32_t *reg = a.flt + ((size_t)qi * gridDim.x + blockIdx.x) * kFltRegionWords;
+    const float *row = a.scores + (size_t)qi * a.n_max;
     float x[kPerThread];
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
         const int j = j0 + k * kAuxThreads + threadIdx.x;
         x[k] = j < n ? row[j] : 0.f;
     }
+    const uint32_t bin = window_threshold(a.win_hdr + (size_t)qi * a.n_win,
+                                          a.win_cnt + (size_t)qi * a.n_win * kTopkWin, a.n_win, a.K, s_red, s_hist);
+    if (bin == kNoBin) {
+        if (threadIdx.x == 0) reg[0] = 0xFFFFFFFFu;
+        return;
+    }
+    if (threadIdx.x < 2) l_cnt[threadIdx.x] = 0;
+    __syncthreads();
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
         const int j = j0 + k * kAuxThreads + threadIdx.x;
@@ -500,7 +500,7 @@ __global__ __launch_bounds__(kWG) void topk_final_kernel(TopkArgs a, int n_flt) 
         for (int i = tid; i < K; i += kWG) out[i] = i < n ? i : -1;
         return;
     }
-    bool ok = a.bin[qi] != kNoBin;
+    bool ok = true;
     if (tid == 0) s_bad = 0;
     __syncthreads();
     // gather the filter lists of the workgroups that covered visible entries:
@@ -606,7 +606,6 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t stream, bool hist_done) {
         return hipGetLastError();
     }
     const int nf = n_filters(a.n_max);
-    hipLaunchKernelGGL(topk_thresh_kernel, dim3(Q), dim3(kWG), 0, stream, a);
     hipLaunchKernelGGL(topk_filter_kernel, dim3(nf, Q), dim3(kAuxThreads), 0, stream, a);
     hipLaunchKernelGGL(topk_final_kernel, dim3(Q), dim3(kWG), 0, stream, a, nf);
     return hipGetLastError();

@@ -52,25 +52,27 @@ __device__ __forceinline__ void hist_window_store(const uint32_t *lh, int32_t *h
 // Merge n_win windows (hdr[w], cnt[w][kTopkWin]) into the exact histogram of
 // the top kTopkWin bins below the global highest bin M, and return the bin
 // holding the K-th largest key (kNoBin if it lies below that range or there is
-// nothing).  Block of 1024 threads.  Loads are issued in two rounds (headers,
-// then up to 256 windows at a time) so latency is paid a few times, not per
-// window.  s_hist needs kTopkWin words, s_red 16.
+// nothing).  Any block size that is a multiple of 64 (up to 1024).  Loads go
+// out in two rounds (headers, then blockDim/4 windows at a time) so latency is
+// paid a few times, not per window.  s_hist needs kTopkWin words, s_red one
+// int per wave.
 __device__ __forceinline__ uint32_t window_threshold(const int32_t *hdr, const uint32_t *cnt, int n_win, int K,
                                                      int *s_red, uint32_t *s_hist) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nt = blockDim.x, nwaves = nt >> 6;
     int m = -1;
-    for (int w = tid; w < n_win; w += 1024) m = max(m, hdr[w]);
+    for (int w = tid; w < n_win; w += nt) m = max(m, hdr[w]);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) m = max(m, __shfl_xor(m, o));
     if (lane == 0) s_red[wave] = m;
-    if (tid < kTopkWin) s_hist[tid] = 0u;
+    for (int i = tid; i < kTopkWin; i += nt) s_hist[i] = 0u;
     __syncthreads();
     int M = -1;
-    for (int w = 0; w < 16; ++w) M = max(M, s_red[w]);
+    for (int w = 0; w < nwaves; ++w) M = max(M, s_red[w]);
     if (M < 0) return kNoBin;  // the same in every thread
     // 4 threads per window, 32 bins (8 x 16 bytes) each
     const int seg = tid & 3;
-    for (int w0 = 0; w0 < n_win; w0 += 256) {
+    for (int w0 = 0; w0 < n_win; w0 += nt >> 2) {
         const int w = w0 + (tid >> 2);
         int mw = -1;
         u32x4_t x[8];
@@ -81,7 +83,7 @@ __device__ __forceinline__ uint32_t window_threshold(const int32_t *hdr, const u
             for (int i = 0; i < 8; ++i) x[i] = src[i];
         }
         if (mw >= 0) {
-            const int off = mw - M + 32 * seg;  // global-window bin of this thread's first count
+            const int off = mw - M + 32 * seg;  // merged-window bin of this thread's first count
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
