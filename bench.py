@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "CSA decode queries/s at 64K–1M ctx; achieved HBM GB/s vs peak (1 GPU)"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # dense bf16 MFMA, MI355X datasheet
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_index_scores_decode_b4_1m.json")
 SCORER_SRC = os.path.join(ROOT, "compressed_sparse_attention_indexer_amd", "csrc", "scorer.hip")
 
@@ -58,6 +59,14 @@ def csa_step_bytes(n_ent, n_queries):
     """Per query: index keys 256 B/entry, q_idx 16 KiB, weights 256 B, q 64 KiB,
     512 selected + 128 window rows of 1 KiB, sink 256 B, fp32 output 128 KiB."""
     return int(sum(256 * int(n) for n in n_ent)) + 868864 * n_queries
+
+
+def visible_counts(case):
+    """Compressed entries each query sees (complete 4-token spans ending at or before its position)."""
+    import numpy as np
+    wl = case.wl
+    b = np.arange(wl.batch * wl.q_len) // wl.q_len
+    return np.minimum(case.seq_len[b] // wl.ratio, (case.q_pos.astype(np.int64) + 1) // wl.ratio)
 
 
 def scorer_bytes(n_ent, n_queries):
@@ -205,6 +214,11 @@ def bench_csa(torch, csa, case, args, detail):
         res["separate_entry_points_ms"], _, _ = time_graph(torch, g_s, gs, args.steps, args.warmup)
         res["kernel_ms"] = per
         res["scorer_alg_bytes"] = scorer_bytes(n_ent, Q)
+        # indexer flops: 2 * 64 heads * 128 dims per (query, visible entry)
+        nvis = visible_counts(case)
+        res["scorer_flops"] = 2 * r.dims.index_heads * r.dims.index_dim * int(nvis.sum())
+        res["scorer_TFLOPs"] = res["scorer_flops"] / (per["index_scores"] * 1e-3) / 1e12
+        res["scorer_frac_mfma_peak"] = res["scorer_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS
     return res, r
 
 

@@ -27,6 +27,8 @@ struct ScoreArgs {
 
 hipError_t launch_index_scores(const ScoreArgs &a, int dtype, hipStream_t stream);
 int score_workgroups(int n_max, int n_queries);  // bf16 scorer workgroups per query
+// many queries per sequence: the GEMM-tiled scorer (it writes no histogram windows)
+bool score_uses_tiles(int dtype, int T);
 
 constexpr int kTopkSmallMax = 4096;       // rows up to this length: one workgroup, row kept in LDS
 constexpr int kTopkOneKernelMax = 65536;  // rows up to this length: threshold+scan+select in one kernel

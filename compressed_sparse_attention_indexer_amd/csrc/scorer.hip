@@ -188,12 +188,212 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 MFMA scorer for many queries of one sequence (prefill chunk), HI = 64,
+// DI = 128.  Here the work is a dense contraction [queries*64 x 128] x
+// [128 x entries] with a per-(query, entry) epilogue, so it is tiled like a
+// GEMM: a workgroup of 4 waves (one per SIMD, so each may hold 512
+// registers) takes 8 consecutive queries of one sequence
+// (two per wave, their index vectors resident in registers as A fragments)
+// and a chunk of entries, which streams through LDS 64 entries at a time
+// (double-buffered, the next tile's global loads in flight while the current
+// one is computed).  Each B fragment read from LDS feeds 8 MFMAs (2 queries x
+// 4 head tiles).  Per 16-entry column tile and query, a lane holds 16 heads
+// of one entry; it folds them with the weights and activation in registers,
+// and one 3-exchange butterfly over the 4 lane groups leaves lane l with the
+// score of entry l of the 64-entry tile, stored as one coalesced 256-byte row
+// segment per query.
+//
+// Workgroup order: when the entry chunks come in multiples of 8, the
+// workgroups sharing an entry chunk are dealt to one XCD (hardware deals
+// consecutive workgroup ids round-robin over the 8 XCDs), so the key tiles
+// they stream are shared through that XCD's L2.
+namespace {
+constexpr int kPfWaves = 4;
+constexpr int kPfQueries = 2 * kPfWaves;     // queries per workgroup
+constexpr int kPfTile = 64;                  // entries per LDS tile
+constexpr int kPfRowWords = kDI / 2 + 4;     // LDS row: 128 bf16 + 16 B pad (conflict-free reads)
+constexpr int kPfTileWords = kPfTile * kPfRowWords;
+constexpr int kPfTargetWgs = 2048;           // about 8 workgroups per CU over the launch
+constexpr int kPfStage = kPfTile * (kDI / 8) / (64 * kPfWaves);  // 16-byte tile chunks per thread
+static_assert(kPfStage * 64 * kPfWaves == kPfTile * (kDI / 8), "tile staging covers the tile");
+}  // namespace
+
+struct TiledPlan {
+    int qb_per_seq;        // query blocks per sequence
+    int n_chunks;          // entry chunks
+    int tiles_per_chunk;
+};
+
+static TiledPlan tiled_plan(const ScoreArgs &a) {
+    TiledPlan p;
+    p.qb_per_seq = (a.T + kPfQueries - 1) / kPfQueries;
+    const int n_qb = a.B * p.qb_per_seq;
+    const int n_tiles = (a.n_max + kPfTile - 1) / kPfTile;
+    int want = (kPfTargetWgs + n_qb - 1) / n_qb;
+    if (want >= 8) want = (want + 7) / 8 * 8;
+    if (want > n_tiles) want = n_tiles;
+    if (want < 1) want = 1;
+    p.tiles_per_chunk = (n_tiles + want - 1) / want;
+    p.n_chunks = (n_tiles + p.tiles_per_chunk - 1) / p.tiles_per_chunk;
+    return p;
+}
+
+template <int kAct>
+__global__ __launch_bounds__(64 * kPfWaves, 1) void index_scores_tiled_kernel(ScoreArgs a, TiledPlan pl) {
+    __shared__ __attribute__((aligned(16))) uint32_t kt[2][kPfTileWords];
+    __shared__ int s_nv[kPfWaves];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int e = lane & 15, g = lane >> 4;
+
+    // workgroup -> (query block, entry chunk)
+    const int n_qb = a.B * pl.qb_per_seq;
+    int qb, ec;
+    if (pl.n_chunks % 8 == 0) {
+        const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+        qb = slot % n_qb;
+        ec = (slot / n_qb) * 8 + xcd;
+    } else {
+        qb = blockIdx.x % n_qb;
+        ec = blockIdx.x / n_qb;
+    }
+    const int b = qb / pl.qb_per_seq;
+    const int t0 = (qb % pl.qb_per_seq) * kPfQueries + 2 * wave;
+    const int64_t L = a.seq_len[b];
+
+    // this wave's two queries (a query past T repeats the last one and stores nothing)
+    int qi[2], nv[2];
+    bool qok[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int t = t0 + q;
+        qok[q] = t < a.T;
+        qi[q] = b * a.T + (qok[q] ? t : a.T - 1);
+        const int v = visible_entries(L, a.q_pos[qi[q]], a.ratio);
+        nv[q] = v < a.n_max ? v : a.n_max;
+    }
+    if (lane == 0) s_nv[wave] = max(qok[0] ? nv[0] : 0, qok[1] ? nv[1] : 0);
+
+    bf16x8_t qa[2][4][4];
+    float wr[2][4][4];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const uint16_t *qsrc = (const uint16_t *)a.q_idx + (size_t)qi[q] * kHI * kDI;
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                qa[q][ht][s] = *(const bf16x8_t *)(qsrc + (16 * ht + e) * kDI + 32 * s + 8 * g);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) wr[q][ht][r] = a.w[(size_t)qi[q] * kHI + 16 * ht + 4 * g + r];
+        }
+    }
+    __syncthreads();
+    int nv_max = 0;
+#pragma unroll
+    for (int w = 0; w < kPfWaves; ++w) nv_max = max(nv_max, s_nv[w]);
+
+    const int j0 = ec * pl.tiles_per_chunk * kPfTile;
+    const int j_end = min(j0 + pl.tiles_per_chunk * kPfTile, a.n_max);
+    // tiles holding an entry some query of the block sees
+    const int n_ct = nv_max > j0 ? (min(j_end, nv_max) - j0 + kPfTile - 1) / kPfTile : 0;
+    const uint16_t *kb = (const uint16_t *)a.k_idx[b];
+    const int last = nv_max > 0 ? nv_max - 1 : 0;
+
+    // staging: thread -> kPfStage chunks of 16 bytes (entry c/16, dims 8*(c%16) .. +8)
+    u32x4_t st[kPfStage];
+    auto fetch = [&](int tile) {
+#pragma unroll
+        for (int u = 0; u < kPfStage; ++u) {
+            const int c = tid + 64 * kPfWaves * u;
+            int j = j0 + tile * kPfTile + (c >> 4);
+            j = j < nv_max ? j : last;
+            st[u] = *as_global<u32x4_t>(kb + (size_t)j * kDI + 8 * (c & 15));
+        }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < kPfStage; ++u) {
+            const int c = tid + 64 * kPfWaves * u;
+            *(u32x4_t *)&kt[buf][(c >> 4) * kPfRowWords + 4 * (c & 15)] = st[u];
+        }
+    };
+
+    if (n_ct > 0) fetch(0);
+    for (int tile = 0; tile < n_ct; ++tile) {
+        const int buf = tile & 1;
+        stash(buf);
+        if (tile + 1 < n_ct) fetch(tile + 1);
+        __syncthreads();
+        float p[2][4];
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) {
+            bf16x8_t kf[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                kf[s] = *(const bf16x8_t *)&kt[buf][(16 * sb + e) * kPfRowWords + 16 * s + 4 * g];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                f32x4_t acc[4];
+#pragma unroll
+                for (int ht = 0; ht < 4; ++ht) {
+                    acc[ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[q][ht][s], kf[s], acc[ht], 0, 0, 0);
+                }
+                float x = 0.f;
+#pragma unroll
+                for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float c = acc[ht][r];
+                        x = fmaf(wr[q][ht][r], kAct == 0 ? fmaxf(c, 0.f) : c, x);
+                    }
+                p[q][sb] = x;  // entry 16*sb + e, heads of lane group g
+            }
+        }
+        // butterfly over the lane groups: lane 16g + e ends with entry 16g + e summed over all heads
+        const int hi = g >> 1, lo = g & 1;
+        const int j = j0 + tile * kPfTile + lane;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            float k2[2];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const float send = hi ? p[q][k] : p[q][2 + k];
+                const float mine = hi ? p[q][2 + k] : p[q][k];
+                k2[k] = mine + __shfl_xor(send, 32);
+            }
+            const float send = lo ? k2[0] : k2[1];
+            const float tot = (lo ? k2[1] : k2[0]) + __shfl_xor(send, 16);
+            if (qok[q] && j < a.n_max) a.scores[(size_t)qi[q] * a.n_max + j] = j < nv[q] ? tot : -INFINITY;
+        }
+    }
+    // entries of the chunk no query of the block sees
+    for (int jj = j0 + n_ct * kPfTile + lane; jj < j_end; jj += 64)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            if (qok[q]) a.scores[(size_t)qi[q] * a.n_max + jj] = -INFINITY;
+}
+
+bool score_uses_tiles(int dtype, int T) { return dtype == kBF16 && T >= kPfQueries; }
+
 hipError_t launch_index_scores(const ScoreArgs &a, int dtype, hipStream_t stream) {
     const int Q = a.B * a.T;
     if (dtype == kF32) {
         dim3 grid((a.n_max + 255) / 256, Q);
         const size_t lds = sizeof(float) * (size_t)(a.HI * a.DI + a.HI);
         hipLaunchKernelGGL(index_scores_f32_kernel, grid, dim3(256), lds, stream, a);
+        return hipGetLastError();
+    }
+    if (score_uses_tiles(dtype, a.T)) {
+        const TiledPlan pl = tiled_plan(a);
+        const dim3 grid(a.B * pl.qb_per_seq * pl.n_chunks);
+        if (a.act == 0)
+            hipLaunchKernelGGL(index_scores_tiled_kernel<0>, grid, dim3(64 * kPfWaves), 0, stream, a, pl);
+        else
+            hipLaunchKernelGGL(index_scores_tiled_kernel<1>, grid, dim3(64 * kPfWaves), 0, stream, a, pl);
         return hipGetLastError();
     }
     dim3 grid(score_workgroups(a.n_max, Q), Q);

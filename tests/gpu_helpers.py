@@ -121,3 +121,14 @@ def flash_case(name, seq_lens, *, batch=None, q_len=1, q_pos0=None, topk=512, wi
 
 def make_case_with_lens(wl, seq_lens):
     return inputs.make_case(wl, seq_lens=seq_lens)
+
+
+def query_subset(case, ts):
+    """The same inputs restricted to queries ts of a single-sequence case (the
+    oracle then evaluates only those queries)."""
+    import dataclasses
+    assert case.wl.batch == 1
+    ts = np.asarray(ts)
+    wl = dataclasses.replace(case.wl, q_len=len(ts))
+    return dataclasses.replace(case, wl=wl, q_pos=case.q_pos[ts].copy(), q=case.q[:, ts].copy(),
+                               q_idx=case.q_idx[:, ts].copy(), w=case.w[:, ts].copy())

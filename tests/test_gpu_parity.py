@@ -15,8 +15,8 @@ import pytest
 import oracle
 from compressed_sparse_attention_indexer_amd import inputs
 from tests.gpu_helpers import (ATT_TOL_BF16, ATT_TOL_F32, assert_attention_close, assert_scores_close,
-                               assert_topk_band, flash_case, make_case_with_lens, nvis_of, oracle_hca,
-                               oracle_scores, oracle_sparse, say)
+                               assert_topk_band, check_topk_valid, flash_case, make_case_with_lens, nvis_of,
+                               oracle_hca, oracle_scores, oracle_sparse, query_subset, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -28,6 +28,18 @@ from compressed_sparse_attention_indexer_amd.staging import DeviceCase  # noqa: 
 def _np(t):
     torch.cuda.synchronize()
     return t.detach().cpu().numpy()
+
+
+def run_fused_t(dc, act=csa.CSA_ACT_RELU):
+    """csa_attention with the intermediate scores and indices exposed (device tensors)."""
+    dims = dc.csa_dims(index_act=act)
+    scores = torch.empty((dims.batch, dims.q_len, dims.max_entries), dtype=torch.float32, device="cuda")
+    idx = torch.empty((dims.batch, dims.q_len, dims.topk), dtype=torch.int32, device="cuda")
+    out, lse = csa.csa_attention(dims, dc.q, dc.q_idx, dc.w, dc.k_idx_p, dc.kv_p, dc.v_p, dc.win_p, dc.win_v_p,
+                                 dc.win_pos0, dc.win_rows, dc.seq_len, dc.q_pos, dc.sink, topk_idx_out=idx,
+                                 scores_out=scores)
+    torch.cuda.synchronize()
+    return scores, idx, out, lse
 
 
 def run_fused(dc, act=csa.CSA_ACT_RELU):
@@ -274,6 +286,23 @@ def test_deterministic_and_no_out_of_bounds_writes():
     np.testing.assert_array_equal(res[0][1], res[1][1])
 
 
+# --------------------------------------------------------------------------- prefill chunk (many queries)
+
+@pytest.mark.parametrize("lens,T,q_pos0", [
+    ([4 * 3000 + 2], 48, 4 * 3000 + 2 - 48),          # 3 query blocks; the causal edge inside the last tile
+    ([4 * 2500 + 1, 4 * 1700 + 3], 20, 4 * 1700 - 20),  # two ragged sequences, a partial query block
+    ([4 * 64 * 40], 16, 4 * 64 * 40 - 16),             # one query block; entries a whole number of tiles
+])
+def test_prefill_chunk_small(lens, T, q_pos0):
+    wl, sl = flash_case(f"prefill_small_{len(lens)}_{T}", lens, q_len=T, q_pos0=q_pos0)
+    check_whole_step(make_case_with_lens(wl, sl), ATT_TOL_BF16)
+
+
+def test_prefill_chunk_no_activation():
+    wl, sl = flash_case("prefill_noact", [4 * 1500 + 3], q_len=33, q_pos0=4 * 1500 + 3 - 40)
+    check_whole_step(make_case_with_lens(wl, sl), ATT_TOL_BF16, act=csa.CSA_ACT_NONE)
+
+
 # --------------------------------------------------------------------------- full-size workloads
 
 def test_decode_b1_64k_full():
@@ -293,3 +322,40 @@ def test_decode_b4_1m_full_csa_and_hca():
     o_out, o_lse = oracle_hca(case)
     assert_attention_close(_np(out), o_out, ATT_TOL_BF16, "hca out")
     np.testing.assert_allclose(_np(lse), o_lse, atol=1e-3, rtol=0)
+
+
+def test_prefill_t2048_1m_sampled():
+    """The 2,048-query chunk over a 1M-token cache at full size: every query's
+    selection is checked for validity and every score row for its causal
+    mask; sampled queries (both ends, query-block edges) are compared with
+    the oracle: scores, the selected set, and attention on that set."""
+    case = inputs.make_case(inputs.WORKLOADS["prefill_t2048_1m"], with_hca=False)
+    wl = case.wl
+    say(f"[case] {wl.name} T={wl.q_len} max_entries={case.max_entries}")
+    dc = DeviceCase(case)
+    scores, idx, out, lse = run_fused_t(dc)
+    nvis = np.array([nvis_of(case, t) for t in range(wl.q_len)])
+    # properties of every query
+    nv_t = torch.from_numpy(nvis).cuda()
+    col = torch.arange(case.max_entries, device="cuda")
+    row = scores[0]
+    masked = col[None, :] >= nv_t[:, None]
+    assert bool(torch.isneginf(row[masked]).all()), "causal mask"
+    assert bool(torch.isfinite(row[~masked]).all()), "visible scores finite"
+    del masked
+    g_idx = idx.cpu().numpy()
+    for t in range(wl.q_len):
+        check_topk_valid(g_idx[0, t], int(nvis[t]), wl.topk)
+    assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all())
+    # sampled queries against the oracle
+    ts = [0, 1, 15, 16, 1000, 2046, 2047]
+    sub = query_subset(case, ts)
+    o_scores = oracle_scores(sub)
+    g_sub = row[ts].cpu().numpy()[None]
+    assert_scores_close(g_sub, o_scores, sub)
+    o_idx = oracle.topk(o_scores, sub.seq_len, sub.q_pos, ratio=wl.ratio, k=wl.topk)
+    n_diff = assert_topk_band(g_idx[:, ts], o_idx, o_scores, sub)
+    o_out, o_lse = oracle_sparse(sub, g_idx[:, ts])
+    rel = assert_attention_close(out[:, ts].cpu().numpy(), o_out, ATT_TOL_BF16, "out")
+    np.testing.assert_allclose(lse[:, ts].cpu().numpy(), o_lse, atol=1e-3, rtol=0)
+    say(f"  ok: sampled {len(ts)} queries, topk band swaps={n_diff} out err/rms={rel:.2e}")
