@@ -40,6 +40,7 @@ constexpr int kTopkAuxChunk = 2048;       // scores per workgroup in the histogr
 constexpr int kFltAboveCap = 64;          // per filter workgroup: entries above the threshold bin
 constexpr int kFltCandCap = 256;          // per filter workgroup: candidates inside it
 constexpr int kFltRegionWords = 2 + kFltAboveCap + 2 * kFltCandCap;
+constexpr int kTopkManyQueries = 256;     // from this many queries on: one selecting workgroup per query
 
 struct TopkArgs {
     const float *scores;        // [Q, n_max]
@@ -49,6 +50,7 @@ struct TopkArgs {
     int B, T, ratio, K, n_max;
     // scratch inside the caller's workspace (rows longer than kTopkSmallMax)
     int n_win;                  // histogram windows per query
+    int hist_chunk;             // entries per window when the top-k builds its own histograms
     int32_t *win_hdr;           // [Q, n_win]
     uint32_t *win_cnt;          // [Q, n_win, kTopkWin]
     uint32_t *bin;              // [Q] threshold bin (long rows)

@@ -42,6 +42,16 @@ __global__ __launch_bounds__(256) void index_scores_f32_kernel(ScoreArgs a) {
     *dst = s;
 }
 
+// Indexer activation on an MFMA result: ReLU (kAct 0) or identity.  ReLU is
+// a signed-integer max with 0 on the bit pattern (negative floats, -0.0
+// included, are negative integers and become +0.0): one instruction, where
+// fmaxf would first canonicalize its operand (MFMA results are not known to
+// be canonical) and so take two.
+template <int kAct>
+__device__ __forceinline__ float index_act(float x) {
+    return kAct == 0 ? __int_as_float(max(__float_as_int(x), 0)) : x;
+}
+
 // ---------------------------------------------------------------------------
 // bf16 MFMA decode scorer, HI = 64 heads, DI = 128.
 //
@@ -148,8 +158,7 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(
             for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float x = acc[ht][r];
-                    p = fmaf(wr[ht][r], kAct == 0 ? fmaxf(x, 0.f) : x, p);
+                    p = fmaf(wr[ht][r], index_act<kAct>(acc[ht][r]), p);
                 }
             p += __shfl_xor(p, 16);
             p += __shfl_xor(p, 32);
@@ -192,31 +201,33 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(
 // bf16 MFMA scorer for many queries of one sequence (prefill chunk), HI = 64,
 // DI = 128.  Here the work is a dense contraction [queries*64 x 128] x
 // [128 x entries] with a per-(query, entry) epilogue, so it is tiled like a
-// GEMM: a workgroup of 4 waves (one per SIMD, so each may hold 512
-// registers) takes 8 consecutive queries of one sequence
-// (two per wave, their index vectors resident in registers as A fragments)
-// and a chunk of entries, which streams through LDS 64 entries at a time
-// (double-buffered, the next tile's global loads in flight while the current
-// one is computed).  Each B fragment read from LDS feeds 8 MFMAs (2 queries x
-// 4 head tiles).  Per 16-entry column tile and query, a lane holds 16 heads
-// of one entry; it folds them with the weights and activation in registers,
-// and one 3-exchange butterfly over the 4 lane groups leaves lane l with the
-// score of entry l of the 64-entry tile, stored as one coalesced 256-byte row
-// segment per query.
+// GEMM: a workgroup of 8 waves takes 8 consecutive queries of one sequence
+// (one per wave, its 64 x 128 index matrix resident in registers as A
+// fragments) and a chunk of entries, which streams through LDS 128 entries at
+// a time (double-buffered, the next tile's global loads in flight while the
+// current one is computed).  Each B fragment read from LDS feeds 4 MFMAs (the
+// 4 head tiles).  Per 16-entry column tile, a lane holds 16 heads of one
+// entry; it folds them with the weights and activation in registers, and a
+// 3-exchange butterfly over the 4 lane groups leaves lane l with the score of
+// entry l of each 64-entry group, stored as one coalesced 256-byte row
+// segment.  The per-element epilogue (activation + weighted add: two VALU
+// instructions per 256 MFMA flops) runs beside the other wave's MFMAs.
 //
 // Workgroup order: when the entry chunks come in multiples of 8, the
 // workgroups sharing an entry chunk are dealt to one XCD (hardware deals
 // consecutive workgroup ids round-robin over the 8 XCDs), so the key tiles
 // they stream are shared through that XCD's L2.
 namespace {
-constexpr int kPfWaves = 4;
-constexpr int kPfQueries = 2 * kPfWaves;     // queries per workgroup
-constexpr int kPfTile = 64;                  // entries per LDS tile
+constexpr int kPfWaves = 8;                  // two waves per SIMD
+constexpr int kPfQW = 1;                     // queries per wave
+constexpr int kPfQueries = kPfQW * kPfWaves; // queries per workgroup
+constexpr int kPfTile = 128;                 // entries per LDS tile
 constexpr int kPfRowWords = kDI / 2 + 4;     // LDS row: 128 bf16 + 16 B pad (conflict-free reads)
 constexpr int kPfTileWords = kPfTile * kPfRowWords;
 constexpr int kPfTargetWgs = 2048;           // about 8 workgroups per CU over the launch
 constexpr int kPfStage = kPfTile * (kDI / 8) / (64 * kPfWaves);  // 16-byte tile chunks per thread
 static_assert(kPfStage * 64 * kPfWaves == kPfTile * (kDI / 8), "tile staging covers the tile");
+static_assert(kPfTile % 64 == 0, "whole 64-entry groups per tile");
 }  // namespace
 
 struct TiledPlan {
@@ -258,26 +269,28 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void index_scores_tiled_kernel(Sc
         ec = blockIdx.x / n_qb;
     }
     const int b = qb / pl.qb_per_seq;
-    const int t0 = (qb % pl.qb_per_seq) * kPfQueries + 2 * wave;
+    const int t0 = (qb % pl.qb_per_seq) * kPfQueries + kPfQW * wave;
     const int64_t L = a.seq_len[b];
 
-    // this wave's two queries (a query past T repeats the last one and stores nothing)
-    int qi[2], nv[2];
-    bool qok[2];
+    // this wave's queries (a query past T repeats the last one and stores nothing)
+    int qi[kPfQW], nv[kPfQW];
+    bool qok[kPfQW];
+    int nv_wave = 0;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < kPfQW; ++q) {
         const int t = t0 + q;
         qok[q] = t < a.T;
         qi[q] = b * a.T + (qok[q] ? t : a.T - 1);
         const int v = visible_entries(L, a.q_pos[qi[q]], a.ratio);
         nv[q] = v < a.n_max ? v : a.n_max;
+        if (qok[q]) nv_wave = max(nv_wave, nv[q]);
     }
-    if (lane == 0) s_nv[wave] = max(qok[0] ? nv[0] : 0, qok[1] ? nv[1] : 0);
+    if (lane == 0) s_nv[wave] = nv_wave;
 
-    bf16x8_t qa[2][4][4];
-    float wr[2][4][4];
+    bf16x8_t qa[kPfQW][4][4];
+    float wr[kPfQW][4][4];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < kPfQW; ++q) {
         const uint16_t *qsrc = (const uint16_t *)a.q_idx + (size_t)qi[q] * kHI * kDI;
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) {
@@ -325,55 +338,55 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void index_scores_tiled_kernel(Sc
         stash(buf);
         if (tile + 1 < n_ct) fetch(tile + 1);
         __syncthreads();
-        float p[2][4];
 #pragma unroll
-        for (int sb = 0; sb < 4; ++sb) {
-            bf16x8_t kf[4];
+        for (int grp = 0; grp < kPfTile / 64; ++grp) {  // 64 entries: one butterfly and store
+            float p[kPfQW][4];
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                kf[s] = *(const bf16x8_t *)&kt[buf][(16 * sb + e) * kPfRowWords + 16 * s + 4 * g];
+            for (int sb = 0; sb < 4; ++sb) {
+                bf16x8_t kf[4];
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                f32x4_t acc[4];
+                for (int s = 0; s < 4; ++s)
+                    kf[s] = *(const bf16x8_t *)&kt[buf][(64 * grp + 16 * sb + e) * kPfRowWords + 16 * s + 4 * g];
 #pragma unroll
-                for (int ht = 0; ht < 4; ++ht) {
-                    acc[ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                for (int q = 0; q < kPfQW; ++q) {
+                    f32x4_t acc[4];
 #pragma unroll
-                    for (int s = 0; s < 4; ++s)
-                        acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[q][ht][s], kf[s], acc[ht], 0, 0, 0);
-                }
-                float x = 0.f;
+                    for (int ht = 0; ht < 4; ++ht) {
+                        acc[ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ht = 0; ht < 4; ++ht)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float c = acc[ht][r];
-                        x = fmaf(wr[q][ht][r], kAct == 0 ? fmaxf(c, 0.f) : c, x);
+                        for (int s = 0; s < 4; ++s)
+                            acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[q][ht][s], kf[s], acc[ht], 0, 0, 0);
                     }
-                p[q][sb] = x;  // entry 16*sb + e, heads of lane group g
-            }
-        }
-        // butterfly over the lane groups: lane 16g + e ends with entry 16g + e summed over all heads
-        const int hi = g >> 1, lo = g & 1;
-        const int j = j0 + tile * kPfTile + lane;
+                    float x = 0.f;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            float k2[2];
+                    for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const float send = hi ? p[q][k] : p[q][2 + k];
-                const float mine = hi ? p[q][2 + k] : p[q][k];
-                k2[k] = mine + __shfl_xor(send, 32);
+                        for (int r = 0; r < 4; ++r) x = fmaf(wr[q][ht][r], index_act<kAct>(acc[ht][r]), x);
+                    p[q][sb] = x;  // entry 16*sb + e, heads of lane group g
+                }
             }
-            const float send = lo ? k2[0] : k2[1];
-            const float tot = (lo ? k2[1] : k2[0]) + __shfl_xor(send, 16);
-            if (qok[q] && j < a.n_max) a.scores[(size_t)qi[q] * a.n_max + j] = j < nv[q] ? tot : -INFINITY;
+            // butterfly over the lane groups: lane 16g + e ends with entry 16g + e summed over all heads
+            const int hi = g >> 1, lo = g & 1;
+            const int j = j0 + tile * kPfTile + 64 * grp + lane;
+#pragma unroll
+            for (int q = 0; q < kPfQW; ++q) {
+                float k2[2];
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const float send = hi ? p[q][k] : p[q][2 + k];
+                    const float mine = hi ? p[q][2 + k] : p[q][k];
+                    k2[k] = mine + __shfl_xor(send, 32);
+                }
+                const float send = lo ? k2[0] : k2[1];
+                const float tot = (lo ? k2[1] : k2[0]) + __shfl_xor(send, 16);
+                if (qok[q] && j < a.n_max) a.scores[(size_t)qi[q] * a.n_max + j] = j < nv[q] ? tot : -INFINITY;
+            }
         }
     }
     // entries of the chunk no query of the block sees
     for (int jj = j0 + n_ct * kPfTile + lane; jj < j_end; jj += 64)
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
+        for (int q = 0; q < kPfQW; ++q)
             if (qok[q]) a.scores[(size_t)qi[q] * a.n_max + jj] = -INFINITY;
 }
 

@@ -336,8 +336,8 @@ __global__ __launch_bounds__(kAuxThreads) void topk_hist_kernel(TopkArgs a) {
     for (int i = threadIdx.x; i < kTopkBins; i += kAuxThreads) lh[i] = 0u;
     __syncthreads();
     const float *row = a.scores + (size_t)qi * a.n_max;
-    const int j0 = blockIdx.x * kTopkAuxChunk;
-    const int j1 = j0 + kTopkAuxChunk < n ? j0 + kTopkAuxChunk : n;
+    const int j0 = blockIdx.x * a.hist_chunk;
+    const int j1 = j0 + a.hist_chunk < n ? j0 + a.hist_chunk : n;
     for (int jb = j0; jb < j1; jb += kTopkAuxChunk) {
         float v[kPerThread];
 #pragma unroll
@@ -356,7 +356,8 @@ __global__ __launch_bounds__(kAuxThreads) void topk_hist_kernel(TopkArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Rows up to kTopkOneKernelMax: threshold, scan and selection in one workgroup.
+// One workgroup per query (rows up to kTopkOneKernelMax, or many queries):
+// threshold from the histogram windows, scan and selection.
 __global__ __launch_bounds__(kWG) void topk_onekernel_kernel(TopkArgs a) {
     __shared__ int32_t v[kTopkMaxK];
     __shared__ uint32_t c_key[kTopkCand];
@@ -566,22 +567,43 @@ __global__ __launch_bounds__(kWG) void topk_final_kernel(TopkArgs a, int n_flt) 
 bool topk_uses_histogram(int n_max) { return n_max > kTopkSmallMax; }
 
 static int n_filters(int n_max) { return (n_max + kTopkAuxChunk - 1) / kTopkAuxChunk; }
-static int n_windows(int n_max, int n_win) { return n_win > 0 ? n_win : n_filters(n_max); }
+// One selecting workgroup per query (no filter kernel) for rows that fit its
+// scan, and whenever there are enough queries to fill the GPU that way.
+static bool one_kernel(int n_max, int n_queries) {
+    return n_max <= kTopkOneKernelMax || n_queries >= kTopkManyQueries;
+}
+// Histogram windows per query: the scorer's workgroups when it builds them,
+// else one per 2,048-entry chunk, fewer (longer chunks) when many queries
+// already fill the GPU.
+static int n_windows(int n_max, int n_win, int n_queries) {
+    if (n_win > 0) return n_win;
+    int nw = n_filters(n_max);
+    if (n_queries >= kTopkManyQueries) {
+        const int want = 8192 / n_queries > 1 ? 8192 / n_queries : 1;
+        nw = nw < want ? nw : want;
+    }
+    return nw;
+}
+static int hist_chunk(int n_max, int nw) {
+    const int per = (n_max + nw - 1) / nw;
+    return (per + kTopkAuxChunk - 1) / kTopkAuxChunk * kTopkAuxChunk;
+}
 
 size_t topk_workspace_bytes(int n_queries, int K, int n_max, int n_win) {
     (void)K;
     if (!topk_uses_histogram(n_max)) return 0;
     const size_t Q = (size_t)n_queries;
-    const size_t nw = (size_t)n_windows(n_max, n_win);
+    const size_t nw = (size_t)n_windows(n_max, n_win, n_queries);
     size_t b = Q * nw * 4 + Q * nw * kTopkWin * 4 + Q * 4 + 4 * 256;
-    if (n_max > kTopkOneKernelMax) b += Q * (size_t)n_filters(n_max) * kFltRegionWords * 4;
+    if (!one_kernel(n_max, n_queries)) b += Q * (size_t)n_filters(n_max) * kFltRegionWords * 4;
     return b;
 }
 
 static inline char *align256(char *p) { return (char *)(((uintptr_t)p + 255) & ~(uintptr_t)255); }
 
 void topk_carve(TopkArgs &a, void *ws, int n_queries, int n_win) {
-    a.n_win = n_windows(a.n_max, n_win);
+    a.n_win = n_windows(a.n_max, n_win, n_queries);
+    a.hist_chunk = hist_chunk(a.n_max, a.n_win);
     if (!topk_uses_histogram(a.n_max)) return;
     const size_t Q = (size_t)n_queries;
     char *p = align256((char *)ws);
@@ -601,7 +623,7 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t stream, bool hist_done) {
         return hipGetLastError();
     }
     if (!hist_done) hipLaunchKernelGGL(topk_hist_kernel, dim3(a.n_win, Q), dim3(kAuxThreads), 0, stream, a);
-    if (a.n_max <= kTopkOneKernelMax) {
+    if (one_kernel(a.n_max, Q)) {
         hipLaunchKernelGGL(topk_onekernel_kernel, dim3(Q), dim3(kWG), 0, stream, a);
         return hipGetLastError();
     }

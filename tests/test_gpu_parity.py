@@ -158,6 +158,20 @@ def test_topk_exact(n_vis, n_max, K, ties):
     np.testing.assert_array_equal(got, want)
 
 
+@pytest.mark.parametrize("n_q,ties", [(300, False), (256, True)])
+def test_topk_many_long_rows(n_q, ties):
+    """Enough queries to fill the GPU with one selecting workgroup each: the
+    histogram windows then cover long chunks (rows over 65,536 entries)."""
+    n_vis = [70000 - 37 * i for i in range(n_q)]
+    say(f"[case] topk many rows n_q={n_q} ties={ties}")
+    scores, seq, pos = _topk_case(n_vis, 70000, 512, seed=n_q, ties=ties)
+    want = oracle.topk(scores, seq, pos, ratio=4, k=512)
+    dims = csa.make_dims(batch=n_q, topk=512, max_entries=70000)
+    got = _np(csa.csa_topk_select(dims, torch.from_numpy(scores).cuda(), torch.from_numpy(seq).cuda(),
+                                  torch.from_numpy(pos).cuda()))
+    np.testing.assert_array_equal(got, want)
+
+
 def test_topk_all_equal_scores_long_row():
     """Every score equal: the candidate bin overflows and the exact whole-row
     fallback must return indices 0..K-1."""
