@@ -300,7 +300,13 @@ def main():
         for i in range(args.steps):
             r.scores_call(i)
         torch.cuda.synchronize()
-        print(json.dumps({"profile_kernels": args.steps}))
+        # calibration for the byte counters: a plain device copy of 256 MiB
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_kernels": args.steps, "copy_bytes": src.numel() * 4}))
         return
 
     main_res, runner = bench_csa(torch, csa, case, args, detail=True)

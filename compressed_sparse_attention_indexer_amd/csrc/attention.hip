@@ -306,84 +306,143 @@ __global__ __launch_bounds__(128 * HG) void mqa_bf16_kernel(MqaArgs a) {
                 a.out[((size_t)qi * a.H + hbase + r) * kD + 256 * dh + 16 * dt + e] = o[dt][r] * fr[r];
         if (a.lse && dh == 0 && g == 0) a.lse[(size_t)qi * a.H + 16 * hg + e] = M * kLn2 + logf(lf);
     } else {
+        // Partial of this split: (m, l) per head, and O / l in fp16 stored the
+        // way the MFMA tiles lie in registers: the 16-byte vector at
+        // [qi, split, wave, dt pair p, lane] holds heads 16hg + 4g + r
+        // (r = 0..3) at dims 256dh + 16dt + e for dt = 2p and 2p + 1.
         const size_t ps = (size_t)qi * a.n_splits + split;
         if (dh == 0 && g == 0) {
             a.part_ml[(ps * a.H + 16 * hg + e) * 2 + 0] = m_run;
             a.part_ml[(ps * a.H + 16 * hg + e) * 2 + 1] = l_run;
         }
         if (ntiles > 0) {
+            const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+            float ir[4];
 #pragma unroll
-            for (int dt = 0; dt < 16; ++dt)
+            for (int r = 0; r < 4; ++r) ir[r] = __shfl(inv, 4 * g + r);
+            u32x4_t *dst = (u32x4_t *)a.part_o + (ps * 8 + wave) * 8 * 64 + lane;
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    a.part_o[(ps * a.H + hbase + r) * kD + 256 * dh + 16 * dt + e] = o[dt][r];
+            for (int p = 0; p < 8; ++p) {
+                uint32_t w4[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {  // word k: dt = 2p + k/2, heads r = 2(k%2), 2(k%2) + 1
+                    const int dt = 2 * p + (k >> 1), r = 2 * (k & 1);
+                    const _Float16 lo = (_Float16)(o[dt][r] * ir[r]);
+                    const _Float16 hi = (_Float16)(o[dt][r + 1] * ir[r + 1]);
+                    w4[k] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+                }
+                dst[p * 64] = u32x4_t{w4[0], w4[1], w4[2], w4[3]};
+            }
         }
     }
 }
 
-// Merge split partials with the sink, counted once: one workgroup per
-// (head, query), 128 threads x 4 output dims.
-__global__ __launch_bounds__(128) void mqa_combine_kernel(MqaArgs a) {
-    __shared__ float sw[1024];
-    __shared__ float red[2];
-    const int h = blockIdx.x, qi = blockIdx.y;
-    const int tid = threadIdx.x;
+// Merge split partials with the sink, counted once.  Workgroup = (16-head
+// group hg, lane group g, query): each of its 256 threads (dh, dt pair p,
+// column e) holds heads 16hg + 4g + r (r = 0..3) at two dims of every
+// split's partial, one 16-byte vector per split.  Wave r first turns head
+// h0 + r's (m, l) pairs into per-split weights and the total (lanes over the
+// splits; wave max and sum), into LDS; meanwhile the partial vectors of the
+// first 16 splits are already in flight.  Then every thread folds its
+// vectors, the next batch's loads issued before the current batch is used.
+// Splits without rows (l = 0) get weight 0; their vectors (never written)
+// are not used.
+constexpr int kCombineMaxSplits = 1024;
+__global__ __launch_bounds__(256) void mqa_combine_kernel(MqaArgs a) {
+    constexpr int kBatch = 16;
+    __shared__ float s_w[kCombineMaxSplits][4];
+    __shared__ float s_M[4], s_L[4];
+    const int qi = blockIdx.y;
+    const int hg = blockIdx.x >> 2, g = blockIdx.x & 3;
+    const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
+    const int dh = tid >> 7, p = (tid >> 4) & 7, e = tid & 15;
+    const int lane = 16 * g + e, wave = 2 * hg + dh;
+    const int h0 = 16 * hg + 4 * g;
     const int S = a.n_splits;
-    const float sink2 = a.sink[h] * kLog2e;
-    float M = sink2;
-    for (int s = tid; s < S; s += 128) {
-        const float m = a.part_ml[(((size_t)qi * S + s) * a.H + h) * 2 + 0];
-        const float l = a.part_ml[(((size_t)qi * S + s) * a.H + h) * 2 + 1];
-        if (l > 0.f) M = fmaxf(M, m);
-    }
-    M = wave_max(M);
-    if ((tid & 63) == 0) red[tid >> 6] = M;
-    __syncthreads();
-    M = fmaxf(red[0], red[1]);
-    __syncthreads();
-    float L = 0.f;
-    for (int s = tid; s < S; s += 128) {
-        const float m = a.part_ml[(((size_t)qi * S + s) * a.H + h) * 2 + 0];
-        const float l = a.part_ml[(((size_t)qi * S + s) * a.H + h) * 2 + 1];
-        const float wgt = l > 0.f ? exp2f(m - M) : 0.f;
-        if (s < 1024) sw[s] = wgt;
-        L += l * wgt;
-    }
-    L = wave_sum(L);
-    if ((tid & 63) == 0) red[tid >> 6] = L;
-    __syncthreads();
-    L = red[0] + red[1] + exp2f(sink2 - M);
-    // sum of weighted partials; loads issued 8 splits at a time (independent),
-    // splits with zero weight (no rows) are never read
-    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const float *src = a.part_o + ((size_t)qi * S * a.H + h) * a.D + 4 * tid;
-    const size_t sstride = (size_t)a.H * a.D;
-    for (int s0 = 0; s0 < S; s0 += 8) {
-        f32x4_t x[8];
+    const u32x4_t *src = (const u32x4_t *)a.part_o + (((size_t)qi * S * 8 + wave) * 8 + p) * 64 + lane;
+    const size_t sstride = 8 * 8 * 64;  // vectors per split
+    u32x4_t ov[2][kBatch];
+    auto load_batch = [&](u32x4_t (&v)[kBatch], int s0) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int s = s0 + u;
-            x[u] = (s < S && sw[s] != 0.f) ? *(const f32x4_t *)(src + s * sstride) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < kBatch; ++u) {
+            const int s = s0 + u < S ? s0 + u : S - 1;  // clamped: in bounds, unconditional
+            v[u] = src[s * sstride];
         }
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-            if (s0 + u < S) acc += sw[s0 + u] * x[u];
+    };
+    load_batch(ov[0], 0);
+    {  // weights of head h0 + wv
+        const float sink2 = a.sink[h0 + wv] * kLog2e;
+        float M = sink2;
+        for (int s = ln; s < S; s += 64) {
+            const float *ml = a.part_ml + (((size_t)qi * S + s) * a.H + h0 + wv) * 2;
+            if (ml[1] > 0.f) M = fmaxf(M, ml[0]);
+        }
+        M = wave_max(M);
+        float L = 0.f;
+        for (int s = ln; s < S; s += 64) {
+            const float *ml = a.part_ml + (((size_t)qi * S + s) * a.H + h0 + wv) * 2;
+            const float l = ml[1];
+            const float w = l > 0.f ? l * exp2f(ml[0] - M) : 0.f;
+            s_w[s][wv] = w;
+            L += w;
+        }
+        L = wave_sum(L);
+        if (ln == 0) {
+            s_M[wv] = M;
+            s_L[wv] = L + (sink2 > -INFINITY ? exp2f(sink2 - M) : 0.f);
+        }
     }
-    const float inv = 1.f / L;
-    *(f32x4_t *)&a.out[((size_t)qi * a.H + h) * a.D + 4 * tid] = acc * inv;
-    if (a.lse && tid == 0) a.lse[(size_t)qi * a.H + h] = M * kLn2 + logf(L);
+    __syncthreads();
+    float acc[4][2] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
+    auto fold = [&](const u32x4_t (&v)[kBatch], int s0) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            if (s0 + u >= S) break;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float w = s_w[s0 + u][r];
+                if (w == 0.f) continue;  // also keeps unwritten partials out
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {  // dt = 2p + kk: word 2kk + r/2, half r%2
+                    const uint32_t wd = v[u][2 * kk + (r >> 1)];
+                    const uint16_t hb = (uint16_t)((r & 1) ? (wd >> 16) : (wd & 0xFFFFu));
+                    acc[r][kk] = fmaf(w, (float)__builtin_bit_cast(_Float16, hb), acc[r][kk]);
+                }
+            }
+        }
+    };
+    for (int s0 = 0; s0 < S; s0 += 2 * kBatch) {
+        if (s0 + kBatch < S) load_batch(ov[1], s0 + kBatch);
+        fold(ov[0], s0);
+        if (s0 + kBatch >= S) break;
+        if (s0 + 2 * kBatch < S) load_batch(ov[0], s0 + 2 * kBatch);
+        fold(ov[1], s0 + kBatch);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float L = s_L[r];
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+            a.out[((size_t)qi * a.H + h0 + r) * kD + 256 * dh + 16 * (2 * p + kk) + e] = acc[r][kk] * inv;
+        if (a.lse && tid == 0) a.lse[(size_t)qi * a.H + h0 + r] = s_M[r] * kLn2 + logf(L);
+    }
 }
+
+constexpr int kPlanWgs = 256;      // workgroups aimed at over the launch
+constexpr int kPlanMinRows = 64;   // rows per split at least
 
 void mqa_plan(int n_queries, int max_rows, int *n_splits, int *rows_per_split) {
-    // ~512 workgroups in flight, at least 64 rows per split, whole tiles.
-    const int want_splits = (512 + n_queries - 1) / n_queries;
+    // about kPlanWgs workgroups, at least kPlanMinRows rows per split, whole tiles
+    const int want_splits = (kPlanWgs + n_queries - 1) / n_queries;
     int rps = (max_rows + want_splits - 1) / want_splits;
-    if (rps < 64) rps = 64;
+    if (rps < kPlanMinRows) rps = kPlanMinRows;
     rps = (rps + kTile - 1) / kTile * kTile;
     int s = (max_rows + rps - 1) / rps;
     if (s < 1) s = 1;
-    if (s > 1024) {
-        s = 1024;
+    if (s > kCombineMaxSplits) {
+        s = kCombineMaxSplits;
         rps = ((max_rows + s - 1) / s + kTile - 1) / kTile * kTile;
         s = (max_rows + rps - 1) / rps;
     }
@@ -397,7 +456,7 @@ size_t mqa_workspace_bytes(int dtype, int n_queries, int H, int D, int max_rows)
     mqa_plan(n_queries, max_rows, &s, &rps);
     if (s == 1) return 0;
     const size_t n = (size_t)n_queries * s * H;
-    return n * D * 4 + n * 2 * 4 + 256;
+    return n * D * 2 + n * 2 * 4 + 256;
 }
 
 void mqa_carve(MqaArgs &a, void *ws, int n_queries) {
@@ -406,8 +465,8 @@ void mqa_carve(MqaArgs &a, void *ws, int n_queries) {
     if (a.n_splits <= 1) return;
     char *p = (char *)(((uintptr_t)ws + 255) & ~(uintptr_t)255);
     const size_t n = (size_t)n_queries * a.n_splits * a.H;
-    a.part_o = (float *)p;
-    a.part_ml = (float *)(p + n * a.D * 4);
+    a.part_o = p;
+    a.part_ml = (float *)(p + n * a.D * 2);
 }
 
 hipError_t launch_mqa(const MqaArgs &a, int dtype, hipStream_t stream) {
@@ -418,7 +477,7 @@ hipError_t launch_mqa(const MqaArgs &a, int dtype, hipStream_t stream) {
         return hipGetLastError();
     }
     hipLaunchKernelGGL(mqa_bf16_kernel<4>, dim3(a.n_splits, Q), dim3(512), 0, stream, a);
-    if (a.n_splits > 1) hipLaunchKernelGGL(mqa_combine_kernel, dim3(a.H, Q), dim3(128), 0, stream, a);
+    if (a.n_splits > 1) hipLaunchKernelGGL(mqa_combine_kernel, dim3(16, Q), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -78,7 +78,7 @@ struct MqaArgs {
     const float *sink;              // [H]
     float *out;                     // [Q, H, D]
     float *lse;                     // [Q, H] or null
-    float *part_o;                  // [Q, S, H, D]   (split partials)
+    void *part_o;                   // [Q, S, 8, 8, 64] 16-byte fp16 vectors: split partials O / l
     float *part_ml;                 // [Q, S, H, 2]
     int B, T, H, D, K, W, ratio;
     int n_splits, rows_per_split;

@@ -32,6 +32,7 @@ constexpr int kWaves = kWG / 64;
 constexpr int kAuxThreads = 256;
 constexpr int kPerThread = kTopkAuxChunk / kAuxThreads;  // 8 scores per thread
 constexpr int kSubCap = 1024;                            // candidates sharing the final sub-bin
+
 constexpr int kBitmapMaxN = 262144;                      // LDS bitmap ordering up to this row length
 
 struct TopkShared {
@@ -359,7 +360,7 @@ __global__ __launch_bounds__(kAuxThreads) void topk_hist_kernel(TopkArgs a) {
 // One workgroup per query (rows up to kTopkOneKernelMax, or many queries):
 // threshold from the histogram windows, scan and selection.
 __global__ __launch_bounds__(kWG) void topk_onekernel_kernel(TopkArgs a) {
-    __shared__ int32_t v[kTopkMaxK];
+    __shared__ __attribute__((aligned(16))) int32_t v[kTopkMaxK];
     __shared__ uint32_t c_key[kTopkCand];
     __shared__ int32_t c_idx[kTopkCand];
     __shared__ SelectShared ss;
@@ -377,20 +378,26 @@ __global__ __launch_bounds__(kWG) void topk_onekernel_kernel(TopkArgs a) {
         for (int i = tid; i < K; i += kWG) out[i] = i < n ? i : -1;
         return;
     }
+    // The first round of scores goes out together with the window loads;
+    // later rounds are loaded one ahead of the round being classified.
+    constexpr int kRound = 16;  // scores per thread per round, all loads in flight together
+    constexpr int kSpan = kRound * kWG;
+    float xa[kRound], xb[kRound];
+    auto load_round = [&](float (&x)[kRound], int j0) {
+#pragma unroll
+        for (int k = 0; k < kRound; ++k) {
+            const int j = j0 + k * kWG + tid;
+            x[k] = j < n ? row[j] : 0.f;
+        }
+    };
+    load_round(xa, 0);
     const uint32_t bin = window_threshold(a.win_hdr + (size_t)qi * a.n_win,
                                           a.win_cnt + (size_t)qi * a.n_win * kTopkWin, a.n_win, K, s_red, s_hist);
     bool ok = bin != kNoBin;
     if (ok) {
         if (tid < 2) s_cnt[tid] = 0;
         __syncthreads();
-        constexpr int kRound = 16;  // scores per thread per round, all loads in flight together
-        for (int j0 = 0; j0 < n; j0 += kRound * kWG) {
-            float x[kRound];
-#pragma unroll
-            for (int k = 0; k < kRound; ++k) {
-                const int j = j0 + k * kWG + tid;
-                x[k] = j < n ? row[j] : 0.f;
-            }
+        auto classify = [&](const float (&x)[kRound], int j0) {
 #pragma unroll
             for (int k = 0; k < kRound; ++k) {
                 const int j = j0 + k * kWG + tid;
@@ -405,6 +412,13 @@ __global__ __launch_bounds__(kWG) void topk_onekernel_kernel(TopkArgs a) {
                     c_idx[sc] = j;
                 }
             }
+        };
+        for (int j0 = 0; j0 < n; j0 += 2 * kSpan) {
+            if (j0 + kSpan < n) load_round(xb, j0 + kSpan);
+            classify(xa, j0);
+            if (j0 + kSpan >= n) break;
+            if (j0 + 2 * kSpan < n) load_round(xa, j0 + 2 * kSpan);
+            classify(xb, j0 + kSpan);
         }
         __syncthreads();
         const int na = s_cnt[0], nc = s_cnt[1];
@@ -483,7 +497,7 @@ __global__ __launch_bounds__(kAuxThreads) void topk_filter_kernel(TopkArgs a) {
 }
 
 __global__ __launch_bounds__(kWG) void topk_final_kernel(TopkArgs a, int n_flt) {
-    __shared__ int32_t v[kTopkMaxK];
+    __shared__ __attribute__((aligned(16))) int32_t v[kTopkMaxK];
     __shared__ uint32_t c_key[kTopkCand];
     __shared__ int32_t c_idx[kTopkCand];
     __shared__ SelectShared ss;

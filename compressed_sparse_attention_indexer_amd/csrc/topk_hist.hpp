@@ -52,16 +52,30 @@ __device__ __forceinline__ void hist_window_store(const uint32_t *lh, int32_t *h
 // Merge n_win windows (hdr[w], cnt[w][kTopkWin]) into the exact histogram of
 // the top kTopkWin bins below the global highest bin M, and return the bin
 // holding the K-th largest key (kNoBin if it lies below that range or there is
-// nothing).  Any block size that is a multiple of 64 (up to 1024).  Loads go
-// out in two rounds (headers, then blockDim/4 windows at a time) so latency is
-// paid a few times, not per window.  s_hist needs kTopkWin words, s_red one
-// int per wave.
+// nothing).  Any block size that is a multiple of 64 (up to 1024); s_hist
+// needs kTopkWin words, s_red one int per wave.  Four threads take a window
+// (32 counts each).  Every header and the counts of the first blockDim/4
+// windows are loaded in one round (the caller may have its own loads in
+// flight too); further windows, if any, take one more round per blockDim/4.
 __device__ __forceinline__ uint32_t window_threshold(const int32_t *hdr, const uint32_t *cnt, int n_win, int K,
                                                      int *s_red, uint32_t *s_hist) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nt = blockDim.x, nwaves = nt >> 6;
+    const int nt = blockDim.x, nwaves = nt >> 6, per_pass = nt >> 2;
+    const int seg = tid & 3;
     int m = -1;
     for (int w = tid; w < n_win; w += nt) m = max(m, hdr[w]);
+    int mw = -1;
+    u32x4_t x[8];
+    auto load_window = [&](int w) {
+        mw = -1;
+        if (w < n_win) {
+            mw = hdr[w];
+            const u32x4_t *src = (const u32x4_t *)(cnt + (size_t)w * kTopkWin + 32 * seg);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = src[i];
+        }
+    };
+    load_window(tid >> 2);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) m = max(m, __shfl_xor(m, o));
     if (lane == 0) s_red[wave] = m;
@@ -70,18 +84,7 @@ __device__ __forceinline__ uint32_t window_threshold(const int32_t *hdr, const u
     int M = -1;
     for (int w = 0; w < nwaves; ++w) M = max(M, s_red[w]);
     if (M < 0) return kNoBin;  // the same in every thread
-    // 4 threads per window, 32 bins (8 x 16 bytes) each
-    const int seg = tid & 3;
-    for (int w0 = 0; w0 < n_win; w0 += nt >> 2) {
-        const int w = w0 + (tid >> 2);
-        int mw = -1;
-        u32x4_t x[8];
-        if (w < n_win) {
-            mw = hdr[w];
-            const u32x4_t *src = (const u32x4_t *)(cnt + (size_t)w * kTopkWin + 32 * seg);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = src[i];
-        }
+    for (int w0 = 0;;) {
         if (mw >= 0) {
             const int off = mw - M + 32 * seg;  // merged-window bin of this thread's first count
 #pragma unroll
@@ -92,6 +95,9 @@ __device__ __forceinline__ uint32_t window_threshold(const int32_t *hdr, const u
                     if (x[i][c] && b >= 0 && b < kTopkWin) atomicAdd(&s_hist[b], x[i][c]);
                 }
         }
+        w0 += per_pass;
+        if (w0 >= n_win) break;
+        load_window(w0 + (tid >> 2));
     }
     __syncthreads();
     if (tid == 0) {
