@@ -58,13 +58,15 @@ __device__ __forceinline__ float index_act(float x) {
 // Per wave and step: 32 entries (two 16-entry column tiles) x 64 heads (four
 // 16-head row tiles) x 128 dims (four k-steps of 32) on
 // v_mfma_f32_16x16x32_bf16.  A = index query (heads x dims, resident in
-// registers), B = index keys (dims x entries) loaded straight from HBM into
-// registers with nontemporal loads, one step ahead of the step being
-// computed.  Lane (e, g) of a tile holds dims [32s + 8g, 32s + 8g + 8) of
-// entry e for k-step s, so each load instruction reads 64 contiguous bytes of
-// every entry it touches.  The C tile gives each lane 4 heads of one entry;
-// the weighted activation sum over those heads is done in registers and the 4
-// lane groups are summed with two cross-lane adds.
+// registers), B = index keys (dims x entries).  A wave-step of keys is 8 KiB
+// of consecutive rows, loaded whole-row (each load instruction reads 1 KiB
+// contiguous) with nontemporal loads two steps ahead; to compute, the wave
+// copies the step into its own LDS block and reads it back as B fragments
+// (lane (e, g) of a tile takes dims [32s + 8g, 32s + 8g + 8) of entry e for
+// k-step s), and the registers it freed take the loads of the step two
+// ahead before the math starts.  The C tile gives each lane 4 heads of one
+// entry; the weighted activation sum over those heads is done in registers
+// and the 4 lane groups are summed with two cross-lane adds.
 //
 // Launch shape: about one 4-wave workgroup per CU.  A workgroup-step covers
 // 128 entries (32 KiB of keys); the steps of a query are dealt round-robin to
@@ -80,11 +82,14 @@ constexpr int kWgStep = kScoreWaves * kWaveStep;      // entries per workgroup s
 constexpr int kTargetWgs = 256;                       // about one workgroup per CU
 constexpr int kScoreDepth = 2;                        // key steps in flight per wave
 typedef bf16x8_t KeyFrag[2][4];
+typedef u32x4_t KeyRaw[8];  // a wave-step of keys as loaded: 8 KiB, 16 B per lane per load
+constexpr int kRawRowWords = kDI / 2 + 4;  // LDS row of 128 bf16 + 16 B pad
 }  // namespace
 
 template <int kAct, bool kHist, int kDepth>
 __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(ScoreArgs a) {
     __shared__ uint32_t lh[kHist ? kTopkBins : 1];
+    __shared__ __attribute__((aligned(16))) uint32_t kraw[kScoreWaves][kWaveStep * kRawRowWords];
     __shared__ int s_red[4];
     const int qi = blockIdx.y;
     const int b = qi / a.T;
@@ -129,18 +134,35 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(
     // Every load is unconditional (indices clamped into the visible rows) so
     // the loop body is straight-line code and the compiler can wait for one
     // step's loads while the next step's are still in flight.
-    auto load = [&](KeyFrag &kf, int base) {
+    // Loads read whole rows: load i of lane l takes 16 bytes of entry
+    // base + 4i + l/16 (1 KiB contiguous per instruction); the step is
+    // redistributed into MFMA fragments through a wave-private LDS block.
+    auto load = [&](KeyRaw &kr, int base) {
 #pragma unroll
-        for (int et = 0; et < 2; ++et) {
-            int j = base + 16 * et + e;
+        for (int i = 0; i < 8; ++i) {
+            int j = base + 4 * i + (lane >> 4);
             j = j < nvis ? j : last;
-            const gptr<bf16x8_t> kr = as_global<bf16x8_t>(kb + (size_t)j * kDI + 8 * g);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) kf[et][s] = __builtin_nontemporal_load(kr + 4 * s);
+            kr[i] = __builtin_nontemporal_load(as_global<u32x4_t>(kb + (size_t)j * kDI + 8 * (lane & 15)));
         }
     };
+    uint32_t *kw = kraw[wave];
+    auto stash = [&](const KeyRaw &kr) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) *(u32x4_t *)&kw[(4 * i + (lane >> 4)) * kRawRowWords + 4 * (lane & 15)] = kr[i];
+    };
+    auto frags = [&](KeyFrag &kf) {
+#pragma unroll
+        for (int et = 0; et < 2; ++et)
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2)
+                kf[et][s2] = *(const bf16x8_t *)&kw[(16 * et + e) * kRawRowWords + 16 * s2 + 4 * g];
+    };
     // `live`: the step exists (a clamped re-run of the last step stores nothing)
-    auto process = [&](const KeyFrag &kf, int base, bool live) {
+    auto process = [&](KeyRaw &kr, int base, bool live, int next) {
+        stash(kr);
+        load(kr, next);  // the registers are free again: the next load goes out before this step's math
+        KeyFrag kf;
+        frags(kf);
         const int j = base + 16 * g + e;  // entry this lane stores (g < 2)
         float part[2];
 #pragma unroll
@@ -175,15 +197,14 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(
         // load sits behind a branch: while step k computes, the loads of steps
         // k+1 .. k+kDepth-1 are in flight.  Steps past the last one reload the
         // last step and store nothing.
-        KeyFrag kbuf[kDepth];
+        KeyRaw kbuf[kDepth];
         auto step = [&](int k) { return base0 + (k < n_load ? k : n_load - 1) * stride; };
 #pragma unroll
         for (int i = 0; i < kDepth; ++i) load(kbuf[i], step(i));
         for (int k = 0; k < n_load; k += kDepth) {
 #pragma unroll
             for (int i = 0; i < kDepth; ++i) {
-                process(kbuf[i], step(k + i), k + i < n_load);
-                load(kbuf[i], step(k + i + kDepth));
+                process(kbuf[i], step(k + i), k + i < n_load, step(k + i + kDepth));
             }
         }
     }
