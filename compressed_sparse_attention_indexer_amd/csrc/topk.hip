@@ -191,8 +191,99 @@ __device__ __forceinline__ int wave_append(int *count, bool valid) {
     return base + __popcll(m & lanemask_lt());
 }
 
+// Block-wide exclusive scan for NT threads (a multiple of 64); s_wave holds
+// NT / 64 ints.  Two barriers.
+template <int NT>
+__device__ __forceinline__ int block_scan_excl(int x, int *s_wave, int *total) {
+    constexpr int NW = NT / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int inc = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(inc, o);
+        if (lane >= o) inc += t;
+    }
+    if (lane == 63) s_wave[wave] = inc;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const int c = s_wave[w];
+        before += w < wave ? c : 0;
+        all += c;
+    }
+    __syncthreads();
+    *total = all;
+    return before + inc - x;
+}
+
+// R consecutive scores j_first .. j_first + R - 1 of a row (0 past n).  Whole
+// 16-byte loads when the chunk lies inside the row and the row is aligned.
+template <int R>
+__device__ __forceinline__ void load_chunk(const float *row, int j_first, int n, int n_max, bool vec, float (&x)[R]) {
+    if (vec && j_first + R <= n_max) {
+#pragma unroll
+        for (int k = 0; k < R; k += 4) {
+            const float4 f = *(const float4 *)(row + j_first + k);
+            x[k] = f.x;
+            x[k + 1] = f.y;
+            x[k + 2] = f.z;
+            x[k + 3] = f.w;
+        }
+#pragma unroll
+        for (int k = 0; k < R; ++k)
+            if (j_first + k >= n) x[k] = 0.f;
+    } else {
+#pragma unroll
+        for (int k = 0; k < R; ++k) x[k] = j_first + k < n ? row[j_first + k] : 0.f;
+    }
+}
+
+// Ordered compaction of one round: thread t owns the R consecutive entries
+// starting at j_first (the threads' chunks consecutive in thread order).
+// Entries whose key bin is above `bin` go to v, those in `bin` to
+// (c_key, c_idx), both in index order after the n_gt / n_eq already there;
+// writes past a capacity are dropped (the counts still grow, so the caller
+// sees the overflow).  n_gt and n_eq are the same in every thread.
+template <int NT, int R>
+__device__ __forceinline__ void classify_ordered(const float (&x)[R], int j_first, int n, uint32_t bin, int *s_wave,
+                                                 int &n_gt, int &n_eq, int32_t *v, int v_cap, uint32_t *c_key,
+                                                 int32_t *c_idx, int c_cap) {
+    int g = 0, q = 0;
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        const uint32_t d = order_key(x[k]) >> 20;
+        const bool ok = j_first + k < n;
+        g += ok && d > bin;
+        q += ok && d == bin;
+    }
+    int tot;
+    const int pre = block_scan_excl<NT>(g | (q << 16), s_wave, &tot);  // per-field sums stay below 2^16
+    int sg = n_gt + (pre & 0xFFFF), sq = n_eq + (pre >> 16);
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        const int j = j_first + k;
+        const uint32_t key = order_key(x[k]);
+        const uint32_t d = key >> 20;
+        if (j < n && d > bin) {
+            if (sg < v_cap) v[sg] = j;
+            ++sg;
+        }
+        if (j < n && d == bin) {
+            if (sq < c_cap) {
+                c_key[sq] = key;
+                c_idx[sq] = j;
+            }
+            ++sq;
+        }
+    }
+    n_gt += tot & 0xFFFF;
+    n_eq += tot >> 16;
+}
+
 struct SelectShared {
     uint32_t words[kBitmapMaxN / 32];  // second-level histogram, then the output bitmap
+    int32_t sel[kTopkMaxK];            // chosen candidates in index order (ordered selection)
     uint32_t sub_key[kSubCap];
     int32_t sub_idx[kSubCap];
     int s_wave[kWaves];
@@ -314,6 +405,92 @@ __device__ bool select_emit(int32_t *v, int na, const uint32_t *c_key, const int
     return true;
 }
 
+// Ordered selection: v[0..na) (entries above the threshold bin) and the
+// candidates c_key/c_idx[0..nc) (inside it) are both in index order, na < K,
+// na + nc >= K and nc <= kWG.  Candidate t (thread t) is chosen if its
+// second-level bin (key bits 19..12) lies above the bin b2 that holds the
+// need-th best candidate, or inside b2 with fewer than need2 better
+// candidates there ((key, lower index) order; b2's few members are gathered
+// in LDS first).  The chosen ones are compacted in index order and merged
+// with v into `out` by binary search.  Returns false (nothing written, same
+// in every thread) if b2 holds more than kSubCap candidates.
+__device__ bool select_ordered(const int32_t *v, int na, const uint32_t *c_key, const int32_t *c_idx, int nc, int K,
+                               int32_t *out, SelectShared &ss) {
+    const int tid = threadIdx.x;
+    const int need = K - na;
+    uint32_t *h = ss.words;
+    if (tid < 256) h[tid] = 0u;
+    if (tid == 0) ss.cnt[0] = 0;
+    __syncthreads();
+    const bool have = tid < nc;
+    const uint32_t key = have ? c_key[tid] : 0u;
+    const int32_t idx = have ? c_idx[tid] : 0;
+    const uint32_t bk = (key >> 12) & 0xFFu;
+    if (have) atomicAdd(&h[bk], 1u);
+    __syncthreads();
+    if (tid < 64) {  // wave 0: bins from the top, 4 per lane
+        uint32_t c[4], sum = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            c[i] = h[255 - (4 * tid + i)];
+            sum += c[i];
+        }
+        uint32_t incl = sum;  // inclusive prefix over lanes (lane 0 = top bins)
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t t = __shfl_up(incl, o);
+            if (tid >= o) incl += t;
+        }
+        uint32_t acc = incl - sum;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (acc < (uint32_t)need && (uint32_t)need <= acc + c[i]) {
+                ss.bcast[0] = 255 - (4 * tid + i);
+                ss.bcast[1] = need - (int)acc;
+            }
+            acc += c[i];
+        }
+    }
+    __syncthreads();
+    const uint32_t b2 = (uint32_t)ss.bcast[0];
+    const int need2 = ss.bcast[1];
+    if (have && bk == b2) {  // gather b2's members (any order)
+        const int slot = atomicAdd(&ss.cnt[0], 1);
+        if (slot < kSubCap) {
+            ss.sub_key[slot] = key;
+            ss.sub_idx[slot] = idx;
+        }
+    }
+    __syncthreads();
+    const int m2 = ss.cnt[0];
+    if (m2 > kSubCap) return false;
+    bool take = have && bk > b2;
+    if (have && bk == b2) {
+        const uint64_t mine = ((uint64_t)key << 32) | (uint32_t)~(uint32_t)idx;
+        int better = 0;
+        for (int u = 0; u < m2; ++u)
+            better += (((uint64_t)ss.sub_key[u] << 32) | (uint32_t)~(uint32_t)ss.sub_idx[u]) > mine;
+        take = better < need2;
+    }
+    int tot;
+    const int pos = block_scan_excl<kWG>(take ? 1 : 0, ss.s_wave, &tot);
+    if (take) ss.sel[pos] = idx;
+    __syncthreads();
+    const int32_t *sel = ss.sel;
+    for (int i = tid; i < na + need; i += kWG) {
+        const bool above = i < na;
+        const int32_t x = above ? v[i] : sel[i - na];
+        const int32_t *other = above ? sel : v;
+        int lo = 0, hi = above ? need : na;  // count of `other` below x
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (other[mid] < x) lo = mid + 1; else hi = mid;
+        }
+        out[(above ? i : i - na) + lo] = x;
+    }
+    return true;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -367,7 +544,6 @@ __global__ __launch_bounds__(kWG) void topk_onekernel_kernel(TopkArgs a) {
     __shared__ TopkShared sh;
     __shared__ uint32_t s_hist[kTopkWin];
     __shared__ int s_red[kWaves];
-    __shared__ int s_cnt[2];
     const int qi = blockIdx.x;
     const int tid = threadIdx.x;
     const int n = query_visible(a, qi);
@@ -379,52 +555,34 @@ __global__ __launch_bounds__(kWG) void topk_onekernel_kernel(TopkArgs a) {
         return;
     }
     // The first round of scores goes out together with the window loads;
-    // later rounds are loaded one ahead of the round being classified.
-    constexpr int kRound = 16;  // scores per thread per round, all loads in flight together
+    // later rounds are loaded one ahead of the round being classified.  Each
+    // thread takes consecutive scores, so the lists come out in index order.
+    constexpr int kRound = 16;  // scores per thread per round
     constexpr int kSpan = kRound * kWG;
+    const bool vec = (a.n_max & 3) == 0 && ((uintptr_t)a.scores & 15) == 0;
     float xa[kRound], xb[kRound];
-    auto load_round = [&](float (&x)[kRound], int j0) {
-#pragma unroll
-        for (int k = 0; k < kRound; ++k) {
-            const int j = j0 + k * kWG + tid;
-            x[k] = j < n ? row[j] : 0.f;
-        }
-    };
-    load_round(xa, 0);
+    load_chunk<kRound>(row, kRound * tid, n, a.n_max, vec, xa);
     const uint32_t bin = window_threshold(a.win_hdr + (size_t)qi * a.n_win,
                                           a.win_cnt + (size_t)qi * a.n_win * kTopkWin, a.n_win, K, s_red, s_hist);
     bool ok = bin != kNoBin;
     if (ok) {
-        if (tid < 2) s_cnt[tid] = 0;
-        __syncthreads();
-        auto classify = [&](const float (&x)[kRound], int j0) {
-#pragma unroll
-            for (int k = 0; k < kRound; ++k) {
-                const int j = j0 + k * kWG + tid;
-                const uint32_t key = order_key(x[k]);
-                const uint32_t d = key >> 20;
-                const bool gt = j < n && d > bin, eq = j < n && d == bin;
-                const int sa = wave_append(&s_cnt[0], gt);
-                const int sc = wave_append(&s_cnt[1], eq);
-                if (gt && sa < K) v[sa] = j;
-                if (eq && sc < kTopkCand) {
-                    c_key[sc] = key;
-                    c_idx[sc] = j;
-                }
-            }
-        };
+        int na = 0, nc = 0;
         for (int j0 = 0; j0 < n; j0 += 2 * kSpan) {
-            if (j0 + kSpan < n) load_round(xb, j0 + kSpan);
-            classify(xa, j0);
+            if (j0 + kSpan < n) load_chunk<kRound>(row, j0 + kSpan + kRound * tid, n, a.n_max, vec, xb);
+            classify_ordered<kWG, kRound>(xa, j0 + kRound * tid, n, bin, s_red, na, nc, v, K, c_key, c_idx, kTopkCand);
             if (j0 + kSpan >= n) break;
-            if (j0 + 2 * kSpan < n) load_round(xa, j0 + 2 * kSpan);
-            classify(xb, j0 + kSpan);
+            if (j0 + 2 * kSpan < n) load_chunk<kRound>(row, j0 + 2 * kSpan + kRound * tid, n, a.n_max, vec, xa);
+            classify_ordered<kWG, kRound>(xb, j0 + kSpan + kRound * tid, n, bin, s_red, na, nc, v, K, c_key, c_idx,
+                                          kTopkCand);
         }
         __syncthreads();
-        const int na = s_cnt[0], nc = s_cnt[1];
         ok = na < K && nc <= kTopkCand && na + nc >= K;
-        __syncthreads();
-        if (ok) ok = select_emit(v, na, c_key, c_idx, nc, n, K, out, ss);
+        if (ok) {
+            if (nc <= kWG)
+                ok = select_ordered(v, na, c_key, c_idx, nc, K, out, ss);
+            else
+                ok = select_emit(v, na, c_key, c_idx, nc, n, K, out, ss);
+        }
     }
     if (!ok) {
         __syncthreads();
@@ -453,33 +611,23 @@ __global__ __launch_bounds__(kAuxThreads) void topk_filter_kernel(TopkArgs a) {
     if (n <= a.K || j0 >= n) return;  // the selection reads regions below n only
     uint32_t *reg = a.flt + ((size_t)qi * gridDim.x + blockIdx.x) * kFltRegionWords;
     const float *row = a.scores + (size_t)qi * a.n_max;
+    const bool vec = (a.n_max & 3) == 0 && ((uintptr_t)a.scores & 15) == 0;
+    const int j_first = j0 + kPerThread * threadIdx.x;  // this thread's consecutive scores
     float x[kPerThread];
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
-        const int j = j0 + k * kAuxThreads + threadIdx.x;
-        x[k] = j < n ? row[j] : 0.f;
-    }
+    load_chunk<kPerThread>(row, j_first, n, a.n_max, vec, x);
     const uint32_t bin = window_threshold(a.win_hdr + (size_t)qi * a.n_win,
                                           a.win_cnt + (size_t)qi * a.n_win * kTopkWin, a.n_win, a.K, s_red, s_hist);
     if (bin == kNoBin) {
         if (threadIdx.x == 0) reg[0] = 0xFFFFFFFFu;
         return;
     }
-    if (threadIdx.x < 2) l_cnt[threadIdx.x] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
-        const int j = j0 + k * kAuxThreads + threadIdx.x;
-        const uint32_t key = order_key(x[k]);
-        const uint32_t d = key >> 20;
-        const bool gt = j < n && d > bin, eq = j < n && d == bin;
-        const int sa = wave_append(&l_cnt[0], gt);
-        const int sc = wave_append(&l_cnt[1], eq);
-        if (gt && sa < kFltAboveCap) l_above[sa] = j;
-        if (eq && sc < kFltCandCap) {
-            l_ckey[sc] = key;
-            l_cidx[sc] = j;
-        }
+    // lists in index order, so the selection can merge them without sorting
+    int n_gt = 0, n_eq = 0;
+    classify_ordered<kAuxThreads, kPerThread>(x, j_first, n, bin, s_red, n_gt, n_eq, l_above, kFltAboveCap, l_ckey,
+                                              l_cidx, kFltCandCap);
+    if (threadIdx.x == 0) {
+        l_cnt[0] = n_gt;
+        l_cnt[1] = n_eq;
     }
     __syncthreads();
     const int na = l_cnt[0], nc = l_cnt[1];
@@ -570,7 +718,12 @@ __global__ __launch_bounds__(kWG) void topk_final_kernel(TopkArgs a, int n_flt) 
     }
     __syncthreads();
     ok = ok && !s_bad && na_tot < K && nc_tot <= kTopkCand && na_tot + nc_tot >= K;
-    if (ok) ok = select_emit(v, na_tot, c_key, c_idx, nc_tot, n, K, out, ss);
+    if (ok) {  // the regions' lists are in index order, and so are their concatenations
+        if (nc_tot <= kWG)
+            ok = select_ordered(v, na_tot, c_key, c_idx, nc_tot, K, out, ss);
+        else
+            ok = select_emit(v, na_tot, c_key, c_idx, nc_tot, n, K, out, ss);
+    }
     if (!ok) {
         __syncthreads();
         topk_row<false>(row, n, K, out, nullptr, sh);
