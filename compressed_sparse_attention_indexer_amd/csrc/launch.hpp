@@ -33,7 +33,7 @@ bool score_uses_tiles(int dtype, int T);
 constexpr int kTopkSmallMax = 4096;       // rows up to this length: one workgroup, row kept in LDS
 constexpr int kTopkOneKernelMax = 65536;  // rows up to this length: threshold+scan+select in one kernel
 constexpr int kTopkBins = 4096;           // key histogram (top 12 key bits)
-constexpr int kTopkWin = 128;             // histogram window kept per workgroup (16 octaves)
+constexpr int kTopkWin = 32;              // histogram window kept per workgroup (4 octaves)
 constexpr int kTopkCand = 8192;           // candidates held in LDS by the selecting workgroup
 constexpr int kTopkMaxK = 2048;
 constexpr int kTopkAuxChunk = 2048;       // scores per workgroup in the histogram and filter kernels

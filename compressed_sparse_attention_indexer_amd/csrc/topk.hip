@@ -9,10 +9,11 @@
 //    writes the selection in index order with an ordered compaction.
 //  * up to kTopkOneKernelMax: the key histogram comes in windows (one per
 //    scorer or histogram workgroup, plain stores); one workgroup per query
-//    merges them into the exact histogram of the top 128 bins (16 octaves
-//    below the largest key), finds the bin holding the K-th key, scans the row
-//    into "above" and "candidate" lists in LDS, selects among the candidates
-//    and writes the indices in order through an LDS bitmap.
+//    merges them into the exact histogram of the top kTopkWin bins (1/8
+//    octave each, just below the largest key), finds the bin holding the K-th
+//    key, scans the row into "above" and "candidate" lists in LDS (ordered
+//    compaction, so both are in index order), selects among the candidates
+//    and merges the two lists into the ascending output.
 //  * longer rows: many workgroups each merge the windows into the threshold
 //    and scan a slice of the row, writing their own lists with plain stores;
 //    one workgroup per query then gathers the lists and selects.
@@ -33,7 +34,6 @@ constexpr int kAuxThreads = 256;
 constexpr int kPerThread = kTopkAuxChunk / kAuxThreads;  // 8 scores per thread
 constexpr int kSubCap = 1024;                            // candidates sharing the final sub-bin
 
-constexpr int kBitmapMaxN = 262144;                      // LDS bitmap ordering up to this row length
 
 struct TopkShared {
     uint32_t hist[256];
@@ -179,18 +179,6 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int *s_wave, int *tot
     return before + inc - x;
 }
 
-// Append `valid` lanes to an LDS list: one LDS atomic per wave.  Returns the
-// slot of this lane (meaningless when !valid).
-__device__ __forceinline__ int wave_append(int *count, bool valid) {
-    const uint64_t m = __ballot(valid);
-    int base = 0;
-    if (m) {
-        if (lane_id() == 0) base = atomicAdd(count, __popcll(m));
-        base = __builtin_amdgcn_readlane(base, 0);
-    }
-    return base + __popcll(m & lanemask_lt());
-}
-
 // Block-wide exclusive scan for NT threads (a multiple of 64); s_wave holds
 // NT / 64 ints.  Two barriers.
 template <int NT>
@@ -282,7 +270,7 @@ __device__ __forceinline__ void classify_ordered(const float (&x)[R], int j_firs
 }
 
 struct SelectShared {
-    uint32_t words[kBitmapMaxN / 32];  // second-level histogram, then the output bitmap
+    uint32_t words[256];               // second-level histogram
     int32_t sel[kTopkMaxK];            // chosen candidates in index order (ordered selection)
     uint32_t sub_key[kSubCap];
     int32_t sub_idx[kSubCap];
@@ -291,149 +279,37 @@ struct SelectShared {
     int bcast[2];
 };
 
-// Given v[0..na) = the entries above the threshold bin (na < K) and the
-// candidates inside it (c_key/c_idx[0..nc), na + nc >= K), keep the K - na
-// best candidates by (key desc, index asc) and write all K indices ascending.
-// Returns false (the same in every thread) if a capacity is exceeded; nothing
-// is written to `out` then.
-__device__ bool select_emit(int32_t *v, int na, const uint32_t *c_key, const int32_t *c_idx, int nc, int n, int K,
-                            int32_t *out, SelectShared &ss) {
-    const int tid = threadIdx.x;
-    const int need = K - na;
-    uint32_t *h2 = ss.words;  // 4096-bin histogram of key bits [19:8]
-    for (int i = tid; i < kTopkBins; i += kWG) h2[i] = 0u;
-    if (tid < 2) ss.cnt[tid] = 0;
-    __syncthreads();
-    for (int i = tid; i < nc; i += kWG) atomicAdd(&h2[(c_key[i] >> 8) & 0xFFFu], 1u);  // spread bins
-    __syncthreads();
-    uint32_t hh[4], s = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        hh[i] = h2[4 * tid + i];
-        s += hh[i];
-    }
-    int tot;
-    const int pre = block_exclusive_scan((int)s, ss.s_wave, &tot);
-    const int above_me = tot - pre - (int)s;  // candidates in higher bins
-    if (above_me < need && need <= above_me + (int)s) {
-        int acc = above_me;
-        for (int i = 3; i >= 0; --i) {
-            if (acc < need && need <= acc + (int)hh[i]) {
-                ss.bcast[0] = 4 * tid + i;
-                ss.bcast[1] = need - acc;
-                break;
-            }
-            acc += (int)hh[i];
-        }
-    }
-    __syncthreads();
-    const uint32_t b2 = (uint32_t)ss.bcast[0];
-    const int need2 = ss.bcast[1];
-    for (int i0 = 0; i0 < nc; i0 += kWG) {
-        const int i = i0 + tid;
-        const uint32_t d2 = i < nc ? (c_key[i] >> 8) & 0xFFFu : 0u;
-        const bool hi = i < nc && d2 > b2, tie = i < nc && d2 == b2;
-        const int s_hi = wave_append(&ss.cnt[0], hi);
-        const int s_tie = wave_append(&ss.cnt[1], tie);
-        if (hi && na + s_hi < K) v[na + s_hi] = c_idx[i];
-        if (tie && s_tie < kSubCap) {
-            ss.sub_key[s_tie] = c_key[i];
-            ss.sub_idx[s_tie] = c_idx[i];
-        }
-    }
-    __syncthreads();
-    const int n_hi = ss.cnt[0], m2 = ss.cnt[1];
-    if (m2 > kSubCap || na + n_hi + need2 != K) return false;
-    for (int t = tid; t < m2; t += kWG) {
-        const uint64_t mine = ((uint64_t)ss.sub_key[t] << 32) | (uint32_t) ~(uint32_t)ss.sub_idx[t];
-        int rank = 0;
-        for (int u = 0; u < m2; ++u) {
-            const uint64_t other = ((uint64_t)ss.sub_key[u] << 32) | (uint32_t) ~(uint32_t)ss.sub_idx[u];
-            rank += other > mine;
-        }
-        if (rank < need2) v[na + n_hi + rank] = ss.sub_idx[t];
-    }
-    __syncthreads();
-    if (n <= kBitmapMaxN) {  // ascending order through a bitmap of the row
-        const int n_words = (n + 31) >> 5;
-        for (int i = tid; i < n_words; i += kWG) ss.words[i] = 0u;
-        __syncthreads();
-        for (int i = tid; i < K; i += kWG) atomicOr(&ss.words[v[i] >> 5], 1u << (v[i] & 31));
-        __syncthreads();
-        constexpr int kWordsPerThread = kBitmapMaxN / 32 / kWG;  // 8
-        uint32_t wv[kWordsPerThread];
-        int c = 0;
-#pragma unroll
-        for (int k = 0; k < kWordsPerThread; ++k) {
-            const int wi = kWordsPerThread * tid + k;
-            wv[k] = wi < n_words ? ss.words[wi] : 0u;
-            c += __popc(wv[k]);
-        }
-        int pos = block_exclusive_scan(c, ss.s_wave, &tot);
-#pragma unroll
-        for (int k = 0; k < kWordsPerThread; ++k) {
-            uint32_t w = wv[k];
-            while (w) {
-                const int b = __ffs(w) - 1;
-                if (pos < K) out[pos] = 32 * (kWordsPerThread * tid + k) + b;
-                ++pos;
-                w &= w - 1u;
-            }
-        }
-    } else {  // bitonic sort of the K indices, padded to a power of two
-        int P = 1;
-        while (P < K) P <<= 1;
-        for (int i = K + tid; i < P; i += kWG) v[i] = 0x7FFFFFFF;
-        __syncthreads();
-        for (int size = 2; size <= P; size <<= 1) {
-            for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                for (int t = tid; t < P / 2; t += kWG) {
-                    const int i = (t / stride) * stride * 2 + (t % stride);
-                    const int j = i + stride;
-                    const bool asc = (i & size) == 0;
-                    const int32_t x = v[i], y = v[j];
-                    if ((x > y) == asc) {
-                        v[i] = y;
-                        v[j] = x;
-                    }
-                }
-                __syncthreads();
-            }
-        }
-        for (int i = tid; i < K; i += kWG) out[i] = v[i];
-    }
-    return true;
-}
-
 // Ordered selection: v[0..na) (entries above the threshold bin) and the
 // candidates c_key/c_idx[0..nc) (inside it) are both in index order, na < K,
-// na + nc >= K and nc <= kWG.  Candidate t (thread t) is chosen if its
+// na + nc >= K, nc <= kTopkCand.  Thread t takes the consecutive candidates
+// [C t, C t + C), C = ceil(nc / kWG).  A candidate is chosen if its
 // second-level bin (key bits 19..12) lies above the bin b2 that holds the
 // need-th best candidate, or inside b2 with fewer than need2 better
-// candidates there ((key, lower index) order; b2's few members are gathered
-// in LDS first).  The chosen ones are compacted in index order and merged
-// with v into `out` by binary search.  Returns false (nothing written, same
-// in every thread) if b2 holds more than kSubCap candidates.
+// candidates there ((key, lower index) order; b2's members are gathered in
+// LDS first).  The chosen ones are compacted in index order and merged with v
+// into `out` by binary search.  Returns false (nothing written, same in every
+// thread) if b2 holds more than kSubCap candidates.
 __device__ bool select_ordered(const int32_t *v, int na, const uint32_t *c_key, const int32_t *c_idx, int nc, int K,
                                int32_t *out, SelectShared &ss) {
+    constexpr int kMaxC = kTopkCand / kWG;
     const int tid = threadIdx.x;
     const int need = K - na;
+    const int C = (nc + kWG - 1) / kWG;
+    const int i0 = C * tid;
     uint32_t *h = ss.words;
     if (tid < 256) h[tid] = 0u;
     if (tid == 0) ss.cnt[0] = 0;
     __syncthreads();
-    const bool have = tid < nc;
-    const uint32_t key = have ? c_key[tid] : 0u;
-    const int32_t idx = have ? c_idx[tid] : 0;
-    const uint32_t bk = (key >> 12) & 0xFFu;
-    if (have) atomicAdd(&h[bk], 1u);
+#pragma unroll
+    for (int c = 0; c < kMaxC; ++c)
+        if (c < C && i0 + c < nc) atomicAdd(&h[(c_key[i0 + c] >> 12) & 0xFFu], 1u);
     __syncthreads();
     if (tid < 64) {  // wave 0: bins from the top, 4 per lane
-        uint32_t c[4], sum = 0;
+        uint32_t cb[4], sum = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            c[i] = h[255 - (4 * tid + i)];
-            sum += c[i];
+            cb[i] = h[255 - (4 * tid + i)];
+            sum += cb[i];
         }
         uint32_t incl = sum;  // inclusive prefix over lanes (lane 0 = top bins)
 #pragma unroll
@@ -444,37 +320,50 @@ __device__ bool select_ordered(const int32_t *v, int na, const uint32_t *c_key, 
         uint32_t acc = incl - sum;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            if (acc < (uint32_t)need && (uint32_t)need <= acc + c[i]) {
+            if (acc < (uint32_t)need && (uint32_t)need <= acc + cb[i]) {
                 ss.bcast[0] = 255 - (4 * tid + i);
                 ss.bcast[1] = need - (int)acc;
             }
-            acc += c[i];
+            acc += cb[i];
         }
     }
     __syncthreads();
     const uint32_t b2 = (uint32_t)ss.bcast[0];
     const int need2 = ss.bcast[1];
-    if (have && bk == b2) {  // gather b2's members (any order)
-        const int slot = atomicAdd(&ss.cnt[0], 1);
-        if (slot < kSubCap) {
-            ss.sub_key[slot] = key;
-            ss.sub_idx[slot] = idx;
+#pragma unroll
+    for (int c = 0; c < kMaxC; ++c) {  // gather b2's members (any order)
+        if (c < C && i0 + c < nc && ((c_key[i0 + c] >> 12) & 0xFFu) == b2) {
+            const int slot = atomicAdd(&ss.cnt[0], 1);
+            if (slot < kSubCap) {
+                ss.sub_key[slot] = c_key[i0 + c];
+                ss.sub_idx[slot] = c_idx[i0 + c];
+            }
         }
     }
     __syncthreads();
     const int m2 = ss.cnt[0];
     if (m2 > kSubCap) return false;
-    bool take = have && bk > b2;
-    if (have && bk == b2) {
-        const uint64_t mine = ((uint64_t)key << 32) | (uint32_t)~(uint32_t)idx;
-        int better = 0;
-        for (int u = 0; u < m2; ++u)
-            better += (((uint64_t)ss.sub_key[u] << 32) | (uint32_t)~(uint32_t)ss.sub_idx[u]) > mine;
-        take = better < need2;
+    uint32_t takes = 0;  // bit c: candidate i0 + c is chosen
+#pragma unroll
+    for (int c = 0; c < kMaxC; ++c) {
+        if (!(c < C && i0 + c < nc)) continue;
+        const uint32_t key = c_key[i0 + c];
+        const uint32_t bk = (key >> 12) & 0xFFu;
+        bool take = bk > b2;
+        if (bk == b2) {
+            const uint64_t mine = ((uint64_t)key << 32) | (uint32_t)~(uint32_t)c_idx[i0 + c];
+            int better = 0;
+            for (int u = 0; u < m2; ++u)
+                better += (((uint64_t)ss.sub_key[u] << 32) | (uint32_t)~(uint32_t)ss.sub_idx[u]) > mine;
+            take = better < need2;
+        }
+        takes |= (uint32_t)take << c;
     }
     int tot;
-    const int pos = block_scan_excl<kWG>(take ? 1 : 0, ss.s_wave, &tot);
-    if (take) ss.sel[pos] = idx;
+    int pos = block_scan_excl<kWG>(__popc(takes), ss.s_wave, &tot);
+#pragma unroll
+    for (int c = 0; c < kMaxC; ++c)
+        if (takes >> c & 1u) ss.sel[pos++] = c_idx[i0 + c];
     __syncthreads();
     const int32_t *sel = ss.sel;
     for (int i = tid; i < na + need; i += kWG) {
@@ -578,10 +467,7 @@ __global__ __launch_bounds__(kWG) void topk_onekernel_kernel(TopkArgs a) {
         __syncthreads();
         ok = na < K && nc <= kTopkCand && na + nc >= K;
         if (ok) {
-            if (nc <= kWG)
-                ok = select_ordered(v, na, c_key, c_idx, nc, K, out, ss);
-            else
-                ok = select_emit(v, na, c_key, c_idx, nc, n, K, out, ss);
+            ok = select_ordered(v, na, c_key, c_idx, nc, K, out, ss);
         }
     }
     if (!ok) {
@@ -719,10 +605,7 @@ __global__ __launch_bounds__(kWG) void topk_final_kernel(TopkArgs a, int n_flt) 
     __syncthreads();
     ok = ok && !s_bad && na_tot < K && nc_tot <= kTopkCand && na_tot + nc_tot >= K;
     if (ok) {  // the regions' lists are in index order, and so are their concatenations
-        if (nc_tot <= kWG)
-            ok = select_ordered(v, na_tot, c_key, c_idx, nc_tot, K, out, ss);
-        else
-            ok = select_emit(v, na_tot, c_key, c_idx, nc_tot, n, K, out, ss);
+        ok = select_ordered(v, na_tot, c_key, c_idx, nc_tot, K, out, ss);
     }
     if (!ok) {
         __syncthreads();

@@ -26,9 +26,9 @@ __device__ __forceinline__ void lds_hist_add(uint32_t *h, uint32_t bin, bool val
 }
 
 // Workgroup of 256 threads: store the window of its 4096-bin LDS histogram `lh`
-// that ends at its highest non-empty bin M: cnt[t] = lh[M - 127 + t] (0 below
-// bin 0), hdr = M (or -1 when empty).  Bins within 128 of the global highest
-// bin are then exactly known from all windows together.
+// that ends at its highest non-empty bin M: cnt[t] = lh[M - (kTopkWin - 1) + t]
+// (0 below bin 0), hdr = M (or -1 when empty).  Bins within kTopkWin of the
+// global highest bin are then exactly known from all windows together.
 __device__ __forceinline__ void hist_window_store(const uint32_t *lh, int32_t *hdr, uint32_t *cnt, int *s_red) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     __syncthreads();
@@ -54,7 +54,7 @@ __device__ __forceinline__ void hist_window_store(const uint32_t *lh, int32_t *h
 // holding the K-th largest key (kNoBin if it lies below that range or there is
 // nothing).  Any block size that is a multiple of 64 (up to 1024); s_hist
 // needs kTopkWin words, s_red one int per wave.  Four threads take a window
-// (32 counts each).  Every header and the counts of the first blockDim/4
+// (kTopkWin / 4 counts each).  Every header and the counts of the first blockDim/4
 // windows are loaded in one round (the caller may have its own loads in
 // flight too); further windows, if any, take one more round per blockDim/4.
 __device__ __forceinline__ uint32_t window_threshold(const int32_t *hdr, const uint32_t *cnt, int n_win, int K,
@@ -64,15 +64,17 @@ __device__ __forceinline__ uint32_t window_threshold(const int32_t *hdr, const u
     const int seg = tid & 3;
     int m = -1;
     for (int w = tid; w < n_win; w += nt) m = max(m, hdr[w]);
+    constexpr int kPerSeg = kTopkWin / 4;  // counts per thread of a window
+    constexpr int kVecs = kPerSeg / 4;
     int mw = -1;
-    u32x4_t x[8];
+    u32x4_t x[kVecs];
     auto load_window = [&](int w) {
         mw = -1;
         if (w < n_win) {
             mw = hdr[w];
-            const u32x4_t *src = (const u32x4_t *)(cnt + (size_t)w * kTopkWin + 32 * seg);
+            const u32x4_t *src = (const u32x4_t *)(cnt + (size_t)w * kTopkWin + kPerSeg * seg);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = src[i];
+            for (int i = 0; i < kVecs; ++i) x[i] = src[i];
         }
     };
     load_window(tid >> 2);
@@ -86,9 +88,9 @@ __device__ __forceinline__ uint32_t window_threshold(const int32_t *hdr, const u
     if (M < 0) return kNoBin;  // the same in every thread
     for (int w0 = 0;;) {
         if (mw >= 0) {
-            const int off = mw - M + 32 * seg;  // merged-window bin of this thread's first count
+            const int off = mw - M + kPerSeg * seg;  // merged-window bin of this thread's first count
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < kVecs; ++i)
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const int b = off + 4 * i + c;
