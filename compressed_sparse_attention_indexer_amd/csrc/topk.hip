@@ -33,6 +33,8 @@ constexpr int kWaves = kWG / 64;
 constexpr int kAuxThreads = 256;
 constexpr int kPerThread = kTopkAuxChunk / kAuxThreads;  // 8 scores per thread
 constexpr int kSubCap = 1024;                            // candidates sharing the final sub-bin
+constexpr int kFinalGroup = 8;                           // selection: threads per filter region
+constexpr int kSpecC = 2;                                // candidates per thread loaded in the first round
 
 
 struct TopkShared {
@@ -155,28 +157,6 @@ __device__ __forceinline__ int query_visible(const TopkArgs &a, int qi) {
     const int b = qi / a.T;
     const int n = visible_entries(a.seq_len[b], a.q_pos[qi], a.ratio);
     return n < a.n_max ? n : a.n_max;
-}
-
-// Block-wide exclusive prefix sum over the 1024 threads (one value each).
-__device__ __forceinline__ int block_exclusive_scan(int x, int *s_wave, int *total) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int inc = x;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(inc, o);
-        if (lane >= o) inc += t;
-    }
-    if (lane == 63) s_wave[wave] = inc;
-    __syncthreads();
-    int before = 0, all = 0;
-    for (int w = 0; w < kWaves; ++w) {
-        const int c = s_wave[w];
-        before += w < wave ? c : 0;
-        all += c;
-    }
-    __syncthreads();
-    *total = all;
-    return before + inc - x;
 }
 
 // Block-wide exclusive scan for NT threads (a multiple of 64); s_wave holds
@@ -537,8 +517,6 @@ __global__ __launch_bounds__(kWG) void topk_final_kernel(TopkArgs a, int n_flt) 
     __shared__ SelectShared ss;
     __shared__ TopkShared sh;
     __shared__ int s_bad;
-    __shared__ int s_pa[kWG];
-    __shared__ int s_pc[kWG];
     const int qi = blockIdx.x;
     const int tid = threadIdx.x;
     const int n = query_visible(a, qi);
@@ -552,55 +530,55 @@ __global__ __launch_bounds__(kWG) void topk_final_kernel(TopkArgs a, int n_flt) 
     bool ok = true;
     if (tid == 0) s_bad = 0;
     __syncthreads();
-    // gather the filter lists of the workgroups that covered visible entries:
-    // headers first (one round), then a flattened copy (one more round)
+    // Gather the filter lists of the workgroups that covered visible entries,
+    // kFinalGroup threads per region.  One round loads every header together
+    // with the first entries of each list (lists are short: a few entries per
+    // region in practice); whatever lies beyond takes one more round.
     const int n_reg = (n + kTopkAuxChunk - 1) / kTopkAuxChunk;
     const uint32_t *reg0 = a.flt + (size_t)qi * n_flt * kFltRegionWords;
+    constexpr int kRegPer = kWG / kFinalGroup;  // regions per pass
+    const int u = tid % kFinalGroup;
     int na_tot = 0, nc_tot = 0;
-    for (int r0 = 0; ok && r0 < n_reg; r0 += kWG) {
-        const int r = r0 + tid;
-        const int nr = n_reg - r0 < kWG ? n_reg - r0 : kWG;
-        uint32_t na = 0, nc = 0;
-        if (r < n_reg) {
-            na = reg0[(size_t)r * kFltRegionWords + 0];
-            nc = reg0[(size_t)r * kFltRegionWords + 1];
-            if (na > (uint32_t)kFltAboveCap || nc > (uint32_t)kFltCandCap) {
-                s_bad = 1;
-                na = nc = 0;
+    for (int r0 = 0; r0 < n_reg; r0 += kRegPer) {
+        const int r = r0 + tid / kFinalGroup;
+        const bool live = r < n_reg;
+        const uint32_t *reg = reg0 + (size_t)(live ? r : r0) * kFltRegionWords;
+        uint32_t na = reg[0], nc = reg[1];
+        uint32_t sa = reg[2 + u];
+        uint32_t sck[kSpecC], sci[kSpecC];
+#pragma unroll
+        for (int k = 0; k < kSpecC; ++k) {
+            sck[k] = reg[2 + kFltAboveCap + u + kFinalGroup * k];
+            sci[k] = reg[2 + kFltAboveCap + kFltCandCap + u + kFinalGroup * k];
+        }
+        if (!live) na = nc = 0;
+        if (na > (uint32_t)kFltAboveCap || nc > (uint32_t)kFltCandCap) {
+            s_bad = 1;  // overflowed or unusable region: the exact path runs
+            na = nc = 0;
+        }
+        int tot;
+        const int pre = block_scan_excl<kWG>(u == 0 ? (int)(na | (nc << 16)) : 0, ss.s_wave, &tot);
+        // this region's list offsets: the scan value of its first thread
+        const int base = __shfl(pre, (tid & 63) & ~(kFinalGroup - 1));
+        const int pa = na_tot + (base & 0xFFFF), pc = nc_tot + (base >> 16);
+        if ((uint32_t)u < na && pa + u < K) v[pa + u] = (int32_t)sa;
+#pragma unroll
+        for (int k = 0; k < kSpecC; ++k) {
+            const int i = u + kFinalGroup * k;
+            if ((uint32_t)i < nc && pc + i < kTopkCand) {
+                c_key[pc + i] = sck[k];
+                c_idx[pc + i] = (int32_t)sci[k];
             }
         }
-        int ta, tc;
-        const int pa = block_exclusive_scan((int)na, ss.s_wave, &ta);
-        const int pc = block_exclusive_scan((int)nc, ss.s_wave, &tc);
-        s_pa[tid] = pa;  // exclusive prefix of this block of regions
-        s_pc[tid] = pc;
-        __syncthreads();
-        // entry f of the block's above-lists lives in region r with s_pa[r] <= f < s_pa[r+1]
-        for (int f = tid; f < ta; f += kWG) {
-            int lo = 0, hi = nr - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (s_pa[mid] <= f) lo = mid; else hi = mid - 1;
+        for (int i = kFinalGroup + u; i < (int)na; i += kFinalGroup)  // beyond the first round
+            if (pa + i < K) v[pa + i] = (int32_t)reg[2 + i];
+        for (int i = kFinalGroup * kSpecC + u; i < (int)nc; i += kFinalGroup)
+            if (pc + i < kTopkCand) {
+                c_key[pc + i] = reg[2 + kFltAboveCap + i];
+                c_idx[pc + i] = (int32_t)reg[2 + kFltAboveCap + kFltCandCap + i];
             }
-            const uint32_t *reg = reg0 + (size_t)(r0 + lo) * kFltRegionWords;
-            if (na_tot + f < K) v[na_tot + f] = (int32_t)reg[2 + (f - s_pa[lo])];
-        }
-        for (int f = tid; f < tc; f += kWG) {
-            int lo = 0, hi = nr - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (s_pc[mid] <= f) lo = mid; else hi = mid - 1;
-            }
-            const uint32_t *reg = reg0 + (size_t)(r0 + lo) * kFltRegionWords;
-            const int i = f - s_pc[lo];
-            if (nc_tot + f < kTopkCand) {
-                c_key[nc_tot + f] = reg[2 + kFltAboveCap + i];
-                c_idx[nc_tot + f] = (int32_t)reg[2 + kFltAboveCap + kFltCandCap + i];
-            }
-        }
-        na_tot += ta;
-        nc_tot += tc;
-        __syncthreads();
+        na_tot += tot & 0xFFFF;
+        nc_tot += tot >> 16;
     }
     __syncthreads();
     ok = ok && !s_bad && na_tot < K && nc_tot <= kTopkCand && na_tot + nc_tot >= K;
