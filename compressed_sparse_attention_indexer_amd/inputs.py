@@ -33,6 +33,7 @@ _TID = {
     "q": 1, "q_idx": 2, "w": 3, "k_idx": 4, "kv": 5, "v": 6, "win": 7,
     "sink": 8, "seq_len": 9, "win_v": 10,
     "hca_q": 11, "hca_kv": 12, "hca_win": 13, "hca_sink": 14,
+    "q8": 15, "k8": 16,
 }
 _ROW_CHUNK = 65536  # rows per independently seeded chunk of a per-sequence cache
 
@@ -226,3 +227,53 @@ def make_case(wl: Workload, with_hca: bool = True, seq_lens=None) -> Case:
 def as_float64(x: np.ndarray, dtype: str) -> np.ndarray:
     """Exact float64 view of a drawn tensor (bf16 bits or float32)."""
     return (bf16_to_f32(x) if dtype == "bf16" else np.asarray(x, dtype=np.float32)).astype(np.float64)
+
+
+# ---------------------------------------------------------------- fp8 (OCP E4M3) index tensors
+# Input preparation for the fp8 indexer: float draws are stored as E4M3 codes
+# with one float32 scale per row (amax / 448), codes rounded to nearest even
+# and saturated at the largest finite value.  The path only ever reads codes
+# and scales.
+
+def _e4m3_table() -> np.ndarray:
+    """Values of the non-negative finite codes 0..126, ascending."""
+    c = np.arange(127)
+    e, m = c >> 3, c & 7
+    return np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (e.astype(np.float64) - 7))
+
+
+def e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """float -> E4M3 code (uint8): round to nearest, ties to even code, saturating."""
+    t = _e4m3_table()
+    a = np.minimum(np.abs(np.asarray(x, np.float64)), t[-1])
+    hi = np.clip(np.searchsorted(t, a), 1, 126)
+    lo = hi - 1
+    dl, dh = a - t[lo], t[hi] - a
+    pick = np.where(dl < dh, lo, np.where(dh < dl, hi, np.where(lo % 2 == 0, lo, hi)))
+    pick = np.where(a == 0, 0, pick)
+    sign = (np.signbit(np.asarray(x)) & (pick != 0)).astype(np.uint8) << 7
+    return (pick.astype(np.uint8) | sign).astype(np.uint8)
+
+
+def quantize_rows_e4m3(x: np.ndarray):
+    """x [..., D] float -> (codes [..., D] uint8, scale [...] float32), scale = amax / 448."""
+    x = np.asarray(x, np.float32)
+    amax = np.abs(x).max(axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    return e4m3_codes(x / scale[..., None]), scale
+
+
+def make_fp8_index(case: "Case"):
+    """fp8 index tensors for a case's shapes, drawn like q_idx / k_idx: returns
+    (q8 [B,T,HI,DI], q_scale [B,T,HI], k8: B x [N_b,DI], k_scale: B x [N_b])."""
+    wl = case.wl
+    B, T, HI, DI = wl.batch, wl.q_len, wl.index_heads, wl.index_dim
+    si = 1.0 / math.sqrt(DI)
+    qf = _normal((B, T, HI, DI), si, "f32", wl.seed, _TID["q8"])
+    q8, qs = quantize_rows_e4m3(qf)
+    k8, ks = [], []
+    for b in range(B):
+        c, sc = quantize_rows_e4m3(_rows(int(case.n_entries[b]), DI, si, "f32", wl.seed, _TID["k8"], b))
+        k8.append(c)
+        ks.append(sc)
+    return q8, qs, k8, ks

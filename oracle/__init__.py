@@ -45,13 +45,16 @@ def lib():
         L.oracle_visible_count.restype = I64
         L.oracle_index_scores.argtypes = [I] * 7 + [P, P, P, P, P, I, P]
         L.oracle_topk.argtypes = [I, I, I, I, P, I, P, P, P]
+        L.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_value.restype = D
+        L.oracle_index_scores_fp8.argtypes = [I] * 6 + [P] * 7 + [I, P]
         L.oracle_attend_rows.argtypes = [I, I, I, D, P, P, P, I, P, P, P]
         L.oracle_partial_rows.argtypes = [I, I, I, D, P, P, P, I, P, P, P]
         L.oracle_merge_partials.argtypes = [I, I, I, P, P, P, P, P, P]
         L.oracle_sparse_mqa.argtypes = [I] * 8 + [D] + [P] * 13
         L.oracle_hca_mqa.argtypes = [I] * 7 + [D] + [P] * 12
         L.oracle_csa_attention.argtypes = [I] * 11 + [D] + [P] * 13 + [I] + [P] * 4
-        for f in ("oracle_index_scores", "oracle_topk", "oracle_attend_rows", "oracle_partial_rows",
+        for f in ("oracle_index_scores", "oracle_index_scores_fp8", "oracle_topk", "oracle_attend_rows", "oracle_partial_rows",
                   "oracle_merge_partials", "oracle_sparse_mqa", "oracle_hca_mqa",
                   "oracle_csa_attention"):
             getattr(L, f).restype = I
@@ -110,6 +113,28 @@ def index_scores(q_idx, w, k_idx: List[np.ndarray], seq_len, q_pos, *, ratio: in
     out = np.empty((B, T, n_max), dtype=np.float32)
     _check(lib().oracle_index_scores(B, T, HI, DI, ratio, act, _dt(dtype), _p(qa), _p(wa), ks.ptr,
                                      _p(sl), _p(qp), n_max, _p(out)), "oracle_index_scores")
+    return out
+
+
+def e4m3_value(code: int) -> float:
+    return float(lib().oracle_e4m3_value(code))
+
+
+def index_scores_fp8(q8, q_scale, w, k8: List[np.ndarray], k_scale: List[np.ndarray], seq_len, q_pos, *,
+                     ratio: int, n_max: int, act: int = ACT_RELU) -> np.ndarray:
+    """q8 [B,T,HI,DI] uint8 codes, q_scale [B,T,HI], k8[b] [N_b,DI] codes, k_scale[b] [N_b]."""
+    B, T, HI, DI = q8.shape
+    qa = np.ascontiguousarray(q8, np.uint8)
+    qs = np.ascontiguousarray(q_scale, np.float32)
+    wa = np.ascontiguousarray(w, np.float32)
+    kc = [np.ascontiguousarray(k, np.uint8) for k in k8]
+    kss = [np.ascontiguousarray(x, np.float32) for x in k_scale]
+    kp = (ctypes.c_void_p * len(kc))(*[k.ctypes.data for k in kc])
+    sp = (ctypes.c_void_p * len(kss))(*[x.ctypes.data for x in kss])
+    sl, qp = np.ascontiguousarray(seq_len, np.int32), np.ascontiguousarray(q_pos, np.int32)
+    out = np.empty((B, T, n_max), dtype=np.float32)
+    _check(lib().oracle_index_scores_fp8(B, T, HI, DI, ratio, act, _p(qa), _p(qs), _p(wa), kp, sp, _p(sl), _p(qp),
+                                         n_max, _p(out)), "oracle_index_scores_fp8")
     return out
 
 

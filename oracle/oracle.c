@@ -98,6 +98,55 @@ static int by_value(const void *a, const void *b) {
     return (x > y) - (x < y);
 }
 
+double oracle_e4m3_value(uint8_t code) {
+    const int sign = code >> 7, e = (code >> 3) & 0xF, m = code & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);  /* subnormal: m/8 * 2^(1-7) */
+    else
+        v = ldexp(1.0 + m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+/* R7: dequantize (code value * row scale, float64), then the score definition. */
+int oracle_index_scores_fp8(int B, int T, int HI, int DI, int ratio, int act, const uint8_t *q8,
+                            const float *q_scale, const float *w, const uint8_t *const *k8,
+                            const float *const *k_scale, const int32_t *seq_len, const int32_t *q_pos,
+                            int n_max, float *scores) {
+    if (B <= 0 || T <= 0 || HI <= 0 || DI <= 0 || ratio <= 0 || n_max <= 0) return ORACLE_EINVAL;
+    if (act != ORACLE_ACT_RELU && act != ORACLE_ACT_NONE) return ORACLE_EINVAL;
+    if (!q8 || !q_scale || !w || !k8 || !k_scale || !seq_len || !q_pos || !scores) return ORACLE_EINVAL;
+    for (int bt = 0; bt < B * T; ++bt) {
+        int b = bt / T;
+        if (!check_query(seq_len[b], q_pos[bt]) || seq_len[b] / ratio > n_max) return ORACLE_EINVAL;
+    }
+    for (int bt = 0; bt < B * T; ++bt) {
+        const int b = bt / T;
+        const int64_t L = seq_len[b], p = q_pos[bt];
+#pragma omp parallel for schedule(static)
+        for (int64_t j = 0; j < n_max; ++j) {
+            if (!entry_visible(j, L, p, ratio)) {
+                scores[(int64_t)bt * n_max + j] = -INFINITY;
+                continue;
+            }
+            const double ks = (double)k_scale[b][j];
+            double s = 0.0;
+            for (int h = 0; h < HI; ++h) {
+                const double qs = (double)q_scale[(int64_t)bt * HI + h];
+                double dot = 0.0;
+                for (int d = 0; d < DI; ++d)
+                    dot += oracle_e4m3_value(q8[((int64_t)bt * HI + h) * DI + d]) * qs *
+                           (oracle_e4m3_value(k8[b][j * DI + d]) * ks);
+                double a = (act == ORACLE_ACT_RELU) ? (dot > 0.0 ? dot : 0.0) : dot;
+                s += (double)w[(int64_t)bt * HI + h] * a;
+            }
+            scores[(int64_t)bt * n_max + j] = (float)s;
+        }
+    }
+    return ORACLE_OK;
+}
+
 int oracle_topk(int B, int T, int ratio, int K, const float *scores, int n_max,
                 const int32_t *seq_len, const int32_t *q_pos, int32_t *idx) {
     if (B <= 0 || T <= 0 || ratio <= 0 || K <= 0 || n_max <= 0) return ORACLE_EINVAL;

@@ -16,6 +16,8 @@
  *       dot product and per-head importance weights and keeps the top-k, and a
  *       learnable per-head scalar sink; section 2 "Unified head dimension":
  *       one 512-d row serves as key and value.
+ *   [C] "DeepSeek-V4-Flash-0731" (mic coverage page), config table:
+ *       quantization_config (fp8, e4m3 format, dynamic activation scheme).
  *   [B] "DeepSeek-V4-Flash" (llm-atlas), raw config.json table: index_n_heads,
  *       index_head_dim, index_topk, sliding_window, head_dim, 64 q-heads / 1
  *       kv-head.
@@ -29,7 +31,9 @@
  *      ascending by index and padded with -1;
  *   R5 one softmax over selected rows then window rows, plus the sink as one
  *      extra logit per head that adds exp(sink) to the denominator only;
- *   R6 softmax scale is a caller value (1/sqrt(D) by default).
+ *   R6 softmax scale is a caller value (1/sqrt(D) by default);
+ *   R7 fp8 index tensors carry one fp32 scale per row (query-head row, key
+ *      entry); the pages name the format but not the scale granularity.
  */
 #ifndef CSA_ORACLE_H
 #define CSA_ORACLE_H
@@ -58,6 +62,23 @@ int oracle_index_scores(int B, int T, int HI, int DI, int ratio, int act, int dt
                         const void *q_idx, const float *w, const void *const *k_idx,
                         const int32_t *seq_len, const int32_t *q_pos, int n_max,
                         float *scores);
+
+/* Value of one OCP FP8 E4M3 code (1 sign, 4 exponent bits with bias 7, 3
+ * mantissa bits; exponent 0 is subnormal, m * 2^-9; S.1111.111 is NaN; no
+ * infinities).  Exact in float64. */
+double oracle_e4m3_value(uint8_t code);
+
+/* Indexer scores with fp8 index queries and keys (the next row after the bf16
+ * path): [C] quantization_config (fp8, e4m3, dynamic activation scales) and
+ * [A] sec. 1 indexer bullet (quantization-aware training).  Reading R7: one
+ * fp32 scale per index-query row (query, head) and per key row (entry);
+ * value = code value * scale.  q8 [B,T,HI,DI] codes, q_scale [B,T,HI],
+ * k8[b] -> [N_b,DI] codes, k_scale[b] -> [N_b].  Then exactly the definition
+ * of oracle_index_scores on the dequantized values (float64, rounded once). */
+int oracle_index_scores_fp8(int B, int T, int HI, int DI, int ratio, int act, const uint8_t *q8,
+                            const float *q_scale, const float *w, const uint8_t *const *k8,
+                            const float *const *k_scale, const int32_t *seq_len, const int32_t *q_pos,
+                            int n_max, float *scores);
 
 /* Top-k selection (R4), [B] index_topk.  idx [B,T,K]. */
 int oracle_topk(int B, int T, int ratio, int K, const float *scores, int n_max,

@@ -465,3 +465,79 @@ def test_fixture_golden_file_matches():
     np.testing.assert_array_equal(scores, np.array(g["scores"], np.float32))
     np.testing.assert_allclose(out, np.array(g["out"]), rtol=1e-12)
     np.testing.assert_allclose(lse, np.array(g["lse"]), rtol=1e-12)
+
+
+# --------------------------------------------------------------------------- fp8 index tensors (E4M3)
+
+@pytest.mark.parametrize("code,value", [
+    (0x00, 0.0), (0x01, 2.0 ** -9), (0x07, 7 * 2.0 ** -9), (0x08, 2.0 ** -6), (0x38, 1.0), (0x3F, 1.875),
+    (0x40, 2.0), (0x77, 240.0), (0x7E, 448.0), (0xB8, -1.0), (0xFE, -448.0), (0x81, -(2.0 ** -9)),
+])
+def test_e4m3_decode_matches_format_table(code, value):
+    """OCP E4M3: bias 7, 3 mantissa bits, subnormals m * 2^-9, largest finite 448."""
+    assert oracle.e4m3_value(code) == value
+
+
+def test_e4m3_special_codes():
+    assert math.isnan(oracle.e4m3_value(0x7F)) and math.isnan(oracle.e4m3_value(0xFF))
+    z = oracle.e4m3_value(0x80)
+    assert z == 0.0 and math.copysign(1.0, z) == -1.0
+
+
+def test_e4m3_round_trip_of_the_input_encoder():
+    """Every finite code decodes to a value the encoder maps back to that code."""
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF, 0x80)], np.uint8)
+    vals = np.array([oracle.e4m3_value(int(c)) for c in codes])
+    np.testing.assert_array_equal(inputs.e4m3_codes(vals), codes)
+
+
+def _fp8_case(seed, B=2, T=1, HI=3, DI=8, N=11):
+    r = np.random.default_rng(seed)
+    q8 = r.integers(0, 256, size=(B, T, HI, DI)).astype(np.uint8)
+    q8[(q8 & 0x7F) == 0x7F] = 0x38  # no NaN codes
+    k8 = [r.integers(0, 256, size=(N, DI)).astype(np.uint8) for _ in range(B)]
+    for k in k8:
+        k[(k & 0x7F) == 0x7F] = 0x30
+    w = r.random((B, T, HI)).astype(np.float32)
+    seq = np.array([4 * N] * B, np.int32)
+    return q8, w, k8, seq
+
+
+def test_fp8_scores_with_unit_scales_equal_the_bf16_definition():
+    """E4M3 values are exact in bf16: with all scales 1 the fp8 scores are the
+    bf16 scores of the decoded values, bit for bit."""
+    q8, w, k8, seq = _fp8_case(3)
+    B, T, HI, DI = q8.shape
+    dec = np.vectorize(oracle.e4m3_value)
+    qv = dec(q8).astype(np.float32)
+    kv = [dec(k).astype(np.float32) for k in k8]
+    ones_q = np.ones((B, T, HI), np.float32)
+    ones_k = [np.ones(len(k), np.float32) for k in k8]
+    got = oracle.index_scores_fp8(q8, ones_q, w, k8, ones_k, seq, seq - 1, ratio=4, n_max=11)
+    want = oracle.index_scores(inputs.bf16_bits(qv), w, [inputs.bf16_bits(k) for k in kv], seq, seq - 1,
+                               ratio=4, n_max=11, dtype="bf16")
+    np.testing.assert_array_equal(got, want)
+
+
+def test_fp8_row_scales_act_per_entry_and_per_head():
+    """A power-of-two key scale multiplies exactly that entry's score; a query
+    scale on head h acts like the same factor on w_h (ReLU commutes with
+    positive scaling)."""
+    q8, w, k8, seq = _fp8_case(4)
+    B, T, HI, DI = q8.shape
+    r = np.random.default_rng(5)
+    qs = r.uniform(0.5, 2.0, (B, T, HI)).astype(np.float32)
+    ks = [r.uniform(0.5, 2.0, len(k)).astype(np.float32) for k in k8]
+    base = oracle.index_scores_fp8(q8, qs, w, k8, ks, seq, seq - 1, ratio=4, n_max=11)
+    ks2 = [k.copy() for k in ks]
+    ks2[1][7] *= 4.0
+    s2 = oracle.index_scores_fp8(q8, qs, w, k8, ks2, seq, seq - 1, ratio=4, n_max=11)
+    want = base.copy()
+    want[1, 0, 7] *= 4.0
+    np.testing.assert_array_equal(s2, want)
+    qs3, w3 = qs.copy(), w.copy()
+    qs3[0, 0, 1] *= 2.0
+    w3[0, 0, 1] *= 2.0
+    a = oracle.index_scores_fp8(q8, qs3, w, k8, ks, seq, seq - 1, ratio=4, n_max=11)
+    b = oracle.index_scores_fp8(q8, qs, w3, k8, ks, seq, seq - 1, ratio=4, n_max=11)
+    np.testing.assert_allclose(a, b, rtol=1e-6)
