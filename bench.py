@@ -249,6 +249,42 @@ def bench_hca(torch, csa, case, args):
             "GBps": b / (ms * 1e-3) / 1e9, "frac_hbm_peak": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
+def fp8_scorer_bytes(n_ent, n_queries):
+    """fp8 index keys: 128 B codes + 4 B scale per entry; per query 8 KiB of codes, 256 B of
+    query scales and 256 B of weights."""
+    return int(sum(132 * int(n) for n in n_ent)) + 8704 * n_queries
+
+
+def bench_fp8_scores(torch, csa, case, args):
+    """The indexer scorer on fp8 (E4M3) index tensors with per-row scales, same shapes."""
+    from compressed_sparse_attention_indexer_amd import inputs
+    wl = case.wl
+    q8, qs, k8, ks = inputs.make_fp8_index(case)
+    dev = "cuda"
+    q8_t, qs_t = torch.from_numpy(q8).to(dev), torch.from_numpy(qs).to(dev)
+    w_t = torch.from_numpy(case.w).to(dev)
+    copies = []
+    for _ in range(args.copies):
+        k_t = [torch.from_numpy(k).to(dev) for k in k8]
+        s_t = [torch.from_numpy(x).to(dev) for x in ks]
+        copies.append((k_t, s_t, csa.ptr_array(k_t, dev), csa.ptr_array(s_t, dev)))
+    seq_t, pos_t = torch.from_numpy(case.seq_len).to(dev), torch.from_numpy(case.q_pos).to(dev)
+    dims = csa.make_dims(batch=wl.batch, q_len=wl.q_len, max_entries=case.max_entries)
+    scores = torch.empty((wl.batch, wl.q_len, case.max_entries), dtype=torch.float32, device=dev)
+
+    def call(i):
+        c = copies[i % len(copies)]
+        csa.csa_index_scores_fp8(dims, q8_t, qs_t, w_t, c[2], c[3], seq_t, pos_t, scores=scores)
+
+    g = capture(torch, call, args.graph_steps)
+    ms, _, _ = time_graph(torch, g, args.graph_steps, args.steps, args.warmup)
+    Q = wl.batch * wl.q_len
+    b = fp8_scorer_bytes(case.n_entries, Q)
+    return {"ms_per_call": ms, "alg_bytes": b, "GBps": b / (ms * 1e-3) / 1e9,
+            "frac_hbm_peak": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "vs_bf16_scorer": None}
+
+
 def traffic_from_profile():
     """HBM bytes per scorer launch from the committed rocprofv3 counter runs,
     only while the scorer source is the one the counters were taken on."""
@@ -314,6 +350,10 @@ def main():
     breakdown = {wl.name: main_res}
     if case.hca_q is not None:
         breakdown[wl.name + "_hca"] = bench_hca(torch, csa, case, args)
+    if wl.dtype == "bf16":
+        f8 = bench_fp8_scores(torch, csa, case, args)
+        f8["vs_bf16_scorer"] = main_res["kernel_ms"]["index_scores"] / f8["ms_per_call"]
+        breakdown[wl.name + "_fp8_index_scores"] = f8
     Q = wl.batch * wl.q_len
     scorer_ms = main_res["kernel_ms"]["index_scores"]
     alg = main_res["scorer_alg_bytes"]

@@ -17,6 +17,7 @@ from ._lib import (CSA_ACT_NONE, CSA_ACT_RELU, CSA_BF16, CSA_F32, CSA_OP_ATTENTI
                    load_library)
 
 __all__ = ["CsaDims", "CsaError", "make_dims", "workspace_size", "ptr_array", "csa_index_scores",
+           "csa_index_scores_fp8",
            "csa_topk_select", "csa_sparse_mqa_decode", "hca_mqa_decode", "csa_attention", "load_library",
            "CSA_F32", "CSA_BF16", "CSA_ACT_RELU", "CSA_ACT_NONE"]
 
@@ -93,6 +94,20 @@ def csa_index_scores(dims: CsaDims, q_idx, w, k_idx: PtrArg, seq_len, q_pos, sco
     ws, nws = _ws(dims, CSA_OP_INDEX_SCORES, workspace, dev)
     check(load_library().csa_index_scores(ctypes.byref(dims), _p(q_idx), _p(w), kp, _p(seq_len), _p(q_pos),
                                           _p(scores), _p(ws), nws, _stream(stream)), "csa_index_scores")
+    return scores
+
+
+def csa_index_scores_fp8(dims: CsaDims, q8, q_scale, w, k8: PtrArg, k_scale: PtrArg, seq_len, q_pos, scores=None,
+                         stream=None):
+    """Indexer scores from fp8 (E4M3) index tensors with per-row scales (see csa.h)."""
+    torch = _torch()
+    dev = q8.device
+    if scores is None:
+        scores = torch.empty((dims.batch, dims.q_len, dims.max_entries), dtype=torch.float32, device=dev)
+    kp, _keep = _pa(k8, dev)
+    sp, _keep2 = _pa(k_scale, dev)
+    check(load_library().csa_index_scores_fp8(ctypes.byref(dims), _p(q8), _p(q_scale), _p(w), kp, sp, _p(seq_len),
+                                              _p(q_pos), _p(scores), _stream(stream)), "csa_index_scores_fp8")
     return scores
 
 

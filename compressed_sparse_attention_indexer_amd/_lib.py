@@ -16,8 +16,9 @@ CSA_ACT_RELU, CSA_ACT_NONE = 0, 1
 CSA_OP_INDEX_SCORES, CSA_OP_TOPK, CSA_OP_SPARSE_MQA, CSA_OP_HCA_MQA, CSA_OP_ATTENTION = range(5)
 
 # every symbol include/csa.h declares
-EXPORTS = ("csa_workspace_size", "csa_index_scores", "csa_topk_select", "csa_sparse_mqa_decode",
-           "hca_mqa_decode", "csa_attention", "csa_status_string", "csa_last_error", "csa_abi_version")
+EXPORTS = ("csa_workspace_size", "csa_index_scores", "csa_index_scores_fp8", "csa_topk_select",
+           "csa_sparse_mqa_decode", "hca_mqa_decode", "csa_attention", "csa_status_string", "csa_last_error",
+           "csa_abi_version")
 
 
 class CsaDims(ctypes.Structure):
@@ -54,11 +55,13 @@ def load_library(path: str = LIB_PATH):
     L.csa_status_string.argtypes = [I32]
     L.csa_workspace_size.argtypes = [DP, I32, ctypes.POINTER(SZ)]
     L.csa_index_scores.argtypes = [DP, P, P, P, P, P, P, P, SZ, P]
+    L.csa_index_scores_fp8.argtypes = [DP] + [P] * 9
     L.csa_topk_select.argtypes = [DP, P, P, P, P, P, SZ, P]
     L.csa_sparse_mqa_decode.argtypes = [DP] + [P] * 13 + [P, SZ, P]
     L.hca_mqa_decode.argtypes = [DP] + [P] * 12 + [P, SZ, P]
     L.csa_attention.argtypes = [DP] + [P] * 17 + [P, SZ, P]
-    for f in ("csa_workspace_size", "csa_index_scores", "csa_topk_select", "csa_sparse_mqa_decode",
+    for f in ("csa_workspace_size", "csa_index_scores", "csa_index_scores_fp8", "csa_topk_select",
+              "csa_sparse_mqa_decode",
               "hca_mqa_decode", "csa_attention"):
         getattr(L, f).restype = I32
     _lib = L

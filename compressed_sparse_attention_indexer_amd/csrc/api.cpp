@@ -311,6 +311,27 @@ csa_status csa_index_scores(const csa_dims *d, const void *q_idx, const float *w
     return hip_status(csa::launch_index_scores(a, d->dtype, (hipStream_t)stream), "csa_index_scores");
 }
 
+csa_status csa_index_scores_fp8(const csa_dims *d, const uint8_t *q8, const float *q_scale, const float *w,
+                                const void *const *k8, const void *const *k_scale, const int32_t *seq_len,
+                                const int32_t *q_pos, float *scores, void *stream) {
+    csa_status s;
+    if ((s = check_common(d))) return s;
+    if (d->index_act != CSA_ACT_RELU && d->index_act != CSA_ACT_NONE)
+        return fail(CSA_ERR_UNSUPPORTED, "unknown index_act %d", d->index_act);
+    if (d->index_heads != 64 || d->index_dim != 128)
+        return fail(CSA_ERR_UNSUPPORTED, "fp8 scorer needs index_heads 64 and index_dim 128 (got %d, %d)",
+                    d->index_heads, d->index_dim);
+    if ((s = check_score_ptrs(q8, w, k8, seq_len, q_pos, scores))) return s;
+    REQUIRE_PTR(q_scale);
+    REQUIRE_PTR(k_scale);
+    REQUIRE_ALIGN(q_scale, 4);
+    REQUIRE_ALIGN(k_scale, 8);
+    csa::ScoreArgs a = score_args(d, q8, w, k8, seq_len, q_pos, scores);
+    a.q_scale = q_scale;
+    a.k_scale = k_scale;
+    return hip_status(csa::launch_index_scores_fp8(a, (hipStream_t)stream), "csa_index_scores_fp8");
+}
+
 csa_status csa_topk_select(const csa_dims *d, const float *scores, const int32_t *seq_len, const int32_t *q_pos,
                            int32_t *topk_idx, void *ws, size_t ws_bytes, void *stream) {
     csa_status s;

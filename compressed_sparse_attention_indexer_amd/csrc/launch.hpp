@@ -23,9 +23,14 @@ struct ScoreArgs {
     int32_t *win_hdr;           // [Q, n_win]
     uint32_t *win_cnt;          // [Q, n_win, kTopkWin]
     int K;
+    // fp8 (E4M3) index tensors: per-row scales (null for bf16 / fp32)
+    const float *q_scale;       // [Q, HI]
+    const void *const *k_scale; // [B] -> [N_b] float
 };
 
 hipError_t launch_index_scores(const ScoreArgs &a, int dtype, hipStream_t stream);
+// fp8 (E4M3) index queries and keys with per-row scales, HI = 64, DI = 128
+hipError_t launch_index_scores_fp8(const ScoreArgs &a, hipStream_t stream);
 int score_workgroups(int n_max, int n_queries);  // bf16 scorer workgroups per query
 // many queries per sequence: the GEMM-tiled scorer (it writes no histogram windows)
 bool score_uses_tiles(int dtype, int T);

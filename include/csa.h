@@ -17,6 +17,8 @@
  *   [B] "DeepSeek-V4-Flash" (llm-atlas), raw config.json table: head_dim 512,
  *       64 query heads / 1 KV head, index_n_heads 64, index_head_dim 128,
  *       index_topk 512, sliding_window 128.
+ *   [C] "DeepSeek-V4-Flash-0731" (mic coverage page), config table:
+ *       quantization_config (fp8, E4M3 format, dynamic activation scheme).
  * Readings where the pages are silent:
  *   - indexer activation between the per-head dot product and the weighting:
  *     ReLU (CSA_ACT_RELU, default) or none (CSA_ACT_NONE); no other constants;
@@ -131,6 +133,28 @@ csa_status csa_index_scores(const csa_dims *dims, const void *q_idx, const float
                             const void *const *k_idx, const int32_t *seq_len,
                             const int32_t *q_pos, float *scores, void *workspace,
                             size_t ws_bytes, void *stream);
+
+/*
+ * Indexer scores with fp8 index tensors -- the same definition as
+ * csa_index_scores on dequantized values; [C] "DeepSeek-V4-Flash-0731"
+ * config table, quantization_config (fp8, E4M3 format, dynamic activation
+ * scales), and [A] INNOVATIONS 1, indexer bullet (quantization-aware
+ * training).  Reading: one fp32 scale per index-query row (query, head) and
+ * per key row (entry); a value is code * scale.
+ *   q8      device [B,T,HI,DI] uint8 OCP FP8 E4M3 codes (16-byte aligned)
+ *   q_scale device [B,T,HI] float32, > 0
+ *   w       device [B,T,HI] float32 importance weights
+ *   k8      device array of B device pointers, k8[b] -> [floor(L_b/r), DI] codes
+ *   k_scale device array of B device pointers, k_scale[b] -> [floor(L_b/r)] float32, > 0
+ *   seq_len, q_pos, scores: as csa_index_scores.
+ * Requires index_heads 64 and index_dim 128 (dims->dtype is not used).
+ * Scales must be positive (ReLU then commutes with them); NaN codes are not
+ * checked.  fp8 x fp8 products are exact in fp32; accumulation is fp32.
+ */
+csa_status csa_index_scores_fp8(const csa_dims *dims, const uint8_t *q8, const float *q_scale,
+                                const float *w, const void *const *k8, const void *const *k_scale,
+                                const int32_t *seq_len, const int32_t *q_pos, float *scores,
+                                void *stream);
 
 /*
  * Top-k selection -- [B] index_topk; [A] INNOVATIONS 1, indexer bullet.

@@ -121,6 +121,8 @@ int oracle_index_scores_fp8(int B, int T, int HI, int DI, int ratio, int act, co
         int b = bt / T;
         if (!check_query(seq_len[b], q_pos[bt]) || seq_len[b] / ratio > n_max) return ORACLE_EINVAL;
     }
+    double val[256]; /* code -> value, from the format definition above */
+    for (int c = 0; c < 256; ++c) val[c] = oracle_e4m3_value((uint8_t)c);
     for (int bt = 0; bt < B * T; ++bt) {
         const int b = bt / T;
         const int64_t L = seq_len[b], p = q_pos[bt];
@@ -136,8 +138,7 @@ int oracle_index_scores_fp8(int B, int T, int HI, int DI, int ratio, int act, co
                 const double qs = (double)q_scale[(int64_t)bt * HI + h];
                 double dot = 0.0;
                 for (int d = 0; d < DI; ++d)
-                    dot += oracle_e4m3_value(q8[((int64_t)bt * HI + h) * DI + d]) * qs *
-                           (oracle_e4m3_value(k8[b][j * DI + d]) * ks);
+                    dot += val[q8[((int64_t)bt * HI + h) * DI + d]] * qs * (val[k8[b][j * DI + d]] * ks);
                 double a = (act == ORACLE_ACT_RELU) ? (dot > 0.0 ? dot : 0.0) : dot;
                 s += (double)w[(int64_t)bt * HI + h] * a;
             }

@@ -171,3 +171,19 @@ def test_product_path_has_no_fallback(monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         _lib.load_library("/nonexistent/libcsa.so")
+
+
+def _scores_fp8(dims, q8=FAKE, qs=FAKE, w=FAKE, k8=FAKE, ks=FAKE, out=FAKE):
+    return csa.load_library().csa_index_scores_fp8(ctypes.byref(dims), q8, qs, w, k8, ks, FAKE, FAKE, out, None)
+
+
+def test_fp8_scorer_validation_before_any_launch():
+    """Shape, pointer and alignment errors come back before anything is enqueued."""
+    flash = csa.make_dims(batch=1, max_entries=16384)
+    assert _scores_fp8(_fixture()) == _lib.CSA_ERR_UNSUPPORTED          # index dims 4 x 16
+    assert _scores_fp8(flash, qs=None) == _lib.CSA_ERR_NULL
+    assert _scores_fp8(flash, ks=None) == _lib.CSA_ERR_NULL
+    assert _scores_fp8(flash, q8=MIS) == _lib.CSA_ERR_ALIGN
+    assert _scores_fp8(flash, k8=FAKE + 4) == _lib.CSA_ERR_ALIGN
+    bad_act = csa.make_dims(batch=1, max_entries=16384, index_act=7)
+    assert _scores_fp8(bad_act) == _lib.CSA_ERR_UNSUPPORTED

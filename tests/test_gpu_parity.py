@@ -373,3 +373,48 @@ def test_prefill_t2048_1m_sampled():
     rel = assert_attention_close(out[:, ts].cpu().numpy(), o_out, ATT_TOL_BF16, "out")
     np.testing.assert_allclose(lse[:, ts].cpu().numpy(), o_lse, atol=1e-3, rtol=0)
     say(f"  ok: sampled {len(ts)} queries, topk band swaps={n_diff} out err/rms={rel:.2e}")
+
+
+# --------------------------------------------------------------------------- fp8 (E4M3) index tensors
+
+def check_fp8_scores(case, act=csa.CSA_ACT_RELU, topk=True):
+    """csa_index_scores_fp8 against the oracle's fp8 definition (every score),
+    then the top-k of the GPU scores against the oracle's set (band rule)."""
+    wl = case.wl
+    say(f"[case] fp8 scores {wl.name} B={wl.batch} T={wl.q_len} max_entries={case.max_entries} act={act}")
+    q8, qs, k8, ks = inputs.make_fp8_index(case)
+    dev = "cuda"
+    k8_t = [torch.from_numpy(k).to(dev) for k in k8]
+    ks_t = [torch.from_numpy(x).to(dev) for x in ks]
+    seq_t = torch.from_numpy(case.seq_len).to(dev)
+    pos_t = torch.from_numpy(case.q_pos).to(dev)
+    dims = csa.make_dims(batch=wl.batch, q_len=wl.q_len, topk=wl.topk, window=wl.window, ratio=wl.ratio,
+                         max_entries=case.max_entries, index_act=act)
+    g = _np(csa.csa_index_scores_fp8(dims, torch.from_numpy(q8).to(dev), torch.from_numpy(qs).to(dev),
+                                     torch.from_numpy(case.w).to(dev), k8_t, ks_t, seq_t, pos_t))
+    o = oracle.index_scores_fp8(q8, qs, case.w, k8, ks, case.seq_len, case.q_pos, ratio=wl.ratio,
+                                n_max=case.max_entries, act=oracle.ACT_NONE if act == csa.CSA_ACT_NONE else oracle.ACT_RELU)
+    assert_scores_close(g, o, case)
+    if topk:
+        o_idx = oracle.topk(o, case.seq_len, case.q_pos, ratio=wl.ratio, k=wl.topk)
+        g_idx = _np(csa.csa_topk_select(dims, torch.from_numpy(g).to(dev), seq_t, pos_t))
+        n_diff = assert_topk_band(g_idx, o_idx, o, case)
+        say(f"  ok: fp8 scores, topk band swaps={n_diff}")
+
+
+@pytest.mark.parametrize("lens", [
+    [4 * 3000 + 2, 4 * 500 + 1, 4 * 64 * 7],   # ragged tails, several wave-steps
+    [50, 4 * 700 + 3],                         # nothing compressed visible in one sequence
+])
+def test_fp8_scores_small(lens):
+    wl, sl = flash_case(f"fp8_small_{len(lens)}_{lens[0]}", lens)
+    check_fp8_scores(make_case_with_lens(wl, sl))
+
+
+def test_fp8_scores_no_activation_and_many_queries():
+    wl, sl = flash_case("fp8_noact_prefill", [4 * 1500 + 3], q_len=20, q_pos0=4 * 1500 + 3 - 25)
+    check_fp8_scores(make_case_with_lens(wl, sl), act=csa.CSA_ACT_NONE, topk=False)
+
+
+def test_fp8_scores_decode_b4_1m_full():
+    check_fp8_scores(inputs.make_case(inputs.WORKLOADS["decode_b4_1m"], with_hca=False))
