@@ -30,7 +30,8 @@ METRIC = "CSA decode queries/s at 64K–1M ctx; achieved HBM GB/s vs peak (1 GPU
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # dense bf16 MFMA, MI355X datasheet
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_index_scores_decode_b4_1m.json")
-SCORER_SRC = os.path.join(ROOT, "compressed_sparse_attention_indexer_amd", "csrc", "scorer.hip")
+SCORER_SRC = [os.path.join(ROOT, "compressed_sparse_attention_indexer_amd", "csrc", f)
+              for f in ("scorer.hip", "scorer_common.hpp")]
 
 
 def parse():
@@ -49,8 +50,11 @@ def parse():
     return p.parse_args()
 
 
-def sha_of(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def sha_of(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
 
 
 # ------------------------------------------------------------------ algorithmic bytes (per call)
