@@ -370,7 +370,7 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.quick:
-        for name in ("decode_b1_64k", "decode_b32_ragged_64k_128k"):
+        for name in ("decode_b1_64k", "decode_b32_ragged_64k_128k", "pro_decode_b4_1m"):
             if name == wl.name:
                 continue
             c2 = inputs.make_case(inputs.WORKLOADS[name])

@@ -79,9 +79,9 @@ csa_status check_attn(const csa_dims *d) {
     if (d->window < 1) return fail(CSA_ERR_DIM, "window must be >= 1");
     if (!(d->softmax_scale >= 0.f) || !std::isfinite(d->softmax_scale))
         return fail(CSA_ERR_DIM, "softmax_scale must be finite and >= 0");
-    if (d->dtype == CSA_BF16 && (d->n_heads != 64 || d->head_dim != 512))
-        return fail(CSA_ERR_UNSUPPORTED, "bf16 attention needs n_heads 64 and head_dim 512 (got %d, %d)", d->n_heads,
-                    d->head_dim);
+    if (d->dtype == CSA_BF16 && ((d->n_heads != 64 && d->n_heads != 128) || d->head_dim != 512))
+        return fail(CSA_ERR_UNSUPPORTED, "bf16 attention needs n_heads 64 or 128 and head_dim 512 (got %d, %d)",
+                    d->n_heads, d->head_dim);
     if (d->dtype == CSA_F32 && (d->n_heads > 128 || d->head_dim > 512))
         return fail(CSA_ERR_UNSUPPORTED, "fp32 attention supports n_heads <= 128, head_dim <= 512");
     if (d->dtype == CSA_BF16 && (long long)d->max_entries + d->window > (1ll << 28))

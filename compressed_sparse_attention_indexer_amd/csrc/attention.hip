@@ -122,7 +122,8 @@ __global__ __launch_bounds__(256) void mqa_f32_kernel(MqaArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 split-K MFMA kernel, D = 512, H = 16 * HG heads.
+// bf16 split-K MFMA kernel, D = 512, 16 * HG heads per workgroup (HG = 4: 64
+// heads; 128 heads take two workgroups, blockIdx.z picking the half).
 //
 // Workgroup = one (query, split): 2*HG waves; wave (hg, dh) owns heads
 // [16hg, 16hg+16) and output dims [256dh, 256dh+256).  Rows stream through
@@ -169,6 +170,7 @@ __global__ __launch_bounds__(128 * HG) void mqa_bf16_kernel(MqaArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int e = lane & 15, g = lane >> 4;
     const int hg = wave >> 1, dh = wave & 1;
+    const int h_off = 64 * blockIdx.z;  // this workgroup's 64 heads: h_off .. h_off + 63
     const RowList rl = make_rows(a, qi);
     const int r0 = split * a.rows_per_split;
     const int r1 = r0 + a.rows_per_split < rl.n_rows ? r0 + a.rows_per_split : rl.n_rows;
@@ -178,7 +180,7 @@ __global__ __launch_bounds__(128 * HG) void mqa_bf16_kernel(MqaArgs a) {
     // B fragments of Q^T: head 16hg + e, dims 256dh + 32ks + 8g .. +8.
     bf16x8_t qf[8];
     {
-        const uint16_t *qrow = (const uint16_t *)a.q + ((size_t)qi * a.H + 16 * hg + e) * kD + 256 * dh + 8 * g;
+        const uint16_t *qrow = (const uint16_t *)a.q + ((size_t)qi * a.H + h_off + 16 * hg + e) * kD + 256 * dh + 8 * g;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8_t *)(qrow + 32 * ks);
     }
@@ -290,9 +292,9 @@ __global__ __launch_bounds__(128 * HG) void mqa_bf16_kernel(MqaArgs a) {
     }
 
     // epilogue: C layout holds O[head 16hg + 4g + r][d = 256dh + 16dt + e]
-    const int hbase = 16 * hg + 4 * g;
+    const int hbase = h_off + 16 * hg + 4 * g;
     if (a.n_splits == 1) {
-        const float sink2 = a.sink[16 * hg + e] * kLog2e;
+        const float sink2 = a.sink[h_off + 16 * hg + e] * kLog2e;
         const float M = fmaxf(m_run, sink2);
         const float lf = l_run * exp2f(m_run - M) + exp2f(sink2 - M);
         const float f = exp2f(m_run - M) / lf;
@@ -304,7 +306,7 @@ __global__ __launch_bounds__(128 * HG) void mqa_bf16_kernel(MqaArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 a.out[((size_t)qi * a.H + hbase + r) * kD + 256 * dh + 16 * dt + e] = o[dt][r] * fr[r];
-        if (a.lse && dh == 0 && g == 0) a.lse[(size_t)qi * a.H + 16 * hg + e] = M * kLn2 + logf(lf);
+        if (a.lse && dh == 0 && g == 0) a.lse[(size_t)qi * a.H + h_off + 16 * hg + e] = M * kLn2 + logf(lf);
     } else {
         // Partial of this split: (m, l) per head, and O / l in fp16 stored the
         // way the MFMA tiles lie in registers: the 16-byte vector at
@@ -312,15 +314,15 @@ __global__ __launch_bounds__(128 * HG) void mqa_bf16_kernel(MqaArgs a) {
         // (r = 0..3) at dims 256dh + 16dt + e for dt = 2p and 2p + 1.
         const size_t ps = (size_t)qi * a.n_splits + split;
         if (dh == 0 && g == 0) {
-            a.part_ml[(ps * a.H + 16 * hg + e) * 2 + 0] = m_run;
-            a.part_ml[(ps * a.H + 16 * hg + e) * 2 + 1] = l_run;
+            a.part_ml[(ps * a.H + h_off + 16 * hg + e) * 2 + 0] = m_run;
+            a.part_ml[(ps * a.H + h_off + 16 * hg + e) * 2 + 1] = l_run;
         }
         if (ntiles > 0) {
             const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
             float ir[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) ir[r] = __shfl(inv, 4 * g + r);
-            u32x4_t *dst = (u32x4_t *)a.part_o + (ps * 8 + wave) * 8 * 64 + lane;
+            u32x4_t *dst = (u32x4_t *)a.part_o + ((ps * gridDim.z + blockIdx.z) * NW + wave) * 8 * 64 + lane;
 #pragma unroll
             for (int p = 0; p < 8; ++p) {
                 uint32_t w4[4];
@@ -338,8 +340,8 @@ __global__ __launch_bounds__(128 * HG) void mqa_bf16_kernel(MqaArgs a) {
     }
 }
 
-// Merge split partials with the sink, counted once.  Workgroup = (16-head
-// group hg, lane group g, query): each of its 256 threads (dh, dt pair p,
+// Merge split partials with the sink, counted once (H = 64 or 128).
+// Workgroup = (16-head group hg, lane group g, query): each of its 256 threads (dh, dt pair p,
 // column e) holds heads 16hg + 4g + r (r = 0..3) at two dims of every
 // split's partial, one 16-byte vector per split.  Wave r first turns head
 // h0 + r's (m, l) pairs into per-split weights and the total (lanes over the
@@ -357,11 +359,13 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(MqaArgs a) {
     const int hg = blockIdx.x >> 2, g = blockIdx.x & 3;
     const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
     const int dh = tid >> 7, p = (tid >> 4) & 7, e = tid & 15;
-    const int lane = 16 * g + e, wave = 2 * hg + dh;
+    const int lane = 16 * g + e;
     const int h0 = 16 * hg + 4 * g;
     const int S = a.n_splits;
-    const u32x4_t *src = (const u32x4_t *)a.part_o + (((size_t)qi * S * 8 + wave) * 8 + p) * 64 + lane;
-    const size_t sstride = 8 * 8 * 64;  // vectors per split
+    // partial vectors: [qi, split, head half z, wave (2 * (hg % 4) + dh), dt pair, lane]
+    const int Z = a.H / 64, z = hg >> 2, wave_l = 2 * (hg & 3) + dh;
+    const u32x4_t *src = (const u32x4_t *)a.part_o + ((((size_t)qi * S * Z + z) * 8 + wave_l) * 8 + p) * 64 + lane;
+    const size_t sstride = (size_t)Z * 8 * 8 * 64;  // vectors per split
     u32x4_t ov[2][kBatch];
     auto load_batch = [&](u32x4_t (&v)[kBatch], int s0) {
 #pragma unroll
@@ -476,8 +480,8 @@ hipError_t launch_mqa(const MqaArgs &a, int dtype, hipStream_t stream) {
         hipLaunchKernelGGL(mqa_f32_kernel, dim3(a.H, Q), dim3(256), lds, stream, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(mqa_bf16_kernel<4>, dim3(a.n_splits, Q), dim3(512), 0, stream, a);
-    if (a.n_splits > 1) hipLaunchKernelGGL(mqa_combine_kernel, dim3(16, Q), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(mqa_bf16_kernel<4>, dim3(a.n_splits, Q, a.H / 64), dim3(512), 0, stream, a);
+    if (a.n_splits > 1) hipLaunchKernelGGL(mqa_combine_kernel, dim3(a.H / 4, Q), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

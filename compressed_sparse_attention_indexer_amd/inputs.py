@@ -81,6 +81,10 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("prefill_t2048_1m", 4, batch=1, q_len=2048, n_heads=64, head_dim=512,
                  index_heads=64, index_dim=128, topk=512, window=128, ratio=4, dtype="bf16",
                  seq_len=1048576, q_pos0=1046528),
+        # V4-Pro attention shape (128 query heads, top-1024) on the million-token batch
+        Workload("pro_decode_b4_1m", 5, batch=4, q_len=1, n_heads=128, head_dim=512,
+                 index_heads=64, index_dim=128, topk=1024, window=128, ratio=4, dtype="bf16",
+                 seq_len=1048576),
     ]
 }
 

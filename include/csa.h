@@ -107,7 +107,8 @@ typedef struct csa_dims {
 
 /*
  * Supported shapes.
- *   CSA_BF16: head_dim 512, index_dim 128, index_heads 64, n_heads 64.
+ *   CSA_BF16: head_dim 512, index_dim 128, index_heads 64, n_heads 64 (Flash)
+ *             or 128 (Pro: [A] ARCHITECTURE_SPEC, DeepSeek-V4-Pro num_heads).
  *   CSA_F32:  head_dim <= 512, index_dim <= 128, index_heads <= 64,
  *             n_heads <= 128 (plain VALU kernels for small fixtures).
  * Limits for both: 1 <= topk <= 2048, window >= 1, ratio >= 1,

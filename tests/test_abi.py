@@ -121,7 +121,7 @@ def test_unsupported_shapes():
     assert _scores(_flash(index_dim=64)) == _lib.CSA_ERR_UNSUPPORTED
     assert _scores(_flash(dtype=7)) == _lib.CSA_ERR_UNSUPPORTED
     assert _scores(_flash(index_act=5)) == _lib.CSA_ERR_UNSUPPORTED
-    assert _sparse(_flash(n_heads=128)) == _lib.CSA_ERR_UNSUPPORTED
+    assert _sparse(_flash(n_heads=96)) == _lib.CSA_ERR_UNSUPPORTED  # bf16 attention: 64 or 128 heads
     assert _sparse(_flash(head_dim=256)) == _lib.CSA_ERR_UNSUPPORTED
     assert _sparse(_fixture(head_dim=1024)) == _lib.CSA_ERR_UNSUPPORTED
     assert _scores(_fixture(index_dim=256)) == _lib.CSA_ERR_UNSUPPORTED

@@ -418,3 +418,22 @@ def test_fp8_scores_no_activation_and_many_queries():
 
 def test_fp8_scores_decode_b4_1m_full():
     check_fp8_scores(inputs.make_case(inputs.WORKLOADS["decode_b4_1m"], with_hca=False))
+
+
+# --------------------------------------------------------------------------- V4-Pro shapes (128 heads, top-1024)
+
+def _pro_case(name, lens, index=111):
+    base = inputs.WORKLOADS["pro_decode_b4_1m"]
+    wl = inputs.scaled(base, name, index=index, batch=len(lens), seq_len=None, seq_len_range=None)
+    return inputs.make_case(wl, seq_lens=np.array(lens, np.int32))
+
+
+@pytest.mark.parametrize("lens", [
+    [4 * 6000 + 3, 4 * 900 + 1, 4 * 200],   # n_vis above and below K = 1024, ragged
+])
+def test_pro_shapes_whole_step_small(lens):
+    check_whole_step(_pro_case(f"pro_small_{lens[0]}", lens), ATT_TOL_BF16)
+
+
+def test_pro_decode_b4_1m_full():
+    check_whole_step(inputs.make_case(inputs.WORKLOADS["pro_decode_b4_1m"]), ATT_TOL_BF16)
