@@ -252,8 +252,8 @@ __global__ __launch_bounds__(128 * HG) void mqa_bf16_kernel(MqaArgs a) {
         float mx = z[0];
 #pragma unroll
         for (int v = 1; v < 8; ++v) mx = fmaxf(mx, z[v]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = max_xor16(mx);
+        mx = max_xor32(mx);
         const float m_new = fmaxf(m_run, mx);
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
         const float alpha = exp2f(m_run - m_use);
@@ -263,8 +263,8 @@ __global__ __launch_bounds__(128 * HG) void mqa_bf16_kernel(MqaArgs a) {
             pv[v] = exp2f(z[v] - m_use);
             ls += pv[v];
         }
-        ls += __shfl_xor(ls, 16);
-        ls += __shfl_xor(ls, 32);
+        ls = sum_xor16(ls);
+        ls = sum_xor32(ls);
         l_run = l_run * alpha + ls;
         m_run = m_new;
         if (__any(alpha != 1.f)) {

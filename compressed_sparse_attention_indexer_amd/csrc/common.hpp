@@ -48,6 +48,43 @@ __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 __device__ __forceinline__ uint64_t lanemask_lt() { return (1ull << lane_id()) - 1ull; }
 
+// Cross-lane combines through the gfx950 lane swaps (VALU, no LDS round trip).
+// swap16(a, b): lanes with bit 4 clear get (a of this lane, a of lane ^ 16)...
+// precisely, per 32-lane half, v_permlane16_swap exchanges lanes 16..31 of its
+// first operand with lanes 0..15 of its second, v_permlane32_swap lanes 32..63
+// of the first with lanes 0..31 of the second.  pair16(a, b) returns, in every
+// lane l, {x(l & ~16), x(l | 16)} where x is a for lanes with bit 4 clear and
+// b for lanes with it set; pair32 the same over bit 5.  With a = b = v this is
+// the pair {v(l & ~16), v(l | 16)}, the same ordered pair in both lanes.
+struct LanePair {
+    float lo, hi;
+};
+__device__ __forceinline__ LanePair pair16(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return LanePair{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ LanePair pair32(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return LanePair{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+// v(l) + v(l ^ 16) and v(l) + v(l ^ 32), bit-identical in both lanes of a pair
+__device__ __forceinline__ float sum_xor16(float v) {
+    const LanePair p = pair16(v, v);
+    return p.lo + p.hi;
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+    const LanePair p = pair32(v, v);
+    return p.lo + p.hi;
+}
+__device__ __forceinline__ float max_xor16(float v) {
+    const LanePair p = pair16(v, v);
+    return fmaxf(p.lo, p.hi);
+}
+__device__ __forceinline__ float max_xor32(float v) {
+    const LanePair p = pair32(v, v);
+    return fmaxf(p.lo, p.hi);
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));

@@ -170,8 +170,8 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(
                 for (int r = 0; r < 4; ++r) {
                     p = fmaf(wr[ht][r], index_act<kAct>(acc[ht][r]), p);
                 }
-            p += __shfl_xor(p, 16);
-            p += __shfl_xor(p, 32);
+            p = sum_xor16(p);
+            p = sum_xor32(p);
             part[et] = p;
         }
         // Lanes of group g < 2 store column tile g: 32 consecutive scores.
@@ -375,19 +375,17 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void index_scores_tiled_kernel(Sc
                 }
             }
             // butterfly over the lane groups: lane 16g + e ends with entry 16g + e summed over all heads
-            const int hi = g >> 1, lo = g & 1;
             const int j = j0 + tile * kPfTile + 64 * grp + lane;
 #pragma unroll
             for (int q = 0; q < kPfQW; ++q) {
                 float k2[2];
 #pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    const float send = hi ? p[q][k] : p[q][2 + k];
-                    const float mine = hi ? p[q][2 + k] : p[q][k];
-                    k2[k] = mine + __shfl_xor(send, 32);
+                for (int k = 0; k < 2; ++k) {  // lower half keeps p[k], upper half p[2 + k]
+                    const LanePair pr = pair32(p[q][k], p[q][2 + k]);
+                    k2[k] = pr.lo + pr.hi;
                 }
-                const float send = lo ? k2[0] : k2[1];
-                const float tot = (lo ? k2[1] : k2[0]) + __shfl_xor(send, 16);
+                const LanePair pr = pair16(k2[0], k2[1]);  // lane group lo keeps k2[lo]
+                const float tot = pr.lo + pr.hi;
                 if (qok[q] && j < a.n_max) a.scores[(size_t)qi[q] * a.n_max + j] = j < nv[q] ? tot : -INFINITY;
             }
         }

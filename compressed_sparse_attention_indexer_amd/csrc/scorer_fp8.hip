@@ -103,8 +103,8 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_fp8_kernel(S
             for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) p = fmaf(wr[ht][r], index_act<kAct>(acc[ht][r]), p);
-            p += __shfl_xor(p, 16);
-            p += __shfl_xor(p, 32);
+            p = sum_xor16(p);
+            p = sum_xor32(p);
             if (g == et) mine = p;  // lane group g keeps column tile g
         }
         if (live && j < a.n_max) srow[j] = j < nvis ? ks * mine : -INFINITY;
