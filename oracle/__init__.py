@@ -28,7 +28,8 @@ def build() -> str:
     """Compile liboracle.so with gcc (OpenMP)."""
     tmp = _SO + ".tmp"
     subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fopenmp", "-fPIC",
-                           "-shared", os.path.join(_HERE, "oracle.c"), "-o", tmp, "-lm"])
+                           "-shared", os.path.join(_HERE, "oracle.c"), os.path.join(_HERE, "compressor.c"), "-o", tmp,
+                           "-lm"])
     os.replace(tmp, _SO)
     return _SO
 
@@ -48,13 +49,14 @@ def lib():
         L.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
         L.oracle_e4m3_value.restype = D
         L.oracle_index_scores_fp8.argtypes = [I] * 6 + [P] * 7 + [I, P]
+        L.oracle_compress.argtypes = [I] * 6 + [D, D, I, P, I, P, P, P, P, I, I, P]
         L.oracle_attend_rows.argtypes = [I, I, I, D, P, P, P, I, P, P, P]
         L.oracle_partial_rows.argtypes = [I, I, I, D, P, P, P, I, P, P, P]
         L.oracle_merge_partials.argtypes = [I, I, I, P, P, P, P, P, P]
         L.oracle_sparse_mqa.argtypes = [I] * 8 + [D] + [P] * 13
         L.oracle_hca_mqa.argtypes = [I] * 7 + [D] + [P] * 12
         L.oracle_csa_attention.argtypes = [I] * 11 + [D] + [P] * 13 + [I] + [P] * 4
-        for f in ("oracle_index_scores", "oracle_index_scores_fp8", "oracle_topk", "oracle_attend_rows", "oracle_partial_rows",
+        for f in ("oracle_index_scores", "oracle_index_scores_fp8", "oracle_compress", "oracle_topk", "oracle_attend_rows", "oracle_partial_rows",
                   "oracle_merge_partials", "oracle_sparse_mqa", "oracle_hca_mqa",
                   "oracle_csa_attention"):
             getattr(L, f).restype = I
@@ -135,6 +137,21 @@ def index_scores_fp8(q8, q_scale, w, k8: List[np.ndarray], k_scale: List[np.ndar
     out = np.empty((B, T, n_max), dtype=np.float32)
     _check(lib().oracle_index_scores_fp8(B, T, HI, DI, ratio, act, _p(qa), _p(qs), _p(wa), kp, sp, _p(sl), _p(qp),
                                          n_max, _p(out)), "oracle_index_scores_fp8")
+    return out
+
+
+def compress(x, wkv, wgate, ape, gamma, *, pos0: int, ratio: int, window: int, first_entry: int, n_entries: int,
+             rope_dims: int = 0, rope_theta: float = 160000.0, eps: float = 1e-6, hadamard: bool = False) -> np.ndarray:
+    """x [tokens, hidden] bf16 bits; wkv/wgate [out_dim, hidden] bf16 bits; ape [window, out_dim];
+    gamma [out_dim].  Returns [n_entries, out_dim] float64."""
+    tokens, hidden = x.shape
+    out_dim = wkv.shape[0]
+    xa, wk, wg = (np.ascontiguousarray(a, np.uint16) for a in (x, wkv, wgate))
+    ap, gm = np.ascontiguousarray(ape, np.float32), np.ascontiguousarray(gamma, np.float32)
+    out = np.empty((n_entries, out_dim), np.float64)
+    _check(lib().oracle_compress(tokens, hidden, out_dim, ratio, window, rope_dims, rope_theta, eps, int(hadamard),
+                                 _p(xa), pos0, _p(wk), _p(wg), _p(ap), _p(gm), first_entry, n_entries, _p(out)),
+           "oracle_compress")
     return out
 
 

@@ -18,6 +18,8 @@
  *       one 512-d row serves as key and value.
  *   [C] "DeepSeek-V4-Flash-0731" (mic coverage page), config table:
  *       quantization_config (fp8, e4m3 format, dynamic activation scheme).
+ *   [D] "DeepSeek-V4-Flash" (llm-atlas), raw config.json table (as [B]):
+ *       compress_rope_theta, rms_norm_eps, qk_rope_head_dim.
  *   [B] "DeepSeek-V4-Flash" (llm-atlas), raw config.json table: index_n_heads,
  *       index_head_dim, index_topk, sliding_window, head_dim, 64 q-heads / 1
  *       kv-head.
@@ -130,6 +132,35 @@ int oracle_csa_attention(int B, int T, int H, int D, int HI, int DI, int K, int 
                          const int32_t *win_pos0, const int32_t *win_rows, const int32_t *seq_len,
                          const int32_t *q_pos, const float *sink, int n_max, float *scores,
                          int32_t *idx, double *out, double *lse);
+
+/* KV / index-key compressor (the step before the path: NEXT-2, NEXT-4), [A]
+ * sec. 1: gated pooling of the tokens of a compression window with a learned
+ * projection (wkv), gating (wgate), absolute position embeddings within the
+ * window (ape), RMSNorm on the output and RoPE on the rope dims; 4:1 with
+ * overlapping windows (CSA), 128:1 (HCA); the indexer's own compressor adds a
+ * Hadamard rotation.  [D] "DeepSeek-V4-Flash" (llm-atlas) config table:
+ * compress_rope_theta 160000, rms_norm_eps 1e-6, qk_rope_head_dim 64.
+ * Readings (the pages give the ingredients, not the formula):
+ *   R8  entry e of ratio r pools raw tokens [r*e + r - window, r*e + r - 1]
+ *       (window = 2r overlapping for CSA, r for HCA); tokens before position
+ *       0 do not exist and are left out;
+ *   R9  per token t at slot i of the window: kv_t = wkv x_t, gate_t = wgate
+ *       x_t + ape[i] (vectors of out_dim); per output dim a softmax over the
+ *       window's tokens of gate_t weights the kv_t;
+ *   R10 RMSNorm: c / sqrt(mean(c^2) + eps) * gamma;
+ *   R11 RoPE on the trailing rope_dims dims: pair (2k, 2k+1) of that slice
+ *       rotated by (r*e) * theta^(-2k/rope_dims), position r*e being the
+ *       entry's first raw token;
+ *   R12 optional normalized Hadamard rotation (Sylvester order out_dim)
+ *       applied last.
+ * x [tokens, hidden] bf16 with token 0 at raw position pos0; wkv, wgate
+ * [out_dim, hidden] bf16; ape [window, out_dim]; gamma [out_dim].  out
+ * [n_entries, out_dim] float64 for entries first_entry.. (ORACLE_EWINDOW if a
+ * window token is not supplied). */
+int oracle_compress(int tokens, int hidden, int out_dim, int ratio, int window, int rope_dims,
+                    double rope_theta, double eps, int hadamard, const uint16_t *x, int pos0,
+                    const uint16_t *wkv, const uint16_t *wgate, const float *ape, const float *gamma,
+                    int first_entry, int n_entries, double *out);
 
 #ifdef __cplusplus
 }

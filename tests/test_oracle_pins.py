@@ -541,3 +541,101 @@ def test_fp8_row_scales_act_per_entry_and_per_head():
     a = oracle.index_scores_fp8(q8, qs3, w, k8, ks, seq, seq - 1, ratio=4, n_max=11)
     b = oracle.index_scores_fp8(q8, qs, w3, k8, ks, seq, seq - 1, ratio=4, n_max=11)
     np.testing.assert_allclose(a, b, rtol=1e-6)
+
+
+# --------------------------------------------------------------------------- compressor (R8-R12)
+
+def _comp_inputs(seed, tokens=24, hidden=32, out_dim=16, window=8):
+    r = np.random.default_rng(seed)
+    x = inputs.bf16_bits(r.standard_normal((tokens, hidden)).astype(np.float32) * 0.5)
+    wkv = inputs.bf16_bits(r.standard_normal((out_dim, hidden)).astype(np.float32) * 0.2)
+    wg = inputs.bf16_bits(r.standard_normal((out_dim, hidden)).astype(np.float32) * 0.2)
+    ape = r.standard_normal((window, out_dim)).astype(np.float32)
+    gamma = r.uniform(0.5, 1.5, out_dim).astype(np.float32)
+    return x, wkv, wg, ape, gamma
+
+
+def _f64(b):
+    return inputs.bf16_to_f32(b).astype(np.float64)
+
+
+def _rms_norm(c, gamma, eps=1e-6):
+    return c / np.sqrt(np.mean(c ** 2) + eps) * gamma
+
+
+def test_compress_uniform_gates_is_mean_pooling():
+    """Zero gate weights and embeddings make the softmax uniform: an entry is
+    RMSNorm(wkv . mean of its window's tokens), a matrix-vector product."""
+    x, wkv, _, _, gamma = _comp_inputs(1)
+    out = oracle.compress(x, wkv, np.zeros_like(wkv), np.zeros((8, 16), np.float32), gamma, pos0=0, ratio=4,
+                          window=8, first_entry=1, n_entries=4)
+    for i, e in enumerate(range(1, 5)):
+        want = _rms_norm(_f64(wkv) @ _f64(x)[4 * e - 4:4 * e + 4].mean(0), gamma)
+        np.testing.assert_allclose(out[i], want, rtol=1e-12, atol=1e-12)
+
+
+def test_compress_first_entry_has_no_tokens_before_zero():
+    """Entry 0 of an overlapping 2r window only has tokens 0..r-1."""
+    x, wkv, _, _, gamma = _comp_inputs(2)
+    out = oracle.compress(x, wkv, np.zeros_like(wkv), np.zeros((8, 16), np.float32), gamma, pos0=0, ratio=4,
+                          window=8, first_entry=0, n_entries=1)
+    np.testing.assert_allclose(out[0], _rms_norm(_f64(wkv) @ _f64(x)[0:4].mean(0), gamma), rtol=1e-12)
+
+
+def test_compress_dominant_slot_selects_one_token():
+    """A huge position embedding at slot 5 of the window puts all the weight on that token."""
+    x, wkv, wg, _, gamma = _comp_inputs(3)
+    ape = np.zeros((8, 16), np.float32)
+    ape[5] = 1e4
+    out = oracle.compress(x, wkv, wg, ape, gamma, pos0=0, ratio=4, window=8, first_entry=2, n_entries=2)
+    for i, e in enumerate((2, 3)):
+        t = 4 * e + 4 - 8 + 5
+        np.testing.assert_allclose(out[i], _rms_norm(_f64(wkv) @ _f64(x)[t], gamma), rtol=1e-9)
+
+
+def test_compress_hca_window_is_the_span_itself():
+    """Without overlap (window = ratio) an entry pools exactly its own r tokens."""
+    x, wkv, _, _, gamma = _comp_inputs(4, tokens=32)
+    out = oracle.compress(x, wkv, np.zeros_like(wkv), np.zeros((8, 16), np.float32), gamma, pos0=0, ratio=8,
+                          window=8, first_entry=2, n_entries=1)
+    np.testing.assert_allclose(out[0], _rms_norm(_f64(wkv) @ _f64(x)[16:24].mean(0), gamma), rtol=1e-12)
+
+
+def test_compress_rope_rotates_pairs_by_position():
+    """Identical tokens give every entry the same pre-RoPE vector; the rope
+    slice of entry e is that vector's pairs rotated by (r e) theta^(-2k/R),
+    the other dims untouched."""
+    x, wkv, wg, ape, gamma = _comp_inputs(5)
+    x[:] = x[0]
+    base = oracle.compress(x, wkv, wg, ape, gamma, pos0=0, ratio=4, window=8, first_entry=2, n_entries=3)
+    rot = oracle.compress(x, wkv, wg, ape, gamma, pos0=0, ratio=4, window=8, first_entry=2, n_entries=3,
+                          rope_dims=8, rope_theta=160000.0)
+    np.testing.assert_array_equal(rot[:, :8], base[:, :8])
+    for i, e in enumerate((2, 3, 4)):
+        for k in range(4):
+            ang = 4 * e * 160000.0 ** (-2.0 * k / 8)
+            a, b = base[i, 8 + 2 * k], base[i, 9 + 2 * k]
+            np.testing.assert_allclose(rot[i, 8 + 2 * k], a * math.cos(ang) - b * math.sin(ang), rtol=1e-12, atol=1e-15)
+            np.testing.assert_allclose(rot[i, 9 + 2 * k], a * math.sin(ang) + b * math.cos(ang), rtol=1e-12, atol=1e-15)
+
+
+def test_compress_output_has_unit_rms_with_unit_gamma():
+    x, wkv, wg, ape, _ = _comp_inputs(6)
+    out = oracle.compress(x, wkv, wg, ape, np.ones(16, np.float32), pos0=0, ratio=4, window=8, first_entry=1,
+                          n_entries=4, rope_dims=8)
+    np.testing.assert_allclose(np.sqrt(np.mean(out ** 2, axis=1)), 1.0, atol=1e-4)
+
+
+def test_compress_hadamard_is_the_normalized_sylvester_matrix():
+    from scipy.linalg import hadamard
+    x, wkv, wg, ape, gamma = _comp_inputs(7)
+    plain = oracle.compress(x, wkv, wg, ape, gamma, pos0=0, ratio=4, window=8, first_entry=1, n_entries=3)
+    rot = oracle.compress(x, wkv, wg, ape, gamma, pos0=0, ratio=4, window=8, first_entry=1, n_entries=3,
+                          hadamard=True)
+    np.testing.assert_allclose(rot, plain @ (hadamard(16) / 4.0).T, rtol=1e-12, atol=1e-14)
+
+
+def test_compress_rejects_windows_not_supplied():
+    x, wkv, wg, ape, gamma = _comp_inputs(8)
+    with pytest.raises(RuntimeError):
+        oracle.compress(x, wkv, wg, ape, gamma, pos0=4, ratio=4, window=8, first_entry=0, n_entries=1)
