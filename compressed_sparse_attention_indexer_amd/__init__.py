@@ -13,11 +13,12 @@ import math
 from typing import List, Optional, Sequence, Union
 
 from ._lib import (CSA_ACT_NONE, CSA_ACT_RELU, CSA_BF16, CSA_F32, CSA_OP_ATTENTION, CSA_OP_HCA_MQA,
-                   CSA_OP_INDEX_SCORES, CSA_OP_SPARSE_MQA, CSA_OP_TOPK, EXPORTS, CsaDims, CsaError, check,
-                   load_library)
+                   CSA_OP_INDEX_SCORES, CSA_OP_SPARSE_MQA, CSA_OP_TOPK, EXPORTS, CsaCompressDims, CsaDims,
+                   CsaError, check, load_library)
 
 __all__ = ["CsaDims", "CsaError", "make_dims", "workspace_size", "ptr_array", "csa_index_scores",
-           "csa_index_scores_fp8",
+           "csa_index_scores_fp8", "CsaCompressDims", "make_compress_dims", "compress_workspace_size",
+           "csa_compress",
            "csa_topk_select", "csa_sparse_mqa_decode", "hca_mqa_decode", "csa_attention", "load_library",
            "CSA_F32", "CSA_BF16", "CSA_ACT_RELU", "CSA_ACT_NONE"]
 
@@ -173,3 +174,31 @@ def csa_attention(dims: CsaDims, q, q_idx, w, k_idx: PtrArg, kv: PtrArg, v: PtrA
         _p(seq_len), _p(q_pos), _p(sink), _p(out), _p(lse), _p(topk_idx_out), _p(scores_out), _p(ws), nws,
         _stream(stream)), "csa_attention")
     return out, lse
+
+
+def make_compress_dims(*, tokens: int, hidden: int, out_dim: int, ratio: int, window: int, first_entry: int,
+                       n_entries: int, pos0: int, rope_dims: int = 0, hadamard: bool = False,
+                       rope_theta: float = 160000.0, rms_eps: float = 1e-6) -> CsaCompressDims:
+    return CsaCompressDims(tokens, hidden, out_dim, ratio, window, rope_dims, int(hadamard), first_entry, n_entries,
+                           pos0, rope_theta, rms_eps)
+
+
+def compress_workspace_size(dims: CsaCompressDims) -> int:
+    n = ctypes.c_size_t(0)
+    check(load_library().csa_compress_workspace_size(ctypes.byref(dims), ctypes.byref(n)),
+          "csa_compress_workspace_size")
+    return int(n.value)
+
+
+def csa_compress(dims: CsaCompressDims, x, wkv, wgate, ape, gamma, out=None, workspace=None, stream=None):
+    """Compressed entries [n_entries, out_dim] bf16 (see csa.h)."""
+    torch = _torch()
+    dev = x.device
+    if out is None:
+        out = torch.empty((dims.n_entries, dims.out_dim), dtype=torch.bfloat16, device=dev)
+    n = compress_workspace_size(dims)
+    if workspace is None:
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+    check(load_library().csa_compress(ctypes.byref(dims), _p(x), _p(wkv), _p(wgate), _p(ape), _p(gamma), _p(out),
+                                      _p(workspace), workspace.numel(), _stream(stream)), "csa_compress")
+    return out

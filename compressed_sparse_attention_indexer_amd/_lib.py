@@ -17,8 +17,8 @@ CSA_OP_INDEX_SCORES, CSA_OP_TOPK, CSA_OP_SPARSE_MQA, CSA_OP_HCA_MQA, CSA_OP_ATTE
 
 # every symbol include/csa.h declares
 EXPORTS = ("csa_workspace_size", "csa_index_scores", "csa_index_scores_fp8", "csa_topk_select",
-           "csa_sparse_mqa_decode", "hca_mqa_decode", "csa_attention", "csa_status_string", "csa_last_error",
-           "csa_abi_version")
+           "csa_sparse_mqa_decode", "hca_mqa_decode", "csa_attention", "csa_compress_workspace_size", "csa_compress",
+           "csa_status_string", "csa_last_error", "csa_abi_version")
 
 
 class CsaDims(ctypes.Structure):
@@ -27,6 +27,12 @@ class CsaDims(ctypes.Structure):
                 ("topk", ctypes.c_int32), ("window", ctypes.c_int32), ("ratio", ctypes.c_int32),
                 ("max_entries", ctypes.c_int32), ("dtype", ctypes.c_int32), ("index_act", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float)]
+
+
+class CsaCompressDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("tokens", "hidden", "out_dim", "ratio", "window", "rope_dims",
+                                               "hadamard", "first_entry", "n_entries", "pos0")] + \
+               [("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float)]
 
 
 class CsaError(RuntimeError):
@@ -60,9 +66,12 @@ def load_library(path: str = LIB_PATH):
     L.csa_sparse_mqa_decode.argtypes = [DP] + [P] * 13 + [P, SZ, P]
     L.hca_mqa_decode.argtypes = [DP] + [P] * 12 + [P, SZ, P]
     L.csa_attention.argtypes = [DP] + [P] * 17 + [P, SZ, P]
+    CP = ctypes.POINTER(CsaCompressDims)
+    L.csa_compress_workspace_size.argtypes = [CP, ctypes.POINTER(SZ)]
+    L.csa_compress.argtypes = [CP] + [P] * 7 + [SZ, P]
     for f in ("csa_workspace_size", "csa_index_scores", "csa_index_scores_fp8", "csa_topk_select",
-              "csa_sparse_mqa_decode",
-              "hca_mqa_decode", "csa_attention"):
+              "csa_sparse_mqa_decode", "hca_mqa_decode", "csa_attention", "csa_compress_workspace_size",
+              "csa_compress"):
         getattr(L, f).restype = I32
     _lib = L
     return L

@@ -332,6 +332,83 @@ csa_status csa_index_scores_fp8(const csa_dims *d, const uint8_t *q8, const floa
     return hip_status(csa::launch_index_scores_fp8(a, (hipStream_t)stream), "csa_index_scores_fp8");
 }
 
+static csa_status check_compress(const csa_compress_dims *d) {
+    if (!d) return fail(CSA_ERR_NULL, "dims is NULL");
+    if (d->tokens < 1 || d->n_entries < 1 || d->first_entry < 0 || d->ratio < 1)
+        return fail(CSA_ERR_DIM, "tokens, n_entries, ratio must be >= 1 and first_entry >= 0");
+    if (d->hidden < 64 || d->hidden % 64) return fail(CSA_ERR_DIM, "hidden must be a positive multiple of 64");
+    if (d->out_dim != 128 && d->out_dim != 256 && d->out_dim != 512)
+        return fail(CSA_ERR_UNSUPPORTED, "out_dim must be 128, 256 or 512 (got %d)", d->out_dim);
+    if (d->window < d->ratio || d->window > 4096) return fail(CSA_ERR_DIM, "window must be in [ratio, 4096]");
+    if (d->rope_dims < 0 || d->rope_dims > d->out_dim || (d->rope_dims & 1))
+        return fail(CSA_ERR_DIM, "rope_dims must be even and <= out_dim");
+    if (d->hadamard != 0 && d->hadamard != 1) return fail(CSA_ERR_DIM, "hadamard must be 0 or 1");
+    if (!(d->rope_theta > 0.f) || !(d->rms_eps > 0.f)) return fail(CSA_ERR_DIM, "rope_theta and rms_eps must be > 0");
+    if ((long long)d->ratio * ((long long)d->first_entry + d->n_entries) > (1ll << 30))
+        return fail(CSA_ERR_DIM, "entry positions beyond 2^30");
+    const long long first_tok = (long long)d->ratio * d->first_entry + d->ratio - d->window;
+    const long long last_tok = (long long)d->ratio * (d->first_entry + d->n_entries - 1) + d->ratio - 1;
+    if ((first_tok < 0 ? 0 : first_tok) < d->pos0 || last_tok >= (long long)d->pos0 + d->tokens)
+        return fail(CSA_ERR_DIM, "x rows [%d, %lld) do not cover the window tokens [%lld, %lld]", d->pos0,
+                    (long long)d->pos0 + d->tokens, first_tok < 0 ? 0 : first_tok, last_tok);
+    return CSA_OK;
+}
+
+static size_t ws_compress(const csa_compress_dims *d) {
+    const int s = csa::compress_splits(d->tokens, d->hidden, d->out_dim);
+    return (size_t)s * d->tokens * 2 * d->out_dim * 4;
+}
+
+csa_status csa_compress_workspace_size(const csa_compress_dims *d, size_t *bytes) {
+    csa_status s;
+    if ((s = check_compress(d))) return s;
+    REQUIRE_PTR(bytes);
+    *bytes = ws_compress(d);
+    return CSA_OK;
+}
+
+csa_status csa_compress(const csa_compress_dims *d, const void *x, const void *wkv, const void *wgate,
+                        const float *ape, const float *gamma, void *out, void *ws, size_t ws_bytes, void *stream) {
+    csa_status s;
+    if ((s = check_compress(d))) return s;
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(wkv);
+    REQUIRE_PTR(wgate);
+    REQUIRE_PTR(ape);
+    REQUIRE_PTR(gamma);
+    REQUIRE_PTR(out);
+    REQUIRE_ALIGN(x, 16);
+    REQUIRE_ALIGN(wkv, 16);
+    REQUIRE_ALIGN(wgate, 16);
+    REQUIRE_ALIGN(ape, 4);
+    REQUIRE_ALIGN(gamma, 4);
+    REQUIRE_ALIGN(out, 4);
+    if ((s = check_ws(ws, ws_bytes, ws_compress(d)))) return s;
+    REQUIRE_ALIGN(ws, 16);
+    csa::CompressArgs a{};
+    a.x = x;
+    a.wkv = wkv;
+    a.wgate = wgate;
+    a.ape = ape;
+    a.gamma = gamma;
+    a.out = out;
+    a.part = (float *)ws;
+    a.tokens = d->tokens;
+    a.hidden = d->hidden;
+    a.out_dim = d->out_dim;
+    a.ratio = d->ratio;
+    a.window = d->window;
+    a.rope_dims = d->rope_dims;
+    a.hadamard = d->hadamard;
+    a.first_entry = d->first_entry;
+    a.n_entries = d->n_entries;
+    a.pos0 = d->pos0;
+    a.n_splits = csa::compress_splits(d->tokens, d->hidden, d->out_dim);
+    a.rope_theta = d->rope_theta;
+    a.rms_eps = d->rms_eps;
+    return hip_status(csa::launch_compress(a, (hipStream_t)stream), "csa_compress");
+}
+
 csa_status csa_topk_select(const csa_dims *d, const float *scores, const int32_t *seq_len, const int32_t *q_pos,
                            int32_t *topk_idx, void *ws, size_t ws_bytes, void *stream) {
     csa_status s;

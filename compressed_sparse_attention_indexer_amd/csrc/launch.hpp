@@ -96,4 +96,17 @@ size_t mqa_workspace_bytes(int dtype, int n_queries, int H, int D, int max_rows)
 void mqa_carve(MqaArgs &a, void *ws, int n_queries);
 hipError_t launch_mqa(const MqaArgs &a, int dtype, hipStream_t stream);
 
+struct CompressArgs {
+    const void *x;              // [tokens, hidden] bf16, token 0 at raw position pos0
+    const void *wkv, *wgate;    // [out_dim, hidden] bf16
+    const float *ape;           // [window, out_dim]
+    const float *gamma;         // [out_dim]
+    void *out;                  // [n_entries, out_dim] bf16
+    float *part;                // [n_splits, tokens, 2 * out_dim] fp32 projections (workspace)
+    int tokens, hidden, out_dim, ratio, window, rope_dims, hadamard, first_entry, n_entries, pos0, n_splits;
+    float rope_theta, rms_eps;
+};
+int compress_splits(int tokens, int hidden, int out_dim);  // K splits of the projection
+hipError_t launch_compress(CompressArgs a, hipStream_t stream);
+
 }  // namespace csa

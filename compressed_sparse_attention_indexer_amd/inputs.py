@@ -34,6 +34,7 @@ _TID = {
     "sink": 8, "seq_len": 9, "win_v": 10,
     "hca_q": 11, "hca_kv": 12, "hca_win": 13, "hca_sink": 14,
     "q8": 15, "k8": 16,
+    "cx": 17, "wkv": 18, "wgate": 19, "ape": 20, "gamma": 21,
 }
 _ROW_CHUNK = 65536  # rows per independently seeded chunk of a per-sequence cache
 
@@ -281,3 +282,17 @@ def make_fp8_index(case: "Case"):
         k8.append(c)
         ks.append(sc)
     return q8, qs, k8, ks
+
+
+# ---------------------------------------------------------------- compressor inputs
+
+def make_compressor_inputs(seed: int, tokens: int, hidden: int, out_dim: int, window: int):
+    """Hidden states x [tokens, hidden] ~ N(0,1) and synthetic weights: wkv, wgate
+    ~ N(0,1)/sqrt(hidden) (bf16 bits), ape ~ N(0, 0.5^2), gamma ~ U(0.5, 1.5)."""
+    sh = 1.0 / math.sqrt(hidden)
+    x = _normal((tokens, hidden), 1.0, "bf16", seed, _TID["cx"])
+    wkv = _normal((out_dim, hidden), sh, "bf16", seed, _TID["wkv"])
+    wgate = _normal((out_dim, hidden), sh, "bf16", seed, _TID["wgate"])
+    ape = _normal((window, out_dim), 0.5, "f32", seed, _TID["ape"])
+    gamma = _rng(seed, _TID["gamma"]).uniform(0.5, 1.5, size=out_dim).astype(np.float32)
+    return x, wkv, wgate, ape, gamma

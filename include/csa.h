@@ -223,6 +223,55 @@ csa_status csa_attention(const csa_dims *dims, const void *q, const void *q_idx,
                          void *workspace, size_t ws_bytes, void *stream);
 
 /* Static string for a status code. */
+/*
+ * KV / index-key compressor -- the step that produces the compressed caches
+ * the path reads ([A] INNOVATIONS 1, CSA and HCA bullets: learned projection
+ * wkv and gating wgate, absolute position embeddings within each compression
+ * window, RMSNorm on the compressed output, RoPE on the rope dims, 4:1 with
+ * overlapping windows and 128:1; the indexer's own compressor adds a
+ * Hadamard rotation; [B] compress_rope_theta 160000, rms_norm_eps 1e-6).
+ * Readings (the pages list the ingredients, not the formula):
+ *   - entry e pools raw tokens [r*e + r - window, r*e + r - 1] (window = 2r
+ *     overlapping for CSA, r for HCA), tokens before position 0 left out;
+ *   - per token t at window slot i: kv_t = wkv x_t, gate_t = wgate x_t +
+ *     ape[i]; per output dim a softmax over the window's tokens of gate_t
+ *     weights kv_t;
+ *   - RMSNorm c / sqrt(mean(c^2) + eps) * gamma;
+ *   - RoPE on the trailing rope_dims dims, pair (2k, 2k+1) rotated by
+ *     (r*e) * theta^(-2k/rope_dims);
+ *   - optional normalized Hadamard rotation (Sylvester order), last.
+ */
+typedef struct csa_compress_dims {
+    int32_t tokens;       /* rows of x: raw positions pos0 .. pos0 + tokens - 1 */
+    int32_t hidden;       /* hidden size, a multiple of 64 */
+    int32_t out_dim;      /* 128, 256 or 512 */
+    int32_t ratio;        /* r >= 1 */
+    int32_t window;       /* tokens pooled per entry, ratio <= window <= 4096 */
+    int32_t rope_dims;    /* even, <= out_dim (0: no RoPE) */
+    int32_t hadamard;     /* 0 or 1 */
+    int32_t first_entry;  /* first entry to produce (>= 0) */
+    int32_t n_entries;    /* entries to produce (>= 1) */
+    int32_t pos0;         /* raw position of x's row 0 */
+    float rope_theta;     /* > 0 */
+    float rms_eps;        /* > 0 */
+} csa_compress_dims;
+
+/* Workspace bytes of csa_compress (host-only). */
+csa_status csa_compress_workspace_size(const csa_compress_dims *dims, size_t *bytes);
+
+/*
+ *   x      device [tokens, hidden] bf16 (16-byte aligned); every window token
+ *          of every requested entry (at raw position >= 0) must be a row of x
+ *   wkv, wgate device [out_dim, hidden] bf16
+ *   ape    device [window, out_dim] float32; gamma device [out_dim] float32
+ *   out    device [n_entries, out_dim] bf16 (entries first_entry ..)
+ * Projections accumulate in fp32; softmax, norm and rotations in fp32 (RoPE
+ * angles in fp64); the result is rounded to bf16.
+ */
+csa_status csa_compress(const csa_compress_dims *dims, const void *x, const void *wkv, const void *wgate,
+                        const float *ape, const float *gamma, void *out, void *workspace, size_t ws_bytes,
+                        void *stream);
+
 const char *csa_status_string(int32_t status);
 
 /* Detail of the last error on the calling thread ("" if none). */

@@ -187,3 +187,28 @@ def test_fp8_scorer_validation_before_any_launch():
     assert _scores_fp8(flash, k8=FAKE + 4) == _lib.CSA_ERR_ALIGN
     bad_act = csa.make_dims(batch=1, max_entries=16384, index_act=7)
     assert _scores_fp8(bad_act) == _lib.CSA_ERR_UNSUPPORTED
+
+
+def _compress(dims, ws_bytes=1 << 30, x=FAKE, out=FAKE, ws=FAKE):
+    return csa.load_library().csa_compress(ctypes.byref(dims), x, FAKE, FAKE, FAKE, FAKE, out, ws, ws_bytes, None)
+
+
+def test_compressor_validation_before_any_launch():
+    """Window coverage, sizes, pointers, alignment and workspace are checked before anything is enqueued."""
+    ok = dict(tokens=8, hidden=4096, out_dim=512, ratio=4, window=8, first_entry=1000, n_entries=1, pos0=3996,
+              rope_dims=64)
+    d = csa.make_compress_dims(**ok)
+    assert csa.compress_workspace_size(d) > 0
+    assert _compress(csa.make_compress_dims(**{**ok, "pos0": 3997})) == _lib.CSA_ERR_DIM       # first window row missing
+    assert _compress(csa.make_compress_dims(**{**ok, "tokens": 7})) == _lib.CSA_ERR_DIM         # last window row missing
+    assert _compress(csa.make_compress_dims(**{**ok, "out_dim": 192})) == _lib.CSA_ERR_UNSUPPORTED
+    assert _compress(csa.make_compress_dims(**{**ok, "hidden": 4000})) == _lib.CSA_ERR_DIM
+    assert _compress(csa.make_compress_dims(**{**ok, "window": 3})) == _lib.CSA_ERR_DIM          # window < ratio
+    assert _compress(csa.make_compress_dims(**{**ok, "rope_dims": 63})) == _lib.CSA_ERR_DIM
+    assert _compress(csa.make_compress_dims(**{**ok, "n_entries": 0})) == _lib.CSA_ERR_DIM
+    # entry 0's window is cut at position 0, so x may start there
+    assert csa.compress_workspace_size(csa.make_compress_dims(**{**ok, "first_entry": 0, "pos0": 0})) > 0
+    assert _compress(d, x=None) == _lib.CSA_ERR_NULL
+    assert _compress(d, x=MIS) == _lib.CSA_ERR_ALIGN
+    assert _compress(d, ws_bytes=16) == _lib.CSA_ERR_WORKSPACE
+    assert csa.load_library().csa_compress(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == _lib.CSA_ERR_NULL

@@ -437,3 +437,52 @@ def test_pro_shapes_whole_step_small(lens):
 
 def test_pro_decode_b4_1m_full():
     check_whole_step(inputs.make_case(inputs.WORKLOADS["pro_decode_b4_1m"]), ATT_TOL_BF16)
+
+
+# --------------------------------------------------------------------------- compressor (the step before the path)
+
+def check_compress(name, *, tokens, hidden, out_dim, ratio, window, first_entry, n_entries, pos0, rope_dims,
+                   hadamard=False, seed=501):
+    say(f"[case] compress {name}: tokens={tokens} hidden={hidden} out={out_dim} r={ratio} window={window} "
+        f"entries={first_entry}+{n_entries} rope={rope_dims} hadamard={hadamard}")
+    x, wkv, wg, ape, gamma = inputs.make_compressor_inputs(seed, tokens, hidden, out_dim, window)
+    dims = csa.make_compress_dims(tokens=tokens, hidden=hidden, out_dim=out_dim, ratio=ratio, window=window,
+                                  first_entry=first_entry, n_entries=n_entries, pos0=pos0, rope_dims=rope_dims,
+                                  hadamard=hadamard)
+    dev = "cuda"
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).to(dev)
+    g = csa.csa_compress(dims, bf(x), bf(wkv), bf(wg), torch.from_numpy(ape).to(dev), torch.from_numpy(gamma).to(dev))
+    torch.cuda.synchronize()
+    got = g.float().cpu().numpy().astype(np.float64)
+    want = oracle.compress(x, wkv, wg, ape, gamma, pos0=pos0, ratio=ratio, window=window, first_entry=first_entry,
+                           n_entries=n_entries, rope_dims=rope_dims, hadamard=hadamard)
+    # the GPU rounds its fp32 result to bf16: within one bf16 ulp of the exact value
+    err = np.abs(got - want)
+    bound = 2.0 ** -7 * np.abs(want) + 1e-5
+    worst = float(np.max(err / bound))
+    assert np.isfinite(got).all() and worst <= 1.0, f"{name}: worst err/bound {worst:.3f}"
+    say(f"  ok: worst err / (1 bf16 ulp) = {worst:.3f}")
+
+
+def test_compress_csa_decode_entry():
+    """One new 4:1 entry at a decode step: its 8-token overlapping window, full hidden size, RoPE on 64 dims."""
+    e = 1000
+    check_compress("csa_decode", tokens=8, hidden=4096, out_dim=512, ratio=4, window=8, first_entry=e, n_entries=1,
+                   pos0=4 * e + 4 - 8, rope_dims=64)
+
+
+def test_compress_csa_chunk_from_position_zero():
+    """A chunk of entries from the sequence start (entry 0's window is cut at position 0)."""
+    check_compress("csa_chunk", tokens=256, hidden=1024, out_dim=512, ratio=4, window=8, first_entry=0,
+                   n_entries=64, pos0=0, rope_dims=64)
+
+
+def test_compress_hca_entries():
+    check_compress("hca", tokens=384, hidden=1024, out_dim=512, ratio=128, window=128, first_entry=2, n_entries=3,
+                   pos0=256, rope_dims=64)
+
+
+def test_compress_index_keys_with_hadamard():
+    """The indexer's key compressor: 128-d output, Hadamard rotation last."""
+    check_compress("index_keys", tokens=40, hidden=2048, out_dim=128, ratio=4, window=8, first_entry=3,
+                   n_entries=8, pos0=8, rope_dims=64, hadamard=True)
