@@ -380,8 +380,8 @@ csa_status csa_compress(const csa_compress_dims *d, const void *x, const void *w
     REQUIRE_ALIGN(x, 16);
     REQUIRE_ALIGN(wkv, 16);
     REQUIRE_ALIGN(wgate, 16);
-    REQUIRE_ALIGN(ape, 4);
-    REQUIRE_ALIGN(gamma, 4);
+    REQUIRE_ALIGN(ape, 16);
+    REQUIRE_ALIGN(gamma, 16);
     REQUIRE_ALIGN(out, 4);
     if ((s = check_ws(ws, ws_bytes, ws_compress(d)))) return s;
     REQUIRE_ALIGN(ws, 16);
@@ -406,6 +406,7 @@ csa_status csa_compress(const csa_compress_dims *d, const void *x, const void *w
     a.n_splits = csa::compress_splits(d->tokens, d->hidden, d->out_dim);
     a.rope_theta = d->rope_theta;
     a.rms_eps = d->rms_eps;
+    a.rope_ln_theta = std::log((double)d->rope_theta);
     return hip_status(csa::launch_compress(a, (hipStream_t)stream), "csa_compress");
 }
 

@@ -105,6 +105,7 @@ struct CompressArgs {
     float *part;                // [n_splits, tokens, 2 * out_dim] fp32 projections (workspace)
     int tokens, hidden, out_dim, ratio, window, rope_dims, hadamard, first_entry, n_entries, pos0, n_splits;
     float rope_theta, rms_eps;
+    double rope_ln_theta;       // ln(rope_theta), worked out on the host in float64
 };
 int compress_splits(int tokens, int hidden, int out_dim);  // K splits of the projection
 hipError_t launch_compress(CompressArgs a, hipStream_t stream);

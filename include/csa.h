@@ -222,7 +222,6 @@ csa_status csa_attention(const csa_dims *dims, const void *q, const void *q_idx,
                          float *out, float *lse, int32_t *topk_idx_out, float *scores_out,
                          void *workspace, size_t ws_bytes, void *stream);
 
-/* Static string for a status code. */
 /*
  * KV / index-key compressor -- the step that produces the compressed caches
  * the path reads ([A] INNOVATIONS 1, CSA and HCA bullets: learned projection
@@ -262,9 +261,14 @@ csa_status csa_compress_workspace_size(const csa_compress_dims *dims, size_t *by
 /*
  *   x      device [tokens, hidden] bf16 (16-byte aligned); every window token
  *          of every requested entry (at raw position >= 0) must be a row of x
- *   wkv, wgate device [out_dim, hidden] bf16
+ *   wkv, wgate device [out_dim, hidden] bf16 (16-byte aligned)
  *   ape    device [window, out_dim] float32; gamma device [out_dim] float32
+ *          (both 16-byte aligned)
  *   out    device [n_entries, out_dim] bf16 (entries first_entry ..)
+ *   workspace device, csa_compress_workspace_size bytes (16-byte aligned): the
+ *          fp32 projections of x's rows
+ * All buffers stay owned by the caller; nothing is allocated.  Shape, pointer,
+ * alignment and workspace errors return before anything is enqueued.
  * Projections accumulate in fp32; softmax, norm and rotations in fp32 (RoPE
  * angles in fp64); the result is rounded to bf16.
  */
@@ -272,6 +276,7 @@ csa_status csa_compress(const csa_compress_dims *dims, const void *x, const void
                         const float *ape, const float *gamma, void *out, void *workspace, size_t ws_bytes,
                         void *stream);
 
+/* Static string for a status code. */
 const char *csa_status_string(int32_t status);
 
 /* Detail of the last error on the calling thread ("" if none). */
