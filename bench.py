@@ -289,6 +289,49 @@ def bench_fp8_scores(torch, csa, case, args):
             "vs_bf16_scorer": None}
 
 
+COMPRESS_CASES = (
+    # name, tokens, out_dim, ratio, window, first entry, entries, hadamard: one new entry at a decode
+    # step (its window), and the entries of a 2,048-token prefill chunk (plus the 4 tokens of
+    # overlap), for the 512-d KV cache, the 128-d index keys (Hadamard) and the 128:1 HCA cache
+    ("kv_decode_entry", 8, 512, 4, 8, 262143, 1, False),
+    ("index_key_decode_entry", 8, 128, 4, 8, 262143, 1, True),
+    ("hca_decode_entry", 128, 512, 128, 128, 8191, 1, False),
+    ("kv_prefill_chunk_2048", 2052, 512, 4, 8, 261632, 512, False),
+    ("index_key_prefill_chunk_2048", 2052, 128, 4, 8, 261632, 512, True),
+    ("hca_prefill_chunk_2048", 2048, 512, 128, 128, 8176, 16, False),
+)
+COMPRESS_HIDDEN = 4096
+
+
+def bench_compress(torch, csa, args):
+    """csa_compress on decode and prefill-chunk shapes (hidden 4096, RoPE on 64 dims).  Bytes: the
+    two weight matrices, the x rows and the bf16 output; flops: the two projections."""
+    import numpy as np
+    from compressed_sparse_attention_indexer_amd import inputs
+    dev, res = "cuda", {}
+    for name, T, D, r, w, fe, ne, had in COMPRESS_CASES:
+        x, wkv, wg, ape, gamma = inputs.make_compressor_inputs(11, T, COMPRESS_HIDDEN, D, w)
+        bf = lambda a: torch.from_numpy(a.view(np.int16)).to(dev)
+        X, WK, WG = bf(x), bf(wkv), bf(wg)
+        AP, GM = torch.from_numpy(ape).to(dev), torch.from_numpy(gamma).to(dev)
+        pos0 = r * fe + r - w
+        dims = csa.make_compress_dims(tokens=T, hidden=COMPRESS_HIDDEN, out_dim=D, ratio=r, window=w,
+                                      first_entry=fe, n_entries=ne, pos0=pos0, rope_dims=64, hadamard=had)
+        out = torch.empty((ne, D), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(max(256, csa.compress_workspace_size(dims)), dtype=torch.uint8, device=dev)
+        g = capture(torch, lambda i: csa.csa_compress(dims, X, WK, WG, AP, GM, out=out, workspace=ws),
+                    args.graph_steps)
+        ms, _, _ = time_graph(torch, g, args.graph_steps, max(args.steps, 20), args.warmup)
+        byt = 2 * D * COMPRESS_HIDDEN * 2 + T * COMPRESS_HIDDEN * 2 + ne * D * 2
+        fl = 2.0 * T * COMPRESS_HIDDEN * 2 * D
+        gbs, tfs = byt / (ms * 1e-3) / 1e9, fl / (ms * 1e-3) / 1e12
+        res[name] = {"us_per_call": ms * 1e3, "entries": ne, "tokens": T, "alg_bytes": byt, "GBps": gbs,
+                     "frac_hbm_peak": gbs / HBM_PEAK_GBS, "flops": fl, "TFLOPs": tfs,
+                     "frac_mfma_peak": tfs / MFMA_BF16_PEAK_TFLOPS}
+        del X, WK, WG, AP, GM, out, ws, g
+    return res
+
+
 def traffic_from_profile():
     """HBM bytes per scorer launch from the committed rocprofv3 counter runs,
     only while the scorer source is the one the counters were taken on."""
@@ -358,6 +401,7 @@ def main():
         f8 = bench_fp8_scores(torch, csa, case, args)
         f8["vs_bf16_scorer"] = main_res["kernel_ms"]["index_scores"] / f8["ms_per_call"]
         breakdown[wl.name + "_fp8_index_scores"] = f8
+    breakdown["compressor"] = bench_compress(torch, csa, args)
     Q = wl.batch * wl.q_len
     scorer_ms = main_res["kernel_ms"]["index_scores"]
     alg = main_res["scorer_alg_bytes"]

@@ -13,7 +13,8 @@
 //     token tiles, and the waves' sums meet in LDS.  Every weight byte is read
 //     once, with a whole batch of loads in flight per wave.
 //   * many tokens (a prefill chunk): a 128 x 128 LDS-tiled GEMM, 64 of hidden
-//     per stage, double-buffered, 4 waves of 64 x 64; hidden is split over 2-8
+//     per stage, double-buffered LDS fed from a 2-stage ring of register
+//     prefetches, 8 waves of 64 x 32; hidden is split over 2-8
 //     workgroups when the tiles alone would leave CUs idle, each split writing
 //     its own fp32 partial.
 // (2) One workgroup per compressed entry: token groups run an online softmax
@@ -37,6 +38,7 @@ constexpr int kGmK = 64;                              // hidden per stage
 constexpr int kGmRow = kGmK + 8;                      // LDS row pitch in bf16 (16 B pad)
 constexpr int kGmStage = 2 * kGmTile * kGmRow;        // bf16 per stage (A then B)
 constexpr int kGmMaxSplits = 8;
+constexpr int kGmWaves = 8;                           // 2 x 4 waves of 64 x 32
 // pooling
 constexpr int kPoolThreads = 1024;
 }  // namespace
@@ -116,71 +118,98 @@ __global__ __launch_bounds__(64 * kGvWaves) void compress_gemv_kernel(CompressAr
     }
 }
 
-// P_s[t, n] = sum over split s's share of hidden of x[t, h] W[n, h]
-__global__ __launch_bounds__(256) void compress_gemm_kernel(CompressArgs a) {
+// P_s[t, n] = sum over split s's share of hidden of x[t, h] W[n, h].  Stage
+// st's global loads are issued kAhead stages before its LDS copy (a ring of
+// register slots); the LDS itself is double-buffered.  Tiles are numbered so
+// that the column tiles of a token tile run on one XCD (consecutive workgroups
+// go to consecutive XCDs) and share its x rows in that XCD's L2.  Measured on
+// the 2,048-token chunk it is bound by how fast each CU's L1 is refilled (one
+// 32 KiB stage per workgroup per 64 of hidden), not by the MFMA rate.
+template <int kWaves, int kAhead>
+__global__ __launch_bounds__(64 * kWaves) void compress_gemm_kernel(CompressArgs a) {
+    constexpr int kThreads = 64 * kWaves;
+    constexpr int kPass = kGmTile * 8 / kThreads;  // copy passes per operand tile (8 threads per 128-B row)
+    constexpr int kWn = kWaves / 2;                 // waves along the columns (2 along the tokens)
+    constexpr int kNt = kGmTile / kWn / 16;         // 16-column MFMA tiles per wave
     __shared__ uint16_t s_tile[2 * kGmStage];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int e = lane & 15, g = lane >> 4;
-    const int wm = wave & 1, wn = wave >> 1;  // 2 x 2 waves of 64 x 64
+    const int wm = wave & 1, wn = wave >> 1;  // wave tile: 64 tokens x 16 kNt columns
     const int N = 2 * a.out_dim;
-    const int m0 = blockIdx.x * kGmTile, n0 = blockIdx.y * kGmTile;
-    const int kspan = a.hidden / gridDim.z, kbeg = blockIdx.z * kspan;
+    const int n_m = gridDim.x, n_n = gridDim.y, n_tiles = n_m * n_n * gridDim.z;
+    const int lin = blockIdx.x + n_m * (blockIdx.y + n_n * blockIdx.z);
+    int tile = lin;
+    if (n_tiles % 8 == 0) tile = (lin % 8) * (n_tiles / 8) + lin / 8;
+    const int tn = tile % n_n, tm = (tile / n_n) % n_m, split = tile / (n_n * n_m);
+    const int m0 = tm * kGmTile, n0 = tn * kGmTile;
+    const int kspan = a.hidden / gridDim.z, kbeg = split * kspan;
     const int nst = kspan / kGmK;
-    // global -> LDS copy: thread covers 16 B chunk (tid % 8) of rows tid / 8 + 32 p
+    // global -> LDS copy: thread covers 16 B chunk (tid % 8) of rows tid / 8 + (kThreads / 8) p
+    constexpr int kRowStep = kThreads / 8;
     const int cr = tid >> 3, cc = 8 * (tid & 7);
-    const uint16_t *asrc[4], *bsrc[4];
+    const uint16_t *asrc[kPass], *bsrc[kPass];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        int t = m0 + cr + 32 * p;
+    for (int p = 0; p < kPass; ++p) {
+        int t = m0 + cr + kRowStep * p;
         t = t < a.tokens ? t : a.tokens - 1;  // rows past the end repeat the last row; never stored
         asrc[p] = (const uint16_t *)a.x + (size_t)t * a.hidden + kbeg + cc;
-        bsrc[p] = proj_row(a, n0 + cr + 32 * p) + kbeg + cc;
+        bsrc[p] = proj_row(a, n0 + cr + kRowStep * p) + kbeg + cc;
     }
-    bf16x8_t ra[4], rb[4];
-    auto fetch = [&](int st) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            ra[p] = *(const bf16x8_t *)(asrc[p] + st * kGmK);
-            rb[p] = *(const bf16x8_t *)(bsrc[p] + st * kGmK);
-        }
-    };
-    auto stash = [&](int buf) {
-        uint16_t *sa = s_tile + buf * kGmStage, *sb = sa + kGmTile * kGmRow;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            *(bf16x8_t *)(sa + (cr + 32 * p) * kGmRow + cc) = ra[p];
-            *(bf16x8_t *)(sb + (cr + 32 * p) * kGmRow + cc) = rb[p];
-        }
-    };
-    f32x4_t acc[4][4];
+    bf16x8_t ra[kAhead][kPass], rb[kAhead][kPass];
+#define GM_FETCH(slot, st)                                                      \
+    _Pragma("unroll") for (int p = 0; p < kPass; ++p) {                         \
+        ra[slot][p] = *(const bf16x8_t *)(asrc[p] + (st) * kGmK);               \
+        rb[slot][p] = *(const bf16x8_t *)(bsrc[p] + (st) * kGmK);               \
+    }
+#define GM_STASH(slot, buf)                                                     \
+    {                                                                           \
+        uint16_t *sa_ = s_tile + (buf) * kGmStage, *sb_ = sa_ + kGmTile * kGmRow; \
+        _Pragma("unroll") for (int p = 0; p < kPass; ++p) {                     \
+            *(bf16x8_t *)(sa_ + (cr + kRowStep * p) * kGmRow + cc) = ra[slot][p]; \
+            *(bf16x8_t *)(sb_ + (cr + kRowStep * p) * kGmRow + cc) = rb[slot][p]; \
+        }                                                                       \
+    }
+    f32x4_t acc[4][kNt];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    fetch(0);
-    stash(0);
+        for (int j = 0; j < kNt; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // the loop body has no branches, so the compiler's memory counters wait only for the
+    // slot being copied: stages past the end are fetched again from the last stage (in
+    // bounds, never used), and kAhead divides the stage count
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j) GM_FETCH(j, min(j, nst - 1))
+    GM_STASH(0, 0)
     __syncthreads();
-    for (int st = 0; st < nst; ++st) {
-        if (st + 1 < nst) fetch(st + 1);
-        const uint16_t *sa = s_tile + (st & 1) * kGmStage, *sb = sa + kGmTile * kGmRow;
+    for (int st0 = 0; st0 < nst; st0 += kAhead) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            bf16x8_t af[4], bfr[4];
+        for (int j = 0; j < kAhead; ++j) {
+            const int st = st0 + j;
+            // slot j held stage st (already in LDS): refill it with stage st + kAhead
+            GM_FETCH(j, min(st + kAhead, nst - 1))
+            const uint16_t *sa = s_tile + (st & 1) * kGmStage, *sb = sa + kGmTile * kGmRow;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                af[i] = *(const bf16x8_t *)(sa + (64 * wm + 16 * i + e) * kGmRow + 16 * g + 8 * ks);
-                bfr[i] = *(const bf16x8_t *)(sb + (64 * wn + 16 * i + e) * kGmRow + 16 * g + 8 * ks);
+            for (int ks = 0; ks < 2; ++ks) {
+                bf16x8_t af[4], bfr[kNt];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    af[i] = *(const bf16x8_t *)(sa + (64 * wm + 16 * i + e) * kGmRow + 16 * g + 8 * ks);
+#pragma unroll
+                for (int q = 0; q < kNt; ++q)
+                    bfr[q] = *(const bf16x8_t *)(sb + (16 * kNt * wn + 16 * q + e) * kGmRow + 16 * g + 8 * ks);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int q = 0; q < kNt; ++q)
+                        acc[i][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[q], acc[i][q], 0, 0, 0);
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            GM_STASH((j + 1) % kAhead, (st + 1) & 1)  // after the last stage: a copy nobody reads
+            __syncthreads();
         }
-        if (st + 1 < nst) stash((st + 1) & 1);
-        __syncthreads();
     }
-    float *P = a.part + (size_t)blockIdx.z * a.tokens * N;
+#undef GM_FETCH
+#undef GM_STASH
+    float *P = a.part + (size_t)split * a.tokens * N;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -188,7 +217,7 @@ __global__ __launch_bounds__(256) void compress_gemm_kernel(CompressArgs a) {
             const int t = m0 + 64 * wm + 16 * i + 4 * g + r;
             if (t >= a.tokens) continue;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) P[(size_t)t * N + n0 + 64 * wn + 16 * j + e] = acc[i][j][r];
+            for (int q = 0; q < kNt; ++q) P[(size_t)t * N + n0 + 16 * kNt * wn + 16 * q + e] = acc[i][q][r];
         }
 }
 
@@ -349,11 +378,19 @@ hipError_t launch_compress(CompressArgs a, hipStream_t stream) {
         hipLaunchKernelGGL(compress_gemv_kernel, dim3(N / 16), dim3(64 * kGvWaves), 0, stream, a);
     } else {
         const dim3 grid((a.tokens + kGmTile - 1) / kGmTile, N / kGmTile, a.n_splits);
-        hipLaunchKernelGGL(compress_gemm_kernel, grid, dim3(256), 0, stream, a);
+        const int nst = a.hidden / a.n_splits / kGmK;  // stages of global loads in flight: 2 or 1
+        constexpr int W = kGmWaves;
+        if (nst % 2 == 0)
+            hipLaunchKernelGGL((compress_gemm_kernel<W, 2>), grid, dim3(64 * W), 0, stream, a);
+        else
+            hipLaunchKernelGGL((compress_gemm_kernel<W, 1>), grid, dim3(64 * W), 0, stream, a);
     }
     const int gs = a.out_dim / 4;
+    // token groups per entry: enough threads to cover one entry's window at decode; with many
+    // entries the workgroups themselves fill the GPU, so small ones (all resident at once) do
     int groups = kPoolThreads / gs;
     while (groups > 1 && groups / 2 >= a.window) groups /= 2;  // no more groups than window tokens
+    while (groups > 1 && (long)a.n_entries * groups * gs > 256L * 1024) groups /= 2;
     hipLaunchKernelGGL(compress_pool_kernel, dim3(a.n_entries), dim3(groups * gs), 0, stream, a);
     return hipGetLastError();
 }

@@ -486,3 +486,33 @@ def test_compress_index_keys_with_hadamard():
     """The indexer's key compressor: 128-d output, Hadamard rotation last."""
     check_compress("index_keys", tokens=40, hidden=2048, out_dim=128, ratio=4, window=8, first_entry=3,
                    n_entries=8, pos0=8, rope_dims=64, hadamard=True)
+
+
+def test_compress_full_chunk_of_entries():
+    """512 entries from 2,052 tokens: the pooling runs fewer token groups per entry when many entries fill the GPU."""
+    check_compress("kv_chunk_512", tokens=2052, hidden=1024, out_dim=512, ratio=4, window=8, first_entry=1000,
+                   n_entries=512, pos0=3996, rope_dims=64)
+
+
+def test_compress_index_keys_eight_way_split():
+    """Few token tiles: hidden split over 8 workgroups, 8 partial sums per row."""
+    check_compress("index_keys_split8", tokens=1000, hidden=2048, out_dim=128, ratio=4, window=8, first_entry=0,
+                   n_entries=250, pos0=0, rope_dims=64, hadamard=True)
+
+
+def test_compress_odd_stage_count():
+    """hidden = 17 x 64: an odd number of 64-wide stages (one stage of loads in flight), no split."""
+    check_compress("odd_stages", tokens=300, hidden=1088, out_dim=256, ratio=4, window=8, first_entry=20,
+                   n_entries=70, pos0=76, rope_dims=32)
+
+
+def test_compress_hca_decode_window():
+    """One 128:1 entry from its 128-token window: the weight-streaming projection over 8 token tiles."""
+    check_compress("hca_decode", tokens=128, hidden=2048, out_dim=512, ratio=128, window=128, first_entry=4000,
+                   n_entries=1, pos0=512000, rope_dims=64)
+
+
+def test_compress_small_hidden_ragged_tokens():
+    """hidden 256 (4 blocks for 8 waves: half the waves idle) and 20 tokens (a ragged second token tile)."""
+    check_compress("small_hidden", tokens=20, hidden=256, out_dim=128, ratio=4, window=8, first_entry=7,
+                   n_entries=4, pos0=24, rope_dims=0, hadamard=True)
