@@ -127,29 +127,34 @@ __global__ __launch_bounds__(256) void mqa_f32_kernel(MqaArgs a) {
 //
 // Workgroup = one (query, split): 2*HG waves; wave (hg, dh) owns heads
 // [16hg, 16hg+16) and output dims [256dh, 256dh+256).  Rows stream through
-// LDS 32 at a time, gathered with 16-byte loads (each thread one row, a
-// prefetch one tile ahead in registers):
-//   krow: bf16 rows [32][520] (padded) feeding QK;
-//   vt:   fp16 values transposed to [d'][32 rows] feeding PV, where
-//         d' = (d % 8) * 64 + d / 8 keeps the transposing writes and the PV
-//         fragment reads free of bank conflicts.
+// LDS 32 at a time as bf16 rows [32][520] (padded), gathered with 16-byte
+// loads (each thread one row, a prefetch one tile ahead in registers); a
+// separate value row set gets its own buffer.
 // QK: S^T[rows x heads] = K * Q^T on v_mfma_f32_16x16x32_bf16, each wave over
 // its 256 dims; the two halves are summed through LDS (a + b in both waves,
 // so both see bit-identical logits).  Online softmax in fp32 (log2 units).
-// PV: O[heads x d] += P * V on v_mfma_f32_16x16x32_f16 with P in fp16 held in
-// registers exactly as QK left it (its row order defines the k order of V).
+// PV: O[heads x d] += P * V on v_mfma_f32_16x16x32_bf16.  P stays in
+// registers exactly as QK left it (its row order defines the k order of V),
+// split into a bf16 high part and a bf16 remainder (two MFMAs, about 16
+// significant bits); the V fragments come straight from the row-major tile
+// through gfx950's transposing LDS read (ds_read_b64_tr_b16), two per
+// fragment.
 // Output: partial (m, l, O) per split, or the final result with the sink when
 // there is one split.
 namespace {
 constexpr int kD = 512;
 constexpr int kTile = 32;
 constexpr int kKrowStride = kD + 8;   // bf16 elements per staged row (1040 B)
-constexpr int kVtRowWords = 18;       // 32 fp16 rows + 2 pad words per d' row
-constexpr int kVtWords = kD * kVtRowWords + 2 * 8;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef short v8i16_t __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ int vt_word(int d, int row) {
-    const int dp = (d & 7) * 64 + (d >> 3);
-    return dp * kVtRowWords + 2 * (dp >> 6) + (row >> 1);
+// Transposing LDS read (gfx950): within each group of 16 lanes, lane i gets
+// element i % 4 of the 8-byte vectors addressed by lanes i / 4, 4 + i / 4,
+// 8 + i / 4 and 12 + i / 4 (in that order).  With lane s of the group
+// addressing row r0 + s / 4, columns c0 + 4 (s % 4) .. + 3 of a row-major
+// bf16 tile, lane i receives rows r0 .. r0 + 3 of column c0 + i.
+__device__ __forceinline__ v4i16_t lds_read_tr16(const uint16_t *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t *)p);
 }
 }  // namespace
 
@@ -162,7 +167,7 @@ __global__ __launch_bounds__(128 * HG) void mqa_bf16_kernel(MqaArgs a) {
     static_assert(kTile % NW == 0 && 64 % RPW == 0, "staging layout");
 
     __shared__ __attribute__((aligned(16))) uint16_t krow[kTile * kKrowStride];
-    __shared__ __attribute__((aligned(16))) uint32_t vt[kVtWords];
+    __shared__ __attribute__((aligned(16))) uint16_t vrow_sep[kTile * kKrowStride];  // separate values only
     __shared__ float xs[NW][8][64];
     __shared__ int rowok[kTile];
 
@@ -215,15 +220,7 @@ __global__ __launch_bounds__(128 * HG) void mqa_bf16_kernel(MqaArgs a) {
         for (int c = 0; c < CPL; ++c) {
             const int ch = cg + LPR * c;
             *(u32x4_t *)&krow[srow * kKrowStride + 8 * ch] = kreg[c];
-            const u32x4_t vv = separate_v ? vreg[c] : kreg[c];
-            _Float16 *vth = (_Float16 *)vt;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float lo = bf16_bits_to_f32(vv[k] & 0xFFFFu);
-                const float hi = bf16_bits_to_f32(vv[k] >> 16);
-                vth[2 * vt_word(8 * ch + 2 * k, srow) + (srow & 1)] = (_Float16)lo;
-                vth[2 * vt_word(8 * ch + 2 * k + 1, srow) + (srow & 1)] = (_Float16)hi;
-            }
+            if (separate_v) *(u32x4_t *)&vrow_sep[srow * kKrowStride + 8 * ch] = vreg[c];
         }
         if (cg == 0) rowok[srow] = have_row;
         if (t + 1 < ntiles) fetch(t + 1);
@@ -276,18 +273,24 @@ __global__ __launch_bounds__(128 * HG) void mqa_bf16_kernel(MqaArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) o[dt][r] *= ar[r];
         }
-        f16x8_t pf;
+        bf16x8_t ph, pl;  // P = ph + pl, each part bf16
 #pragma unroll
-        for (int v = 0; v < 8; ++v) pf[v] = (_Float16)pv[v];
+        for (int v = 0; v < 8; ++v) {
+            ph[v] = (__bf16)pv[v];
+            pl[v] = (__bf16)(pv[v] - (float)ph[v]);
+        }
+        const uint16_t *vrow = separate_v ? vrow_sep : krow;
+        const int s16 = lane & 15;  // this lane's address role in the transposing read
         // PV over this wave's 256 output dims.
 #pragma unroll
         for (int dt = 0; dt < 16; ++dt) {
-            const int d = 256 * dh + 16 * dt + e;
-            const int w0 = vt_word(d, 4 * g);
-            const uint32_t x0 = vt[w0], x1 = vt[w0 + 1], x2 = vt[w0 + 8], x3 = vt[w0 + 9];
-            const u32x4_t vw = u32x4_t{x0, x1, x2, x3};
-            const f16x8_t vf = __builtin_bit_cast(f16x8_t, vw);
-            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pf, vf, o[dt], 0, 0, 0);
+            // B fragment: V[rows 4g .. 4g+3 and 16+4g .. 16+4g+3][d = 256dh + 16dt + e]
+            const uint16_t *vp0 = vrow + (4 * g + (s16 >> 2)) * kKrowStride + 256 * dh + 16 * dt + 4 * (s16 & 3);
+            const v4i16_t lo = lds_read_tr16(vp0);
+            const v4i16_t hi = lds_read_tr16(vp0 + 16 * kKrowStride);
+            const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, (v8i16_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vf, o[dt], 0, 0, 0);
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vf, o[dt], 0, 0, 0);
         }
     }
 
