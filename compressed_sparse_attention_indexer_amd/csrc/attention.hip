@@ -196,8 +196,10 @@ __global__ __launch_bounds__(128 * HG) void mqa_bf16_kernel(MqaArgs a) {
     float m_run = -INFINITY, l_run = 0.f;  // head 16hg + e, log2 units
 
     // staging role: one row, CPL chunks of 16 bytes
-    const int srow = wave * RPW + (lane % RPW);
-    const int cg = lane / RPW;
+    // (a group of LPR consecutive lanes takes one row, so each 16-lane phase of
+    // the LDS writes covers 256 contiguous bytes)
+    const int srow = wave * RPW + lane / LPR;
+    const int cg = lane % LPR;
     const bool separate_v = a.v != nullptr || a.win_v != nullptr;
     u32x4_t kreg[CPL], vreg[CPL];
     bool have_row = false;
