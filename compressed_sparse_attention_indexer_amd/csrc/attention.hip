@@ -145,6 +145,7 @@ namespace {
 constexpr int kD = 512;
 constexpr int kTile = 32;
 constexpr int kKrowStride = kD + 8;   // bf16 elements per staged row (1040 B)
+constexpr float kLazyMax = 8.f;       // log2 headroom of the running softmax reference
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef short v8i16_t __attribute__((ext_vector_type(8)));
 
@@ -203,15 +204,19 @@ __global__ __launch_bounds__(128 * HG) void mqa_bf16_kernel(MqaArgs a) {
     const bool separate_v = a.v != nullptr || a.win_v != nullptr;
     u32x4_t kreg[CPL], vreg[CPL];
     bool have_row = false;
+    // a missing row (padding, out of range, past the list) reads this query's q
+    // instead: finite values whose logit is masked to -inf, so its weight is 0
+    const uint16_t *dummy = (const uint16_t *)a.q + (size_t)qi * a.H * kD;
     auto fetch = [&](int t) {
         const uint16_t *kp, *vp;
         row_ptrs(a, qi, rl, r0 + t * kTile + srow < r1 ? r0 + t * kTile + srow : -1, &kp, &vp);
         have_row = kp != nullptr;
+        if (!have_row) kp = vp = dummy;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             const int ch = cg + LPR * c;
-            kreg[c] = have_row ? *(const u32x4_t *)(kp + 8 * ch) : u32x4_t{0u, 0u, 0u, 0u};
-            if (separate_v) vreg[c] = have_row ? *(const u32x4_t *)(vp + 8 * ch) : u32x4_t{0u, 0u, 0u, 0u};
+            kreg[c] = *as_global<u32x4_t>(kp + 8 * ch);
+            if (separate_v) vreg[c] = *as_global<u32x4_t>(vp + 8 * ch);
         }
     };
     if (ntiles > 0) fetch(0);
@@ -253,20 +258,24 @@ __global__ __launch_bounds__(128 * HG) void mqa_bf16_kernel(MqaArgs a) {
         for (int v = 1; v < 8; ++v) mx = fmaxf(mx, z[v]);
         mx = max_xor16(mx);
         mx = max_xor32(mx);
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = exp2f(m_run - m_use);
+        // The reference max moves only when a logit passes it by more than kLazyMax (log2
+        // units, also on the first finite logit): weights stay below 2^kLazyMax, and the
+        // output accumulators are rescaled only when it moves.
+        const bool move = mx > m_run + kLazyMax;
+        const float m_ref = move ? mx : m_run;
+        const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+        const float alpha = move ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
         float pv[8], ls = 0.f;
 #pragma unroll
         for (int v = 0; v < 8; ++v) {
-            pv[v] = exp2f(z[v] - m_use);
+            pv[v] = __builtin_amdgcn_exp2f(z[v] - m_use);
             ls += pv[v];
         }
         ls = sum_xor16(ls);
         ls = sum_xor32(ls);
         l_run = l_run * alpha + ls;
-        m_run = m_new;
-        if (__any(alpha != 1.f)) {
+        m_run = m_ref;
+        if (__any(move)) {
             float ar[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * g + r);
@@ -290,7 +299,7 @@ __global__ __launch_bounds__(128 * HG) void mqa_bf16_kernel(MqaArgs a) {
             const uint16_t *vp0 = vrow + (4 * g + (s16 >> 2)) * kKrowStride + 256 * dh + 16 * dt + 4 * (s16 & 3);
             const v4i16_t lo = lds_read_tr16(vp0);
             const v4i16_t hi = lds_read_tr16(vp0 + 16 * kKrowStride);
-            const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, (v8i16_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+            const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vf, o[dt], 0, 0, 0);
             o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vf, o[dt], 0, 0, 0);
         }
