@@ -390,15 +390,24 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(MqaArgs a) {
     };
     load_batch(ov[0], 0);
     {  // weights of head h0 + wv
+        // (m, l) of split s = ln + 64 i: the first 64 splits' pairs stay in registers
+        // between the max and the weights (one read); further ones are read twice
         const float sink2 = a.sink[h0 + wv] * kLog2e;
-        float M = sink2;
-        for (int s = ln; s < S; s += 64) {
+        float2 ml0 = float2{0.f, 0.f};
+        if (ln < S) ml0 = *(const float2 *)(a.part_ml + (((size_t)qi * S + ln) * a.H + h0 + wv) * 2);
+        float M = ml0.y > 0.f ? fmaxf(sink2, ml0.x) : sink2;
+        for (int s = ln + 64; s < S; s += 64) {
             const float *ml = a.part_ml + (((size_t)qi * S + s) * a.H + h0 + wv) * 2;
             if (ml[1] > 0.f) M = fmaxf(M, ml[0]);
         }
         M = wave_max(M);
         float L = 0.f;
-        for (int s = ln; s < S; s += 64) {
+        if (ln < S) {
+            const float w = ml0.y > 0.f ? ml0.y * exp2f(ml0.x - M) : 0.f;
+            s_w[ln][wv] = w;
+            L += w;
+        }
+        for (int s = ln + 64; s < S; s += 64) {
             const float *ml = a.part_ml + (((size_t)qi * S + s) * a.H + h0 + wv) * 2;
             const float l = ml[1];
             const float w = l > 0.f ? l * exp2f(ml[0] - M) : 0.f;
