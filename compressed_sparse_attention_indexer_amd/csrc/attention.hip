@@ -355,24 +355,34 @@ __global__ __launch_bounds__(128 * HG) void mqa_bf16_kernel(MqaArgs a) {
 }
 
 // Merge split partials with the sink, counted once (H = 64 or 128).
-// Workgroup = (16-head group hg, lane group g, query): each of its 256 threads (dh, dt pair p,
-// column e) holds heads 16hg + 4g + r (r = 0..3) at two dims of every
-// split's partial, one 16-byte vector per split.  Wave r first turns head
+// Workgroup = (16-head group hg, lane group g, dim part dq of Zq, query):
+// heads h0 .. h0 + 3 (h0 = 16hg + 4g) at 512 / Zq of the dims (Zq = 1, 2 or 4,
+// chosen so the launch has about 256 workgroups).  A 16-byte partial vector
+// holds those 4 heads at two dims; the part's 256 / Zq vector positions of a
+// split are spread over 256 / Zq threads (position: half dh, dt pair p,
+// column e), and thread group sg of Zq folds splits sg, sg + Zq, ... , so with
+// few queries every CU in the launch streams only a part of a head group's
+// partials.  Wave r first turns head
 // h0 + r's (m, l) pairs into per-split weights and the total (lanes over the
-// splits; wave max and sum), into LDS; meanwhile the partial vectors of the
-// first 16 splits are already in flight.  Then every thread folds its
-// vectors, the next batch's loads issued before the current batch is used.
-// Splits without rows (l = 0) get weight 0; their vectors (never written)
-// are not used.
+// splits; wave max and sum), into LDS, while the first partial vectors are
+// already in flight; then each thread group folds its splits (the next
+// batch's loads issued before the current batch is used), and the groups'
+// sums meet in LDS.  Splits without rows (l = 0) get weight 0; their vectors (never
+// written) are not used.
 constexpr int kCombineMaxSplits = 1024;
+template <int Zq>
 __global__ __launch_bounds__(256) void mqa_combine_kernel(MqaArgs a) {
     constexpr int kBatch = 16;
     __shared__ float s_w[kCombineMaxSplits][4];
     __shared__ float s_M[4], s_L[4];
-    const int qi = blockIdx.y;
+    __shared__ float s_acc[1536];  // (Zq - 1) groups x 8 sums x 256 / Zq positions
+    const int qi = blockIdx.y, dq = blockIdx.z;
     const int hg = blockIdx.x >> 2, g = blockIdx.x & 3;
     const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
-    const int dh = tid >> 7, p = (tid >> 4) & 7, e = tid & 15;
+    constexpr int npos = 256 / Zq;
+    const int sg = tid / npos, c = tid % npos;
+    const int pos = dq * npos + c;  // 0 .. 255 over the head group's 512 dims
+    const int dh = pos >> 7, p = (pos >> 4) & 7, e = pos & 15;
     const int lane = 16 * g + e;
     const int h0 = 16 * hg + 4 * g;
     const int S = a.n_splits;
@@ -380,18 +390,18 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(MqaArgs a) {
     const int Z = a.H / 64, z = hg >> 2, wave_l = 2 * (hg & 3) + dh;
     const u32x4_t *src = (const u32x4_t *)a.part_o + ((((size_t)qi * S * Z + z) * 8 + wave_l) * 8 + p) * 64 + lane;
     const size_t sstride = (size_t)Z * 8 * 8 * 64;  // vectors per split
+    // this thread group's splits: sg, sg + Zq, ...: n_mine of them
+    const int n_mine = S > sg ? (S - sg + Zq - 1) / Zq : 0;
     u32x4_t ov[2][kBatch];
-    auto load_batch = [&](u32x4_t (&v)[kBatch], int s0) {
+    auto load_batch = [&](u32x4_t (&v)[kBatch], int i0) {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            const int s = s0 + u < S ? s0 + u : S - 1;  // clamped: in bounds, unconditional
-            v[u] = src[s * sstride];
+            const int i = i0 + u < n_mine ? i0 + u : n_mine - 1;  // clamped: in bounds, unconditional
+            v[u] = src[(size_t)(sg + Zq * i) * sstride];
         }
     };
-    load_batch(ov[0], 0);
-    {  // weights of head h0 + wv
-        // (m, l) of split s = ln + 64 i: the first 64 splits' pairs stay in registers
-        // between the max and the weights (one read); further ones are read twice
+    if (n_mine > 0) load_batch(ov[0], 0);
+    {  // weights of head h0 + wv; the first 64 splits' (m, l) pairs stay in registers
         const float sink2 = a.sink[h0 + wv] * kLog2e;
         float2 ml0 = float2{0.f, 0.f};
         if (ln < S) ml0 = *(const float2 *)(a.part_ml + (((size_t)qi * S + ln) * a.H + h0 + wv) * 2);
@@ -422,13 +432,14 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(MqaArgs a) {
     }
     __syncthreads();
     float acc[4][2] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
-    auto fold = [&](const u32x4_t (&v)[kBatch], int s0) {
+    auto fold = [&](const u32x4_t (&v)[kBatch], int i0) {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            if (s0 + u >= S) break;
+            if (i0 + u >= n_mine) break;
+            const int s = sg + Zq * (i0 + u);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float w = s_w[s0 + u][r];
+                const float w = s_w[s][r];
                 if (w == 0.f) continue;  // also keeps unwritten partials out
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {  // dt = 2p + kk: word 2kk + r/2, half r%2
@@ -439,21 +450,33 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(MqaArgs a) {
             }
         }
     };
-    for (int s0 = 0; s0 < S; s0 += 2 * kBatch) {
-        if (s0 + kBatch < S) load_batch(ov[1], s0 + kBatch);
-        fold(ov[0], s0);
-        if (s0 + kBatch >= S) break;
-        if (s0 + 2 * kBatch < S) load_batch(ov[0], s0 + 2 * kBatch);
-        fold(ov[1], s0 + kBatch);
+    for (int i0 = 0; i0 < n_mine; i0 += 2 * kBatch) {
+        if (i0 + kBatch < n_mine) load_batch(ov[1], i0 + kBatch);
+        fold(ov[0], i0);
+        if (i0 + kBatch >= n_mine) break;
+        if (i0 + 2 * kBatch < n_mine) load_batch(ov[0], i0 + 2 * kBatch);
+        fold(ov[1], i0 + kBatch);
     }
+    // the groups' sums meet in group 0
+    if (sg > 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) s_acc[((sg - 1) * 8 + 2 * r + kk) * npos + c] = acc[r][kk];
+    }
+    __syncthreads();
+    if (sg != 0) return;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const float L = s_L[r];
         const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-            a.out[((size_t)qi * a.H + h0 + r) * kD + 256 * dh + 16 * (2 * p + kk) + e] = acc[r][kk] * inv;
-        if (a.lse && tid == 0) a.lse[(size_t)qi * a.H + h0 + r] = s_M[r] * kLn2 + logf(L);
+        for (int kk = 0; kk < 2; ++kk) {
+            float v = acc[r][kk];
+            for (int q = 1; q < Zq; ++q) v += s_acc[((q - 1) * 8 + 2 * r + kk) * npos + c];
+            a.out[((size_t)qi * a.H + h0 + r) * kD + 256 * dh + 16 * (2 * p + kk) + e] = v * inv;
+        }
+        if (a.lse && dq == 0 && tid == 0) a.lse[(size_t)qi * a.H + h0 + r] = s_M[r] * kLn2 + logf(L);
     }
 }
 
@@ -504,7 +527,17 @@ hipError_t launch_mqa(const MqaArgs &a, int dtype, hipStream_t stream) {
         return hipGetLastError();
     }
     hipLaunchKernelGGL(mqa_bf16_kernel<4>, dim3(a.n_splits, Q, a.H / 64), dim3(512), 0, stream, a);
-    if (a.n_splits > 1) hipLaunchKernelGGL(mqa_combine_kernel, dim3(a.H / 4, Q), dim3(256), 0, stream, a);
+    if (a.n_splits > 1) {
+        int zq = 1;  // dim parts of the combine: about 256 workgroups
+        while (zq < 4 && (long)Q * (a.H / 4) * zq * 2 <= 256) zq *= 2;
+        const dim3 grid(a.H / 4, Q, zq);
+        if (zq == 4)
+            hipLaunchKernelGGL(mqa_combine_kernel<4>, grid, dim3(256), 0, stream, a);
+        else if (zq == 2)
+            hipLaunchKernelGGL(mqa_combine_kernel<2>, grid, dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL(mqa_combine_kernel<1>, grid, dim3(256), 0, stream, a);
+    }
     return hipGetLastError();
 }
 
