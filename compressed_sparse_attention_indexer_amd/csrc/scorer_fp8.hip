@@ -21,13 +21,14 @@ namespace {
 constexpr int kF8WaveStep = 64;                        // entries per wave and step
 constexpr int kF8WgStep = kScoreWaves * kF8WaveStep;   // entries per workgroup step
 constexpr int kF8RowWords = 128 / 4 + 4;               // LDS row: 128 codes + 16 B pad
+constexpr int kF8Depth = 2;                            // wave-steps of loads in flight
 struct F8Raw {
     u32x4_t k[8];  // 64 rows x 128 bytes, 16 bytes per lane per load
     float ks;      // scale of the entry this lane stores
 };
 }  // namespace
 
-template <int kAct>
+template <int kAct, int kDepth>
 __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_fp8_kernel(ScoreArgs a) {
     __shared__ __attribute__((aligned(16))) uint32_t kraw[kScoreWaves][kF8WaveStep * kF8RowWords];
     const int qi = blockIdx.y;
@@ -111,13 +112,15 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_fp8_kernel(S
     };
 
     if (n_load > 0) {
-        F8Raw kbuf[2];
+        // kDepth steps in flight, unrolled so no load sits behind a branch; steps past the
+        // last one reload the last step and store nothing
+        F8Raw kbuf[kDepth];
         auto step = [&](int k) { return base0 + (k < n_load ? k : n_load - 1) * stride; };
-        load(kbuf[0], step(0));
-        load(kbuf[1], step(1));
-        for (int k = 0; k < n_load; k += 2) {
-            process(kbuf[0], step(k), k < n_load, step(k + 2));
-            process(kbuf[1], step(k + 1), k + 1 < n_load, step(k + 3));
+#pragma unroll
+        for (int i = 0; i < kDepth; ++i) load(kbuf[i], step(i));
+        for (int k = 0; k < n_load; k += kDepth) {
+#pragma unroll
+            for (int i = 0; i < kDepth; ++i) process(kbuf[i], step(k + i), k + i < n_load, step(k + i + kDepth));
         }
     }
     for (int k = n_load; k < n_steps; ++k) {  // steps past the visible entries: -inf
@@ -134,9 +137,9 @@ hipError_t launch_index_scores_fp8(const ScoreArgs &a, hipStream_t stream) {
     if (per_query < 1) per_query = 1;
     const dim3 grid(per_query, Q), block(64 * kScoreWaves);
     if (a.act == 0)
-        hipLaunchKernelGGL(index_scores_fp8_kernel<0>, grid, block, 0, stream, a);
+        hipLaunchKernelGGL((index_scores_fp8_kernel<0, kF8Depth>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL(index_scores_fp8_kernel<1>, grid, block, 0, stream, a);
+        hipLaunchKernelGGL((index_scores_fp8_kernel<1, kF8Depth>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
