@@ -89,10 +89,6 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(
     int nvis = visible_entries(a.seq_len[b], a.q_pos[qi], a.ratio);
     nvis = nvis < a.n_max ? nvis : a.n_max;
     const bool with_hist = kHist && nvis > a.K;  // same for the whole workgroup
-    if (with_hist) {
-        for (int i = threadIdx.x; i < kTopkBins; i += 64 * kScoreWaves) lh[i] = 0u;
-        __syncthreads();
-    }
     float *srow = a.scores + (size_t)qi * a.n_max;
 
     // A fragments: head 16*ht + e, dims 32s + 8g .. +8 for k-step s.
@@ -180,15 +176,22 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(
         if (with_hist) lds_hist_add(lh, order_key(sv) >> 20, live && g < 2 && j < nvis);
     };
 
+    // Software pipeline kDepth steps deep, unrolled by kDepth so that no load
+    // sits behind a branch: while step k computes, the loads of steps k+1 ..
+    // k+kDepth-1 are in flight.  Steps past the last one reload the last step
+    // and store nothing.  The histogram is cleared while the first loads are
+    // out (its barrier is reached by every wave, with or without steps).
+    KeyRaw kbuf[kDepth];
+    auto step = [&](int k) { return base0 + (k < n_load ? k : n_load - 1) * stride; };
     if (n_load > 0) {
-        // Software pipeline kDepth steps deep, unrolled by kDepth so that no
-        // load sits behind a branch: while step k computes, the loads of steps
-        // k+1 .. k+kDepth-1 are in flight.  Steps past the last one reload the
-        // last step and store nothing.
-        KeyRaw kbuf[kDepth];
-        auto step = [&](int k) { return base0 + (k < n_load ? k : n_load - 1) * stride; };
 #pragma unroll
         for (int i = 0; i < kDepth; ++i) load(kbuf[i], step(i));
+    }
+    if (with_hist) {
+        for (int i = threadIdx.x; i < kTopkBins; i += 64 * kScoreWaves) lh[i] = 0u;
+        __syncthreads();
+    }
+    if (n_load > 0) {
         for (int k = 0; k < n_load; k += kDepth) {
 #pragma unroll
             for (int i = 0; i < kDepth; ++i) {
