@@ -36,24 +36,46 @@ __device__ __forceinline__ RowList make_rows(const MqaArgs &a, int qi) {
     return r;
 }
 
+// One sequence's cache bases (v / win_v null when key and value share a row).
 template <typename T>
-__device__ __forceinline__ void row_ptrs(const MqaArgs &a, int qi, const RowList &rl, int i,
-                                         const T **kp, const T **vp) {
+struct SeqRows {
+    const T *kv, *v, *win, *win_v;
+    int win_pos0;
+};
+
+template <typename T>
+__device__ __forceinline__ SeqRows<T> seq_rows(const MqaArgs &a, int qi) {
     const int b = qi / a.T;
+    return SeqRows<T>{(const T *)a.kv[b], a.v ? (const T *)a.v[b] : nullptr, (const T *)a.win[b],
+                      a.win_v ? (const T *)a.win_v[b] : nullptr, a.win_pos0[b]};
+}
+
+// Key and value pointers of row i (null if the row is not attended), from the
+// sequence's bases; `jl` is the row's list value when the caller has already
+// read it (selected rows), else -2 to read it here.
+template <typename T>
+__device__ __forceinline__ void row_ptrs(const MqaArgs &a, const SeqRows<T> &sq, int qi, const RowList &rl, int i,
+                                         const T **kp, const T **vp, int jl = -2) {
     *kp = nullptr;
     *vp = nullptr;
     if (i < 0 || i >= rl.n_rows) return;
     if (i < rl.n_sel) {
-        const int j = a.topk_idx ? a.topk_idx[(size_t)qi * a.K + i] : i;
+        const int j = !a.topk_idx ? i : jl != -2 ? jl : a.topk_idx[(size_t)qi * a.K + i];
         if (j < 0 || j >= rl.n_ent) return;
-        *kp = (const T *)a.kv[b] + (size_t)j * a.D;
-        *vp = a.v ? (const T *)a.v[b] + (size_t)j * a.D : *kp;
+        *kp = sq.kv + (size_t)j * a.D;
+        *vp = sq.v ? sq.v + (size_t)j * a.D : *kp;
     } else {
         const int pos = rl.wlo + (i - rl.n_sel);
-        const size_t off = (size_t)(pos - a.win_pos0[b]) * a.D;
-        *kp = (const T *)a.win[b] + off;
-        *vp = a.win_v ? (const T *)a.win_v[b] + off : *kp;
+        const size_t off = (size_t)(pos - sq.win_pos0) * a.D;
+        *kp = sq.win + off;
+        *vp = sq.win_v ? sq.win_v + off : *kp;
     }
+}
+
+template <typename T>
+__device__ __forceinline__ void row_ptrs(const MqaArgs &a, int qi, const RowList &rl, int i, const T **kp,
+                                         const T **vp) {
+    row_ptrs(a, seq_rows<T>(a, qi), qi, rl, i, kp, vp);
 }
 
 }  // namespace
@@ -177,12 +199,10 @@ __global__ __launch_bounds__(128 * HG) void mqa_bf16_kernel(MqaArgs a) {
     const int e = lane & 15, g = lane >> 4;
     const int hg = wave >> 1, dh = wave & 1;
     const int h_off = 64 * blockIdx.z;  // this workgroup's 64 heads: h_off .. h_off + 63
-    const RowList rl = make_rows(a, qi);
-    const int r0 = split * a.rows_per_split;
-    const int r1 = r0 + a.rows_per_split < rl.n_rows ? r0 + a.rows_per_split : rl.n_rows;
-    const int ntiles = r1 > r0 ? (r1 - r0 + kTile - 1) / kTile : 0;
-    const float scale2 = a.scale * kLog2e;
-
+    // q, the sequence's cache bases and the first tile's list value of this
+    // thread's staging row are read in the same round as the query's row counts
+    // (i < K is inside the top-k list whatever the counts; the row itself is
+    // checked once they are known).
     // B fragments of Q^T: head 16hg + e, dims 256dh + 32ks + 8g .. +8.
     bf16x8_t qf[8];
     {
@@ -190,6 +210,15 @@ __global__ __launch_bounds__(128 * HG) void mqa_bf16_kernel(MqaArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8_t *)(qrow + 32 * ks);
     }
+    const SeqRows<uint16_t> sq = seq_rows<uint16_t>(a, qi);
+    const int srow0 = wave * RPW + lane / LPR;
+    const int i_first = split * a.rows_per_split + srow0;
+    const int j_first = a.topk_idx && i_first < a.K ? a.topk_idx[(size_t)qi * a.K + i_first] : -2;
+    const RowList rl = make_rows(a, qi);
+    const int r0 = split * a.rows_per_split;
+    const int r1 = r0 + a.rows_per_split < rl.n_rows ? r0 + a.rows_per_split : rl.n_rows;
+    const int ntiles = r1 > r0 ? (r1 - r0 + kTile - 1) / kTile : 0;
+    const float scale2 = a.scale * kLog2e;
 
     f32x4_t o[16];
 #pragma unroll
@@ -209,7 +238,8 @@ __global__ __launch_bounds__(128 * HG) void mqa_bf16_kernel(MqaArgs a) {
     const uint16_t *dummy = (const uint16_t *)a.q + (size_t)qi * a.H * kD;
     auto fetch = [&](int t) {
         const uint16_t *kp, *vp;
-        row_ptrs(a, qi, rl, r0 + t * kTile + srow < r1 ? r0 + t * kTile + srow : -1, &kp, &vp);
+        row_ptrs(a, sq, qi, rl, r0 + t * kTile + srow < r1 ? r0 + t * kTile + srow : -1, &kp, &vp,
+                 t == 0 ? j_first : -2);
         have_row = kp != nullptr;
         if (!have_row) kp = vp = dummy;
 #pragma unroll

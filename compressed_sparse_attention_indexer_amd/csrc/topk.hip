@@ -464,6 +464,9 @@ __global__ __launch_bounds__(kWG) void topk_onekernel_kernel(TopkArgs a) {
 // [0] above count (0xFFFFFFFF when a list overflowed or there is no usable
 // threshold), [1] candidate count, then the above list, candidate keys and
 // candidate indices.
+// kVec: the rows are 16-byte aligned and n_max is a multiple of 4 (whole
+// 16-byte score loads; decided on the host, so the loads need no branch).
+template <bool kVec>
 __global__ __launch_bounds__(kAuxThreads) void topk_filter_kernel(TopkArgs a) {
     __shared__ int32_t l_above[kFltAboveCap];
     __shared__ uint32_t l_ckey[kFltCandCap];
@@ -472,17 +475,34 @@ __global__ __launch_bounds__(kAuxThreads) void topk_filter_kernel(TopkArgs a) {
     __shared__ uint32_t s_hist[kTopkWin];
     __shared__ int s_red[4];
     const int qi = blockIdx.y;
-    const int n = query_visible(a, qi);
     const int j0 = blockIdx.x * kTopkAuxChunk;
-    if (n <= a.K || j0 >= n) return;  // the selection reads regions below n only
     uint32_t *reg = a.flt + ((size_t)qi * gridDim.x + blockIdx.x) * kFltRegionWords;
     const float *row = a.scores + (size_t)qi * a.n_max;
-    const bool vec = (a.n_max & 3) == 0 && ((uintptr_t)a.scores & 15) == 0;
     const int j_first = j0 + kPerThread * threadIdx.x;  // this thread's consecutive scores
+    // The chunk's scores and the histogram windows are read in the same round as the
+    // query's visible count (both stay inside their arrays whatever the count); the
+    // scores past the count are zeroed once it is known, and a workgroup with nothing to
+    // do leaves after the window merge (whose result it then ignores).
+    const int seq_len = a.seq_len[qi / a.T], q_pos = a.q_pos[qi];  // read now, used after the merge
     float x[kPerThread];
-    load_chunk<kPerThread>(row, j_first, n, a.n_max, vec, x);
+    if (kVec) {  // n_max % 4 == 0, so a chunk starting inside the row ends inside it
+        const int jf = j_first < a.n_max ? j_first : a.n_max - kPerThread;
+#pragma unroll
+        for (int k = 0; k < kPerThread; k += 4) {
+            const float4 f = *(const float4 *)(row + jf + k);
+            x[k] = f.x, x[k + 1] = f.y, x[k + 2] = f.z, x[k + 3] = f.w;
+        }
+    } else {
+        load_chunk<kPerThread>(row, j_first, a.n_max, a.n_max, false, x);
+    }
     const uint32_t bin = window_threshold(a.win_hdr + (size_t)qi * a.n_win,
                                           a.win_cnt + (size_t)qi * a.n_win * kTopkWin, a.n_win, a.K, s_red, s_hist);
+    const int nv = visible_entries(seq_len, q_pos, a.ratio);
+    const int n = nv < a.n_max ? nv : a.n_max;
+    if (n <= a.K || j0 >= n) return;  // the selection reads regions below n only
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k)
+        if (j_first + k >= n) x[k] = 0.f;
     if (bin == kNoBin) {
         if (threadIdx.x == 0) reg[0] = 0xFFFFFFFFu;
         return;
@@ -519,10 +539,35 @@ __global__ __launch_bounds__(kWG) void topk_final_kernel(TopkArgs a, int n_flt) 
     __shared__ int s_bad;
     const int qi = blockIdx.x;
     const int tid = threadIdx.x;
-    const int n = query_visible(a, qi);
     const int K = a.K;
     const float *row = a.scores + (size_t)qi * a.n_max;
     int32_t *out = a.idx + (size_t)qi * K;
+    // Gather the filter lists of the workgroups that covered visible entries,
+    // kFinalGroup threads per region.  One round loads every header together
+    // with the first entries of each list (lists are short: a few entries per
+    // region in practice); whatever lies beyond takes one more round.  The
+    // first pass's loads go out with the query's visible count (they stay
+    // inside the regions this launch has; regions past the count are ignored).
+    const uint32_t *reg0 = a.flt + (size_t)qi * n_flt * kFltRegionWords;
+    constexpr int kRegPer = kWG / kFinalGroup;  // regions per pass
+    const int u = tid % kFinalGroup;
+    struct RegionHead {
+        uint32_t na, nc, sa, sck[kSpecC], sci[kSpecC];
+    };
+    auto load_head = [&](int r, RegionHead &h) {
+        const uint32_t *reg = reg0 + (size_t)r * kFltRegionWords;
+        h.na = reg[0];
+        h.nc = reg[1];
+        h.sa = reg[2 + u];
+#pragma unroll
+        for (int k = 0; k < kSpecC; ++k) {
+            h.sck[k] = reg[2 + kFltAboveCap + u + kFinalGroup * k];
+            h.sci[k] = reg[2 + kFltAboveCap + kFltCandCap + u + kFinalGroup * k];
+        }
+    };
+    RegionHead h0;
+    load_head(min(tid / kFinalGroup, n_flt - 1), h0);
+    const int n = query_visible(a, qi);
     if (n <= K) {
         for (int i = tid; i < K; i += kWG) out[i] = i < n ? i : -1;
         return;
@@ -530,27 +575,18 @@ __global__ __launch_bounds__(kWG) void topk_final_kernel(TopkArgs a, int n_flt) 
     bool ok = true;
     if (tid == 0) s_bad = 0;
     __syncthreads();
-    // Gather the filter lists of the workgroups that covered visible entries,
-    // kFinalGroup threads per region.  One round loads every header together
-    // with the first entries of each list (lists are short: a few entries per
-    // region in practice); whatever lies beyond takes one more round.
     const int n_reg = (n + kTopkAuxChunk - 1) / kTopkAuxChunk;
-    const uint32_t *reg0 = a.flt + (size_t)qi * n_flt * kFltRegionWords;
-    constexpr int kRegPer = kWG / kFinalGroup;  // regions per pass
-    const int u = tid % kFinalGroup;
     int na_tot = 0, nc_tot = 0;
     for (int r0 = 0; r0 < n_reg; r0 += kRegPer) {
         const int r = r0 + tid / kFinalGroup;
         const bool live = r < n_reg;
+        RegionHead hd;
+        if (r0 == 0)
+            hd = h0;
+        else
+            load_head(live ? r : r0, hd);
         const uint32_t *reg = reg0 + (size_t)(live ? r : r0) * kFltRegionWords;
-        uint32_t na = reg[0], nc = reg[1];
-        uint32_t sa = reg[2 + u];
-        uint32_t sck[kSpecC], sci[kSpecC];
-#pragma unroll
-        for (int k = 0; k < kSpecC; ++k) {
-            sck[k] = reg[2 + kFltAboveCap + u + kFinalGroup * k];
-            sci[k] = reg[2 + kFltAboveCap + kFltCandCap + u + kFinalGroup * k];
-        }
+        uint32_t na = hd.na, nc = hd.nc;
         if (!live) na = nc = 0;
         if (na > (uint32_t)kFltAboveCap || nc > (uint32_t)kFltCandCap) {
             s_bad = 1;  // overflowed or unusable region: the exact path runs
@@ -561,13 +597,13 @@ __global__ __launch_bounds__(kWG) void topk_final_kernel(TopkArgs a, int n_flt) 
         // this region's list offsets: the scan value of its first thread
         const int base = __shfl(pre, (tid & 63) & ~(kFinalGroup - 1));
         const int pa = na_tot + (base & 0xFFFF), pc = nc_tot + (base >> 16);
-        if ((uint32_t)u < na && pa + u < K) v[pa + u] = (int32_t)sa;
+        if ((uint32_t)u < na && pa + u < K) v[pa + u] = (int32_t)hd.sa;
 #pragma unroll
         for (int k = 0; k < kSpecC; ++k) {
             const int i = u + kFinalGroup * k;
             if ((uint32_t)i < nc && pc + i < kTopkCand) {
-                c_key[pc + i] = sck[k];
-                c_idx[pc + i] = (int32_t)sci[k];
+                c_key[pc + i] = hd.sck[k];
+                c_idx[pc + i] = (int32_t)hd.sci[k];
             }
         }
         for (int i = kFinalGroup + u; i < (int)na; i += kFinalGroup)  // beyond the first round
@@ -656,7 +692,10 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t stream, bool hist_done) {
         return hipGetLastError();
     }
     const int nf = n_filters(a.n_max);
-    hipLaunchKernelGGL(topk_filter_kernel, dim3(nf, Q), dim3(kAuxThreads), 0, stream, a);
+    if ((a.n_max & 3) == 0 && ((uintptr_t)a.scores & 15) == 0 && a.n_max >= kPerThread)
+        hipLaunchKernelGGL(topk_filter_kernel<true>, dim3(nf, Q), dim3(kAuxThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(topk_filter_kernel<false>, dim3(nf, Q), dim3(kAuxThreads), 0, stream, a);
     hipLaunchKernelGGL(topk_final_kernel, dim3(Q), dim3(kWG), 0, stream, a, nf);
     return hipGetLastError();
 }

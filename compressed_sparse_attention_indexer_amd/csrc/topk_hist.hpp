@@ -62,8 +62,6 @@ __device__ __forceinline__ uint32_t window_threshold(const int32_t *hdr, const u
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nt = blockDim.x, nwaves = nt >> 6, per_pass = nt >> 2;
     const int seg = tid & 3;
-    int m = -1;
-    for (int w = tid; w < n_win; w += nt) m = max(m, hdr[w]);
     constexpr int kPerSeg = kTopkWin / 4;  // counts per thread of a window
     constexpr int kVecs = kPerSeg / 4;
     int mw = -1;
@@ -77,7 +75,9 @@ __device__ __forceinline__ uint32_t window_threshold(const int32_t *hdr, const u
             for (int i = 0; i < kVecs; ++i) x[i] = src[i];
         }
     };
-    load_window(tid >> 2);
+    load_window(tid >> 2);  // issued before the header maximum below waits for its loads
+    int m = -1;
+    for (int w = tid; w < n_win; w += nt) m = max(m, hdr[w]);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) m = max(m, __shfl_xor(m, o));
     if (lane == 0) s_red[wave] = m;
