@@ -147,6 +147,7 @@ def _topk_case(n_vis_list, n_max, K, seed, ties=False):
     ([40000, 33000], 40000, 512, False),
     ([262144, 200000, 300, 262144], 262144, 512, True),
     ([262144], 262144, 1, False),
+    ([70001, 65537], 70001, 512, True),  # many-workgroup path with a row length that is not a multiple of 4
 ])
 def test_topk_exact(n_vis, n_max, K, ties):
     say(f"[case] topk n_vis={n_vis} n_max={n_max} K={K} ties={ties}")
