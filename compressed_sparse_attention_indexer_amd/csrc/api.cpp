@@ -96,9 +96,11 @@ float scale_of(const csa_dims *d) {
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Histogram windows come from the bf16 scorer in the fused call (one per scorer
-// workgroup) and from the top-k's own histogram kernel otherwise.
+// workgroup, or per entry chunk of the tiled scorer) and from the top-k's own
+// histogram kernel otherwise (0 here).
 int win_count(const csa_dims *d, bool fused) {
-    if (!fused || d->dtype != CSA_BF16 || csa::score_uses_tiles(csa::kBF16, d->q_len)) return 0;
+    if (!fused || d->dtype != CSA_BF16) return 0;
+    if (csa::score_uses_tiles(csa::kBF16, d->q_len)) return csa::tiled_windows(d->batch, d->q_len, d->max_entries);
     return csa::score_workgroups(d->max_entries, n_queries(d));
 }
 size_t ws_topk(const csa_dims *d, bool fused = false) {
@@ -484,8 +486,7 @@ csa_status csa_attention(const csa_dims *d, const void *q, const void *q_idx, co
     const csa::TopkArgs ta = topk_args(d, scores, seq_len, q_pos, idx, base + off_topk, true);
     csa::ScoreArgs sa = score_args(d, q_idx, w, k_idx, seq_len, q_pos, scores);
     // the bf16 scorer also writes the top-k key-histogram windows while it writes the scores
-    const bool fused_hist = d->dtype == CSA_BF16 && csa::topk_uses_histogram(d->max_entries) &&
-                            !csa::score_uses_tiles(csa::kBF16, d->q_len);
+    const bool fused_hist = csa::topk_uses_histogram(d->max_entries) && win_count(d, true) > 0;
     if (fused_hist) {
         sa.win_hdr = ta.win_hdr;
         sa.win_cnt = ta.win_cnt;

@@ -32,8 +32,10 @@ hipError_t launch_index_scores(const ScoreArgs &a, int dtype, hipStream_t stream
 // fp8 (E4M3) index queries and keys with per-row scales, HI = 64, DI = 128
 hipError_t launch_index_scores_fp8(const ScoreArgs &a, hipStream_t stream);
 int score_workgroups(int n_max, int n_queries);  // bf16 scorer workgroups per query
-// many queries per sequence: the GEMM-tiled scorer (it writes no histogram windows)
+// many queries per sequence: the GEMM-tiled scorer
 bool score_uses_tiles(int dtype, int T);
+// histogram windows per query the tiled scorer can write (its entry chunks), 0 if it cannot
+int tiled_windows(int B, int T, int n_max);
 
 constexpr int kTopkSmallMax = 4096;       // rows up to this length: one workgroup, row kept in LDS
 constexpr int kTopkOneKernelMax = 65536;  // rows up to this length: threshold+scan+select in one kernel

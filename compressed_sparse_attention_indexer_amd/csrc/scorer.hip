@@ -262,10 +262,21 @@ static TiledPlan tiled_plan(const ScoreArgs &a) {
     return p;
 }
 
-template <int kAct>
+template <int kAct, bool kHist>
 __global__ __launch_bounds__(64 * kPfWaves, 1) void index_scores_tiled_kernel(ScoreArgs a, TiledPlan pl) {
+    static_assert(!kHist || kPfQW == 1, "one histogram per wave holds one query");
     __shared__ __attribute__((aligned(16))) uint32_t kt[2][kPfTileWords];
     __shared__ int s_nv[kPfWaves];
+    // Optional top-k key-histogram window of each wave's query over this
+    // workgroup's chunk.  Only the kTopkWin bins at and below the highest bin
+    // seen so far (m_top, the same in every lane) are kept, as lane-private
+    // counters: bin m_top - o of lane l is word 64 * o + l, so the 64 lanes of
+    // an add touch 64 different banks and never wait on one another.  A score
+    // above m_top is held back in a register until the end of its tile; then
+    // every lane shifts its counters down by the rise and adds what it held.
+    // The 64-entry groups themselves stay free of branches.
+    __shared__ uint32_t lh[kHist ? kPfWaves : 1][kHist ? kTopkWin * 64 : 1];
+    int m_top = -1;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int e = lane & 15, g = lane >> 4;
 
@@ -313,6 +324,10 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void index_scores_tiled_kernel(Sc
             for (int r = 0; r < 4; ++r) wr[q][ht][r] = a.w[(size_t)qi[q] * kHI + 16 * ht + 4 * g + r];
         }
     }
+    const bool with_hist = kHist && qok[0] && nv[0] > a.K;  // one query per wave: its own histogram
+    if (kHist) {
+        for (int i = tid; i < kPfWaves * kTopkWin * 64; i += 64 * kPfWaves) (&lh[0][0])[i] = 0u;
+    }
     __syncthreads();
     int nv_max = 0;
 #pragma unroll
@@ -350,6 +365,7 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void index_scores_tiled_kernel(Sc
         stash(buf);
         if (tile + 1 < n_ct) fetch(tile + 1);
         __syncthreads();
+        int held[kPfTile / 64];  // per group: a bin above m_top, else -1
 #pragma unroll
         for (int grp = 0; grp < kPfTile / 64; ++grp) {  // 64 entries: one butterfly and store
             float p[kPfQW][4];
@@ -390,6 +406,32 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void index_scores_tiled_kernel(Sc
                 const LanePair pr = pair16(k2[0], k2[1]);  // lane group lo keeps k2[lo]
                 const float tot = pr.lo + pr.hi;
                 if (qok[q] && j < a.n_max) a.scores[(size_t)qi[q] * a.n_max + j] = j < nv[q] ? tot : -INFINITY;
+                if (kHist) {
+                    const bool v = with_hist && j < nv[q];
+                    const int bin = (int)(order_key(tot) >> 20);
+                    const bool up = v && bin > m_top;
+                    held[grp] = up ? bin : -1;
+                    const int o = m_top - bin;
+                    const bool in = v && !up && o < kTopkWin;
+                    atomicAdd(&lh[wave][64 * (in ? o : 0) + lane], in ? 1u : 0u);
+                }
+            }
+        }
+        if (kHist) {
+            int hm = held[0];
+#pragma unroll
+            for (int g2 = 1; g2 < kPfTile / 64; ++g2) hm = max(hm, held[g2]);
+            if (__ballot(hm > m_top)) {  // the top bin rose in this tile (rare after the first)
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) hm = max(hm, __shfl_xor(hm, o));
+                const int d = hm - m_top;
+                uint32_t *hw = &lh[wave][lane];
+#pragma unroll
+                for (int o = kTopkWin - 1; o >= 0; --o) hw[64 * o] = o >= d ? hw[64 * (o - d)] : 0u;
+                m_top = hm;
+#pragma unroll
+                for (int g2 = 0; g2 < kPfTile / 64; ++g2)
+                    if (held[g2] >= 0 && m_top - held[g2] < kTopkWin) hw[64 * (m_top - held[g2])] += 1u;
             }
         }
     }
@@ -398,6 +440,22 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void index_scores_tiled_kernel(Sc
 #pragma unroll
         for (int q = 0; q < kPfQW; ++q)
             if (qok[q]) a.scores[(size_t)qi[q] * a.n_max + jj] = -INFINITY;
+    if (kHist) __syncthreads();  // the wave's histogram atomics are done before it is read
+    if (with_hist) {
+        // the chunk's window as the top-k expects it: hdr = highest non-empty bin
+        // M (-1 if none), cnt[t] = count of bin M - (kTopkWin - 1) + t.  Lane t
+        // sums counter kTopkWin - 1 - t over all lanes, starting at its own
+        // lane so that the 32 reads of a step fall into 32 banks.
+        const size_t w = (size_t)qi[0] * pl.n_chunks + ec;
+        if (lane < kTopkWin) {
+            const uint32_t *row = &lh[wave][64 * (kTopkWin - 1 - lane)];
+            uint32_t c = 0;
+#pragma unroll 16
+            for (int k = 0; k < 64; ++k) c += row[(k + lane) & 63];
+            a.win_cnt[w * kTopkWin + lane] = m_top - (kTopkWin - 1) + lane >= 0 ? c : 0u;
+        }
+        if (lane == 0) a.win_hdr[w] = m_top;
+    }
 }
 
 bool score_uses_tiles(int dtype, int T) { return dtype == kBF16 && T >= kPfQueries; }
@@ -412,11 +470,19 @@ hipError_t launch_index_scores(const ScoreArgs &a, int dtype, hipStream_t stream
     }
     if (score_uses_tiles(dtype, a.T)) {
         const TiledPlan pl = tiled_plan(a);
-        const dim3 grid(a.B * pl.qb_per_seq * pl.n_chunks);
-        if (a.act == 0)
-            hipLaunchKernelGGL(index_scores_tiled_kernel<0>, grid, dim3(64 * kPfWaves), 0, stream, a, pl);
-        else
-            hipLaunchKernelGGL(index_scores_tiled_kernel<1>, grid, dim3(64 * kPfWaves), 0, stream, a, pl);
+        const dim3 grid(a.B * pl.qb_per_seq * pl.n_chunks), block(64 * kPfWaves);
+        const bool hist = a.win_hdr != nullptr;  // the caller sized the windows with tiled_windows
+        if (a.act == 0) {
+            if (hist)
+                hipLaunchKernelGGL((index_scores_tiled_kernel<0, true>), grid, block, 0, stream, a, pl);
+            else
+                hipLaunchKernelGGL((index_scores_tiled_kernel<0, false>), grid, block, 0, stream, a, pl);
+        } else {
+            if (hist)
+                hipLaunchKernelGGL((index_scores_tiled_kernel<1, true>), grid, block, 0, stream, a, pl);
+            else
+                hipLaunchKernelGGL((index_scores_tiled_kernel<1, false>), grid, block, 0, stream, a, pl);
+        }
         return hipGetLastError();
     }
     dim3 grid(score_workgroups(a.n_max, Q), Q);
@@ -434,6 +500,14 @@ hipError_t launch_index_scores(const ScoreArgs &a, int dtype, hipStream_t stream
             hipLaunchKernelGGL((index_scores_bf16_kernel<1, false, kScoreDepth>), grid, block, 0, stream, a);
     }
     return hipGetLastError();
+}
+
+int tiled_windows(int B, int T, int n_max) {
+    ScoreArgs a{};
+    a.B = B;
+    a.T = T;
+    a.n_max = n_max;
+    return tiled_plan(a).n_chunks;
 }
 
 int score_workgroups(int n_max, int n_queries) {

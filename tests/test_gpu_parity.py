@@ -318,6 +318,27 @@ def test_prefill_chunk_no_activation():
     check_whole_step(make_case_with_lens(wl, sl), ATT_TOL_BF16, act=csa.CSA_ACT_NONE)
 
 
+@pytest.mark.parametrize("lens,T,q_pos0", [
+    ([4 * 20000 + 3], 300, 4 * 20000 + 3 - 300),     # many queries: one selecting workgroup each
+    ([4 * 6000 + 1, 4 * 9000 + 2], 40, 2030),        # visible counts cross K inside the chunk
+    ([4 * 70000], 16, 4 * 70000 - 16),               # long rows, few queries: filter and final kernels
+])
+def test_prefill_fused_selection_equals_standalone_topk(lens, T, q_pos0):
+    """The tiled scorer builds the key histograms for the selection while it
+    writes the scores; the selection must equal the top-k kernel run alone
+    (its own histogram pass) and the oracle's top-k on the same scores."""
+    wl, sl = flash_case(f"prefill_fused_{len(lens)}_{T}", lens, q_len=T, q_pos0=q_pos0)
+    case = make_case_with_lens(wl, sl)
+    say(f"[case] {wl.name} B={wl.batch} T={T} max_entries={case.max_entries}")
+    dc = DeviceCase(case)
+    g_scores, g_idx, g_out, g_lse = run_fused(dc)
+    assert np.isfinite(g_out).all() and np.isfinite(g_lse).all()
+    t_idx = _np(csa.csa_topk_select(dc.csa_dims(), torch.from_numpy(g_scores).cuda(), dc.seq_len, dc.q_pos))
+    np.testing.assert_array_equal(t_idx, g_idx)
+    want = oracle.topk(g_scores, case.seq_len, case.q_pos, ratio=4, k=512)
+    np.testing.assert_array_equal(g_idx, want)
+
+
 # --------------------------------------------------------------------------- full-size workloads
 
 def test_decode_b1_64k_full():
