@@ -144,8 +144,13 @@ __global__ __launch_bounds__(256) void mqa_f32_kernel(MqaArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 split-K MFMA kernel, D = 512, 16 * HG heads per workgroup (HG = 4: 64
-// heads; 128 heads take two workgroups, blockIdx.z picking the half).
+// bf16 split-K MFMA kernel, D = 512, 16 * HG heads per workgroup (launched
+// with HG = 2: 32 heads, blockIdx.z picking the head group, so 64 heads take two
+// workgroups and 128 heads four).  With 4-wave workgroups two of them share a
+// CU (launch bounds ask for it: VGPRs stay at or below 256); their tiles'
+// barrier phases (staging, QK, the logit exchange, softmax, PV) then overlap
+// instead of running in lockstep, which took the decode step's attention from
+// 10.8 to 8.7 us against one 8-wave workgroup of 64 heads per CU.
 //
 // Workgroup = one (query, split): 2*HG waves; wave (hg, dh) owns heads
 // [16hg, 16hg+16) and output dims [256dh, 256dh+256).  Rows stream through
@@ -181,8 +186,8 @@ __device__ __forceinline__ v4i16_t lds_read_tr16(const uint16_t *p) {
 }
 }  // namespace
 
-template <int HG>
-__global__ __launch_bounds__(128 * HG) void mqa_bf16_kernel(MqaArgs a) {
+template <int HG, bool kSepV>
+__global__ __launch_bounds__(128 * HG, 2) void mqa_bf16_kernel(MqaArgs a) {
     constexpr int NW = 2 * HG;                // waves
     constexpr int RPW = kTile / NW;           // staged rows per wave
     constexpr int LPR = 64 / RPW;             // lanes per staged row
@@ -190,7 +195,7 @@ __global__ __launch_bounds__(128 * HG) void mqa_bf16_kernel(MqaArgs a) {
     static_assert(kTile % NW == 0 && 64 % RPW == 0, "staging layout");
 
     __shared__ __attribute__((aligned(16))) uint16_t krow[kTile * kKrowStride];
-    __shared__ __attribute__((aligned(16))) uint16_t vrow_sep[kTile * kKrowStride];  // separate values only
+    __shared__ __attribute__((aligned(16))) uint16_t vrow_sep[kSepV ? kTile * kKrowStride : 8];  // separate values only
     __shared__ float xs[NW][8][64];
     __shared__ int rowok[kTile];
 
@@ -198,7 +203,7 @@ __global__ __launch_bounds__(128 * HG) void mqa_bf16_kernel(MqaArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int e = lane & 15, g = lane >> 4;
     const int hg = wave >> 1, dh = wave & 1;
-    const int h_off = 64 * blockIdx.z;  // this workgroup's 64 heads: h_off .. h_off + 63
+    const int h_off = 16 * HG * blockIdx.z;  // this workgroup's heads: h_off .. h_off + 16 HG - 1
     // q, the sequence's cache bases and the first tile's list value of this
     // thread's staging row are read in the same round as the query's row counts
     // (i < K is inside the top-k list whatever the counts; the row itself is
@@ -230,8 +235,7 @@ __global__ __launch_bounds__(128 * HG) void mqa_bf16_kernel(MqaArgs a) {
     // the LDS writes covers 256 contiguous bytes)
     const int srow = wave * RPW + lane / LPR;
     const int cg = lane % LPR;
-    const bool separate_v = a.v != nullptr || a.win_v != nullptr;
-    u32x4_t kreg[CPL], vreg[CPL];
+    u32x4_t kreg[CPL], vreg[kSepV ? CPL : 1];
     bool have_row = false;
     // a missing row (padding, out of range, past the list) reads this query's q
     // instead: finite values whose logit is masked to -inf, so its weight is 0
@@ -246,7 +250,7 @@ __global__ __launch_bounds__(128 * HG) void mqa_bf16_kernel(MqaArgs a) {
         for (int c = 0; c < CPL; ++c) {
             const int ch = cg + LPR * c;
             kreg[c] = *as_global<u32x4_t>(kp + 8 * ch);
-            if (separate_v) vreg[c] = *as_global<u32x4_t>(vp + 8 * ch);
+            if (kSepV) vreg[c] = *as_global<u32x4_t>(vp + 8 * ch);
         }
     };
     if (ntiles > 0) fetch(0);
@@ -257,7 +261,7 @@ __global__ __launch_bounds__(128 * HG) void mqa_bf16_kernel(MqaArgs a) {
         for (int c = 0; c < CPL; ++c) {
             const int ch = cg + LPR * c;
             *(u32x4_t *)&krow[srow * kKrowStride + 8 * ch] = kreg[c];
-            if (separate_v) *(u32x4_t *)&vrow_sep[srow * kKrowStride + 8 * ch] = vreg[c];
+            if (kSepV) *(u32x4_t *)&vrow_sep[srow * kKrowStride + 8 * ch] = vreg[c];
         }
         if (cg == 0) rowok[srow] = have_row;
         if (t + 1 < ntiles) fetch(t + 1);
@@ -320,7 +324,7 @@ __global__ __launch_bounds__(128 * HG) void mqa_bf16_kernel(MqaArgs a) {
             ph[v] = (__bf16)pv[v];
             pl[v] = (__bf16)(pv[v] - (float)ph[v]);
         }
-        const uint16_t *vrow = separate_v ? vrow_sep : krow;
+        const uint16_t *vrow = kSepV ? vrow_sep : krow;
         const int s16 = lane & 15;  // this lane's address role in the transposing read
         // PV over this wave's 256 output dims.
 #pragma unroll
@@ -354,8 +358,9 @@ __global__ __launch_bounds__(128 * HG) void mqa_bf16_kernel(MqaArgs a) {
     } else {
         // Partial of this split: (m, l) per head, and O / l in fp16 stored the
         // way the MFMA tiles lie in registers: the 16-byte vector at
-        // [qi, split, wave, dt pair p, lane] holds heads 16hg + 4g + r
-        // (r = 0..3) at dims 256dh + 16dt + e for dt = 2p and 2p + 1.
+        // [qi, split, head group, dh, dt pair p, lane] (head group = the
+        // query's 16-head group h_off / 16 + hg, whatever HG is) holds heads
+        // 16hg + 4g + r (r = 0..3) at dims 256dh + 16dt + e for dt = 2p and 2p + 1.
         const size_t ps = (size_t)qi * a.n_splits + split;
         if (dh == 0 && g == 0) {
             a.part_ml[(ps * a.H + h_off + 16 * hg + e) * 2 + 0] = m_run;
@@ -416,7 +421,8 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(MqaArgs a) {
     const int lane = 16 * g + e;
     const int h0 = 16 * hg + 4 * g;
     const int S = a.n_splits;
-    // partial vectors: [qi, split, head half z, wave (2 * (hg % 4) + dh), dt pair, lane]
+    // partial vectors: [qi, split, 16-head group hg, dh, dt pair, lane], here
+    // indexed as 64-head block z = hg / 4 and (hg % 4, dh) inside it
     const int Z = a.H / 64, z = hg >> 2, wave_l = 2 * (hg & 3) + dh;
     const u32x4_t *src = (const u32x4_t *)a.part_o + ((((size_t)qi * S * Z + z) * 8 + wave_l) * 8 + p) * 64 + lane;
     const size_t sstride = (size_t)Z * 8 * 8 * 64;  // vectors per split
@@ -510,7 +516,8 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(MqaArgs a) {
     }
 }
 
-constexpr int kPlanWgs = 256;      // workgroups aimed at over the launch
+constexpr int kMqaHG = 2;          // 16-head groups per workgroup
+constexpr int kPlanWgs = 256;      // (query, split) pairs aimed at over the launch
 constexpr int kPlanMinRows = 64;   // rows per split at least
 
 void mqa_plan(int n_queries, int max_rows, int *n_splits, int *rows_per_split) {
@@ -556,7 +563,11 @@ hipError_t launch_mqa(const MqaArgs &a, int dtype, hipStream_t stream) {
         hipLaunchKernelGGL(mqa_f32_kernel, dim3(a.H, Q), dim3(256), lds, stream, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(mqa_bf16_kernel<4>, dim3(a.n_splits, Q, a.H / 64), dim3(512), 0, stream, a);
+    const dim3 grid(a.n_splits, Q, a.H / (16 * kMqaHG)), block(128 * kMqaHG);
+    if (a.v != nullptr || a.win_v != nullptr)  // separate value rows
+        hipLaunchKernelGGL((mqa_bf16_kernel<kMqaHG, true>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((mqa_bf16_kernel<kMqaHG, false>), grid, block, 0, stream, a);
     if (a.n_splits > 1) {
         int zq = 1;  // dim parts of the combine: about 256 workgroups
         while (zq < 4 && (long)Q * (a.H / 4) * zq * 2 <= 256) zq *= 2;
