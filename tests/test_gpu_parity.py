@@ -99,6 +99,18 @@ def test_flash_whole_step_small(lens):
     check_whole_step(make_case_with_lens(wl, sl), ATT_TOL_BF16)
 
 
+@pytest.mark.parametrize("lens,T,q_pos0", [
+    ([4 * 9000 + 1, 4 * 3000 + 2], 1, None),     # decode: several splits and the combine
+    ([4 * 2500 + 3], 24, 4 * 2500 + 3 - 30),     # a few queries of a prefill chunk
+])
+def test_separate_value_rows(lens, T, q_pos0):
+    """Value rows apart from the key rows (compressed cache and window): the
+    attention kernel's separate-value instance against the oracle."""
+    import dataclasses
+    wl, sl = flash_case(f"flash_sepv_{T}", lens, q_len=T, q_pos0=q_pos0)
+    check_whole_step(make_case_with_lens(dataclasses.replace(wl, separate_v=True), sl), ATT_TOL_BF16)
+
+
 def test_flash_no_activation():
     wl, sl = flash_case("flash_noact", [4 * 2000, 4 * 900])
     check_whole_step(make_case_with_lens(wl, sl), ATT_TOL_BF16, act=csa.CSA_ACT_NONE)
