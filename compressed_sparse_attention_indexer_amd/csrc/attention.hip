@@ -231,8 +231,8 @@ __global__ __launch_bounds__(128 * HG, 2) void mqa_bf16_kernel(MqaArgs a) {
     float m_run = -INFINITY, l_run = 0.f;  // head 16hg + e, log2 units
 
     // staging role: one row, CPL chunks of 16 bytes
-    // (a group of LPR consecutive lanes takes one row, so each 16-lane phase of
-    // the LDS writes covers 256 contiguous bytes)
+    // (a group of LPR consecutive lanes takes one row, 8 with HG = 2, so each
+    // 8-lane phase of the 16-byte LDS writes covers 128 contiguous bytes)
     const int srow = wave * RPW + lane / LPR;
     const int cg = lane % LPR;
     u32x4_t kreg[CPL], vreg[kSepV ? CPL : 1];
@@ -517,7 +517,7 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(MqaArgs a) {
 }
 
 constexpr int kMqaHG = 2;          // 16-head groups per workgroup
-constexpr int kPlanWgs = 256;      // (query, split) pairs aimed at over the launch
+constexpr int kPlanWgs = 128;      // (query, split) pairs aimed at over the launch (two or more workgroups each)
 constexpr int kPlanMinRows = 64;   // rows per split at least
 
 void mqa_plan(int n_queries, int max_rows, int *n_splits, int *rows_per_split) {
