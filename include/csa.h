@@ -212,7 +212,9 @@ csa_status hca_mqa_decode(const csa_dims *dims, const void *q, const void *const
  * Whole CSA step: csa_index_scores -> csa_topk_select -> csa_sparse_mqa_decode,
  * enqueued on one stream.  topk_idx_out (device [B,T,K] int32) and scores_out
  * (device [B,T,max_entries] float32) are optional outputs; when NULL the
- * intermediates live in the workspace.
+ * intermediates live in the workspace.  With bf16 index tensors the scorer
+ * also writes the selection's key-histogram windows (one launch fewer); the
+ * selected indices equal csa_topk_select's on the same scores.
  */
 csa_status csa_attention(const csa_dims *dims, const void *q, const void *q_idx, const float *w,
                          const void *const *k_idx, const void *const *kv, const void *const *v,
