@@ -186,8 +186,10 @@ csa_status csa_topk_select(const csa_dims *dims, const float *scores, const int3
  *   sink     device [H] float32 logits
  *   out      device [B,T,H,D] float32 (output)
  *   lse      NULL, or device [B,T,H] float32 natural-log sum of exp incl. the sink (output)
- * bf16 path: QK in bf16 MFMA, softmax in fp32, PV in fp16 MFMA (V converted
- * from bf16, exact for |v| < 65504), fp32 accumulation and output.
+ * bf16 path: QK in bf16 MFMA, softmax in fp32, PV in bf16 MFMA on V as given
+ * with the weights split into a bf16 high part and a bf16 remainder (about 16
+ * significant bits), fp32 accumulation.  Split partials O/l are kept in fp16
+ * (|O/l| <= max |v| < 65504), combined in fp32; fp32 output.
  */
 csa_status csa_sparse_mqa_decode(const csa_dims *dims, const void *q, const void *const *kv,
                                  const void *const *v, const int32_t *topk_idx,
