@@ -108,12 +108,18 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(
 
     const uint16_t *kb = (const uint16_t *)a.k_idx[b];
     const int last = nvis > 0 ? nvis - 1 : 0;
-    // step k of this wave starts at entry base0 + k * stride
-    const int stride = gridDim.x * kWgStep;
-    const int base0 = blockIdx.x * kWgStep + wave * kWaveStep;
-    const int n_steps = base0 < a.n_max ? (a.n_max - base0 + stride - 1) / stride : 0;
-    // steps that hold a visible entry come first: 0 .. n_load-1
-    const int n_load = base0 < nvis ? (nvis - base0 + stride - 1) / stride : 0;
+    // Work split: the query's visible entries, in workgroup steps of kWgStep,
+    // are cut into gridDim.x contiguous ranges, one per workgroup, so each
+    // workgroup streams one stretch of the key rows; wave w takes entries
+    // kWaveStep * w .. + kWaveStep - 1 of each step (step k of this wave starts
+    // at entry base0 + k * stride).  Steps wholly past the visible entries get
+    // -inf only, dealt round-robin.
+    const int vis_steps = (nvis + kWgStep - 1) / kWgStep;
+    const int chunk = (vis_steps + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int s0 = blockIdx.x * chunk;
+    const int n_load = vis_steps - s0 < chunk ? (vis_steps - s0 > 0 ? vis_steps - s0 : 0) : chunk;
+    const int stride = kWgStep;
+    const int base0 = s0 * kWgStep + wave * kWaveStep;
 
     // Every load is unconditional (indices clamped into the visible rows) so
     // the loop body is straight-line code and the compiler can wait for one
@@ -180,7 +186,11 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(
     // sits behind a branch: while step k computes, the loads of steps k+1 ..
     // k+kDepth-1 are in flight.  Steps past the last one reload the last step
     // and store nothing.  The histogram is cleared while the first loads are
-    // out (its barrier is reached by every wave, with or without steps).
+    // out; then the waves meet at a barrier (every wave reaches it, with or
+    // without steps), so the four go on loading adjacent 8 KiB blocks of their
+    // workgroup's stretch together rather than drifting apart from their
+    // staggered starts (measured: 47.0 -> 43.7 us for batch 4 x 262,144
+    // entries, against 46.4 us with the barrier and round-robin steps).
     KeyRaw kbuf[kDepth];
     auto step = [&](int k) { return base0 + (k < n_load ? k : n_load - 1) * stride; };
     if (n_load > 0) {
@@ -189,8 +199,8 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(
     }
     if (with_hist) {
         for (int i = threadIdx.x; i < kTopkBins; i += 64 * kScoreWaves) lh[i] = 0u;
-        __syncthreads();
     }
+    __syncthreads();
     if (n_load > 0) {
         for (int k = 0; k < n_load; k += kDepth) {
 #pragma unroll
@@ -199,8 +209,9 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(
             }
         }
     }
-    for (int k = n_load; k < n_steps; ++k) {  // steps past the visible entries: -inf
-        const int j = base0 + k * stride + 16 * g + e;
+    const int all_steps = (a.n_max + kWgStep - 1) / kWgStep;
+    for (int st = vis_steps + blockIdx.x; st < all_steps; st += gridDim.x) {  // steps past the visible entries
+        const int j = st * kWgStep + wave * kWaveStep + 16 * g + e;
         if (g < 2 && j < a.n_max) srow[j] = -INFINITY;
     }
     if (with_hist) {
