@@ -147,6 +147,8 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(
             for (int s2 = 0; s2 < 4; ++s2)
                 kf[et][s2] = *(const bf16x8_t *)&kw[(16 * et + e) * kRawRowWords + 16 * s2 + 4 * g];
     };
+    static_assert(kScoreWaves == 4, "the histogram window store takes 256 threads");
+    int hmax = -1;  // highest histogram bin this thread added
     // `live`: the step exists (a clamped re-run of the last step stores nothing)
     auto process = [&](KeyRaw &kr, int base, bool live, int next) {
         stash(kr);
@@ -179,7 +181,12 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(
         // Lanes of group g < 2 store column tile g: 32 consecutive scores.
         const float sv = j < nvis ? (g == 0 ? part[0] : part[1]) : -INFINITY;
         if (live && g < 2 && j < a.n_max) srow[j] = sv;
-        if (with_hist) lds_hist_add(lh, order_key(sv) >> 20, live && g < 2 && j < nvis);
+        if (with_hist) {
+            const uint32_t bin = order_key(sv) >> 20;
+            const bool add = live && g < 2 && j < nvis;
+            lds_hist_add(lh, bin, add);
+            if (add) hmax = max(hmax, (int)bin);
+        }
     };
 
     // Software pipeline kDepth steps deep, unrolled by kDepth so that no load
@@ -216,7 +223,7 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(
     }
     if (with_hist) {
         const size_t w = (size_t)qi * gridDim.x + blockIdx.x;
-        hist_window_store(lh, a.win_hdr + w, a.win_cnt + w * kTopkWin, s_red);
+        hist_window_store_top(lh, hmax, a.win_hdr + w, a.win_cnt + w * kTopkWin, s_red);
     }
 }
 

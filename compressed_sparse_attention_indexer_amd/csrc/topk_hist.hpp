@@ -49,6 +49,23 @@ __device__ __forceinline__ void hist_window_store(const uint32_t *lh, int32_t *h
     if (tid == 0) *hdr = M;
 }
 
+// The same for a workgroup of 256 threads whose threads already know the
+// highest bin they added (mb, -1 if none): no scan of the histogram.
+__device__ __forceinline__ void hist_window_store_top(const uint32_t *lh, int mb, int32_t *hdr, uint32_t *cnt,
+                                                      int *s_red) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mb = max(mb, __shfl_xor(mb, o));
+    if (lane == 0) s_red[wave] = mb;
+    __syncthreads();  // also: every add to lh is done
+    const int M = max(max(s_red[0], s_red[1]), max(s_red[2], s_red[3]));
+    if (tid < kTopkWin) {
+        const int b = M - (kTopkWin - 1) + tid;
+        cnt[tid] = (M >= 0 && b >= 0) ? lh[b] : 0u;
+    }
+    if (tid == 0) *hdr = M;
+}
+
 // Merge n_win windows (hdr[w], cnt[w][kTopkWin]) into the exact histogram of
 // the top kTopkWin bins below the global highest bin M, and return the bin
 // holding the K-th largest key (kNoBin if it lies below that range or there is
