@@ -9,8 +9,9 @@ Inputs are seeded synthetic tensors, resident in HBM before timing.
 One step = one pass of the CSA layer's hot path through the fused entry
 point csa_attention: indexer scores -> top-k -> sparse MQA with sink, over
 the whole batch.  Steps are captured in a HIP graph and replayed; the index-key and KV
-caches rotate between several device copies so the 256 MiB last-level cache
-cannot hold them from one step to the next.  The paired HCA layer, the other
+caches rotate between enough device copies (at least twice the 256 MiB
+last-level cache in all, for every workload) that no step finds the previous
+steps' rows in that cache.  The paired HCA layer, the other
 decode workloads and the per-kernel times are reported under "breakdown".
 
 Prints one JSON line.
@@ -173,6 +174,17 @@ class CsaRunner:
                                dc.seq_len, dc.q_pos, dc.sink, out=self.out, lse=self.lse, workspace=self.ws_all)
 
 
+LLC_BYTES = 256 << 20  # MI355X last-level (Infinity) cache
+
+
+def rotation(bytes_per_copy, minimum):
+    """Cache copies to rotate so the whole set is at least twice the last-level
+    cache: a cyclic pass over more than the cache then finds nothing of the
+    previous pass in it."""
+    need = -(-2 * LLC_BYTES // max(1, int(bytes_per_copy)))
+    return max(minimum, min(need, 256))
+
+
 def time_graph(torch, g, graph_steps, steps, warmup):
     for _ in range(max(1, warmup // graph_steps)):
         g.replay()
@@ -192,18 +204,19 @@ def time_graph(torch, g, graph_steps, steps, warmup):
 def bench_csa(torch, csa, case, args, detail):
     from compressed_sparse_attention_indexer_amd.staging import DeviceCase
     dc = DeviceCase(case)
-    r = CsaRunner(torch, csa, dc, args.copies)
+    copies = rotation(sum(x.numel() * x.element_size() for x in dc.k_idx), args.copies)
+    r = CsaRunner(torch, csa, dc, copies)
     Q = r.dims.batch * r.dims.q_len
     n_ent = case.n_entries
-    gs = args.graph_steps
+    gs = max(args.graph_steps, copies)  # every copy is used within one replay
     g_step = capture(torch, r.fused, gs)
     ms, wall, n = time_graph(torch, g_step, gs, args.steps, args.warmup)
     # graph replay result == eager result (deterministic kernels)
     out_graph = r.out.clone()
-    r.fused((n - 1) % args.copies)
+    r.fused((n - 1) % copies)
     torch.cuda.synchronize()
     same = bool(torch.equal(out_graph, r.out))
-    res = {"ms_per_step": ms, "queries_per_s": Q / (ms * 1e-3), "steps": n, "wall_s": wall,
+    res = {"ms_per_step": ms, "queries_per_s": Q / (ms * 1e-3), "steps": n, "wall_s": wall, "cache_copies": copies,
            "graph_matches_eager": same,
            "alg_bytes_per_step": csa_step_bytes(n_ent, Q),
            "step_GBps": csa_step_bytes(n_ent, Q) / (ms * 1e-3) / 1e9}
@@ -236,20 +249,22 @@ def bench_hca(torch, csa, case, args):
     ws = torch.zeros(max(256, csa.workspace_size(d, csa._lib.CSA_OP_HCA_MQA)), dtype=torch.uint8, device="cuda")
     copies = [dc.hca_kv_p]
     keep = []
-    for _ in range(args.copies - 1):
+    n_copies = rotation(sum(x.numel() * x.element_size() for x in dc.hca_kv), args.copies)
+    for _ in range(n_copies - 1):
         k2 = [x.clone() for x in dc.hca_kv]
         keep.append(k2)
         copies.append(csa.ptr_array(k2, "cuda"))
+    gs = max(args.graph_steps, n_copies)
 
     def call(i):
         csa.hca_mqa_decode(d, dc.hca_q, copies[i % len(copies)], None, dc.hca_win_p, None, dc.win_pos0,
                            dc.win_rows, dc.seq_len, dc.q_pos, dc.hca_sink, out=out, lse=lse, workspace=ws)
 
-    g = capture(torch, call, args.graph_steps)
-    ms, _, n = time_graph(torch, g, args.graph_steps, args.steps, args.warmup)
+    g = capture(torch, call, gs)
+    ms, _, n = time_graph(torch, g, gs, args.steps, args.warmup)
     n_h = case.seq_len // case.wl.hca_ratio
     b = hca_bytes(n_h, Q)
-    return {"ms_per_call": ms, "queries_per_s": Q / (ms * 1e-3), "alg_bytes": b,
+    return {"ms_per_call": ms, "queries_per_s": Q / (ms * 1e-3), "alg_bytes": b, "cache_copies": n_copies,
             "GBps": b / (ms * 1e-3) / 1e9, "frac_hbm_peak": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
@@ -268,10 +283,14 @@ def bench_fp8_scores(torch, csa, case, args):
     q8_t, qs_t = torch.from_numpy(q8).to(dev), torch.from_numpy(qs).to(dev)
     w_t = torch.from_numpy(case.w).to(dev)
     copies = []
-    for _ in range(args.copies):
-        k_t = [torch.from_numpy(k).to(dev) for k in k8]
-        s_t = [torch.from_numpy(x).to(dev) for x in ks]
+    n_copies = rotation(sum(k.nbytes for k in k8) + sum(x.nbytes for x in ks), args.copies)
+    k_0 = [torch.from_numpy(k).to(dev) for k in k8]
+    s_0 = [torch.from_numpy(x).to(dev) for x in ks]
+    for c in range(n_copies):
+        k_t = k_0 if c == 0 else [x.clone() for x in k_0]
+        s_t = s_0 if c == 0 else [x.clone() for x in s_0]
         copies.append((k_t, s_t, csa.ptr_array(k_t, dev), csa.ptr_array(s_t, dev)))
+    gs = max(args.graph_steps, n_copies)
     seq_t, pos_t = torch.from_numpy(case.seq_len).to(dev), torch.from_numpy(case.q_pos).to(dev)
     dims = csa.make_dims(batch=wl.batch, q_len=wl.q_len, max_entries=case.max_entries)
     scores = torch.empty((wl.batch, wl.q_len, case.max_entries), dtype=torch.float32, device=dev)
@@ -280,11 +299,11 @@ def bench_fp8_scores(torch, csa, case, args):
         c = copies[i % len(copies)]
         csa.csa_index_scores_fp8(dims, q8_t, qs_t, w_t, c[2], c[3], seq_t, pos_t, scores=scores)
 
-    g = capture(torch, call, args.graph_steps)
-    ms, _, _ = time_graph(torch, g, args.graph_steps, args.steps, args.warmup)
+    g = capture(torch, call, gs)
+    ms, _, _ = time_graph(torch, g, gs, args.steps, args.warmup)
     Q = wl.batch * wl.q_len
     b = fp8_scorer_bytes(case.n_entries, Q)
-    return {"ms_per_call": ms, "alg_bytes": b, "GBps": b / (ms * 1e-3) / 1e9,
+    return {"ms_per_call": ms, "alg_bytes": b, "GBps": b / (ms * 1e-3) / 1e9, "cache_copies": n_copies,
             "frac_hbm_peak": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "vs_bf16_scorer": None}
 
@@ -425,7 +444,7 @@ def main():
     if args.prefill:
         c4 = inputs.make_case(inputs.WORKLOADS["prefill_t2048_1m"])
         a2 = argparse.Namespace(**vars(args))
-        a2.steps, a2.warmup, a2.graph_steps, a2.copies = 3, 1, 1, 1
+        a2.steps, a2.warmup, a2.graph_steps, a2.copies = 3, 1, 1, 1  # the rotation still covers 2x the LLC
         r4, rr = bench_csa(torch, csa, c4, a2, detail=True)
         breakdown["prefill_t2048_1m"] = r4
         del rr, c4
@@ -444,7 +463,7 @@ def main():
                    "window": wl.window, "heads": wl.n_heads, "head_dim": wl.head_dim,
                    "index_heads": wl.index_heads, "index_dim": wl.index_dim,
                    "step": "csa_attention (index_scores -> topk_select -> sparse_mqa + sink), graph-replayed",
-                   "cache_copies_rotated": args.copies},
+                   "cache_copies_rotated": main_res["cache_copies"]},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "breakdown": breakdown,
