@@ -16,7 +16,9 @@ namespace csa {
 // act(q8_h . k8_j); the head weights absorb the query scales once, and each
 // stored score takes its entry's scale.  A wave-step is 64 entries (8 KiB,
 // 1 KiB contiguous per load instruction), redistributed through a
-// wave-private LDS block as in the bf16 kernel.
+// wave-private LDS block as in the bf16 kernel.  Unlike the bf16 kernel, the
+// workgroup steps of a query are dealt round-robin to its workgroups: the
+// contiguous stretches with a start barrier measured slower for these rows.
 namespace {
 constexpr int kF8WaveStep = 64;                        // entries per wave and step
 constexpr int kF8WgStep = kScoreWaves * kF8WaveStep;   // entries per workgroup step
