@@ -217,12 +217,13 @@ def test_topk_any_workspace_contents_stay_exact(fill):
         np.testing.assert_array_equal(got, want)
 
 
-def test_fused_selection_equals_standalone_topk():
+@pytest.mark.parametrize("act", [csa.CSA_ACT_RELU, csa.CSA_ACT_NONE])
+def test_fused_selection_equals_standalone_topk(act):
     wl, sl = flash_case("flash_fused_vs_standalone", [4 * 40000, 4 * 9000, 4 * 20000 + 1])
     case = make_case_with_lens(wl, sl)
-    say(f"[case] {wl.name}")
+    say(f"[case] {wl.name} act={act}")
     dc = DeviceCase(case)
-    g_scores, g_idx, _, _ = run_fused(dc)
+    g_scores, g_idx, _, _ = run_fused(dc, act)
     dims = dc.csa_dims()
     t_idx = _np(csa.csa_topk_select(dims, torch.from_numpy(g_scores).cuda(), dc.seq_len, dc.q_pos))
     np.testing.assert_array_equal(t_idx, g_idx)
@@ -330,20 +331,23 @@ def test_prefill_chunk_no_activation():
     check_whole_step(make_case_with_lens(wl, sl), ATT_TOL_BF16, act=csa.CSA_ACT_NONE)
 
 
-@pytest.mark.parametrize("lens,T,q_pos0", [
-    ([4 * 20000 + 3], 300, 4 * 20000 + 3 - 300),     # many queries: one selecting workgroup each
-    ([4 * 6000 + 1, 4 * 9000 + 2], 40, 2030),        # visible counts cross K inside the chunk
-    ([4 * 70000], 16, 4 * 70000 - 16),               # long rows, few queries: filter and final kernels
+@pytest.mark.parametrize("lens,T,q_pos0,act", [
+    ([4 * 20000 + 3], 300, 4 * 20000 + 3 - 300, csa.CSA_ACT_RELU),  # many queries: one selecting workgroup each
+    ([4 * 6000 + 1, 4 * 9000 + 2], 40, 2030, csa.CSA_ACT_RELU),     # visible counts cross K inside the chunk
+    ([4 * 70000], 16, 4 * 70000 - 16, csa.CSA_ACT_RELU),            # long rows, few queries: filter and final
+    ([4 * 30000 + 1], 24, 4 * 30000 - 30, csa.CSA_ACT_NONE),        # signed scores: keys in both halves
 ])
-def test_prefill_fused_selection_equals_standalone_topk(lens, T, q_pos0):
+def test_prefill_fused_selection_equals_standalone_topk(lens, T, q_pos0, act):
     """The tiled scorer builds the key histograms for the selection while it
     writes the scores; the selection must equal the top-k kernel run alone
     (its own histogram pass) and the oracle's top-k on the same scores."""
     wl, sl = flash_case(f"prefill_fused_{len(lens)}_{T}", lens, q_len=T, q_pos0=q_pos0)
     case = make_case_with_lens(wl, sl)
-    say(f"[case] {wl.name} B={wl.batch} T={T} max_entries={case.max_entries}")
+    say(f"[case] {wl.name} B={wl.batch} T={T} max_entries={case.max_entries} act={act}")
     dc = DeviceCase(case)
-    g_scores, g_idx, g_out, g_lse = run_fused(dc)
+    g_scores, g_idx, g_out, g_lse = run_fused(dc, act)
+    if act == csa.CSA_ACT_NONE:
+        assert (g_scores[np.isfinite(g_scores)] < 0).any(), "the case should hold negative scores"
     assert np.isfinite(g_out).all() and np.isfinite(g_lse).all()
     t_idx = _np(csa.csa_topk_select(dc.csa_dims(), torch.from_numpy(g_scores).cuda(), dc.seq_len, dc.q_pos))
     np.testing.assert_array_equal(t_idx, g_idx)
