@@ -196,8 +196,8 @@ csa::MqaArgs mqa_args(const csa_dims *d, const void *q, const void *const *kv, c
     a.ratio = d->ratio;
     a.scale = scale_of(d);
     a.n_splits = 1;
-    a.rows_per_split = max_rows;
-    if (d->dtype == CSA_BF16) csa::mqa_plan(n_queries(d), max_rows, &a.n_splits, &a.rows_per_split);
+    a.n_tiles = 1;
+    if (d->dtype == CSA_BF16) csa::mqa_plan(n_queries(d), max_rows, &a.n_splits, &a.n_tiles);
     csa::mqa_carve(a, ws, n_queries(d));
     return a;
 }

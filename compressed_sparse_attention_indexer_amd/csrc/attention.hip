@@ -217,11 +217,13 @@ __global__ __launch_bounds__(128 * HG, 2) void mqa_bf16_kernel(MqaArgs a) {
     }
     const SeqRows<uint16_t> sq = seq_rows<uint16_t>(a, qi);
     const int srow0 = wave * RPW + lane / LPR;
-    const int i_first = split * a.rows_per_split + srow0;
+    // this split's rows: whole tiles, the query's tiles dealt as evenly as possible over the splits
+    const int r0 = (int)((long long)split * a.n_tiles / a.n_splits) * kTile;
+    const int r_end = (int)((long long)(split + 1) * a.n_tiles / a.n_splits) * kTile;
+    const int i_first = r0 + srow0;
     const int j_first = a.topk_idx && i_first < a.K ? a.topk_idx[(size_t)qi * a.K + i_first] : -2;
     const RowList rl = make_rows(a, qi);
-    const int r0 = split * a.rows_per_split;
-    const int r1 = r0 + a.rows_per_split < rl.n_rows ? r0 + a.rows_per_split : rl.n_rows;
+    const int r1 = r_end < rl.n_rows ? r_end : rl.n_rows;
     const int ntiles = r1 > r0 ? (r1 - r0 + kTile - 1) / kTile : 0;
     const float scale2 = a.scale * kLog2e;
 
@@ -520,27 +522,24 @@ constexpr int kMqaHG = 2;          // 16-head groups per workgroup
 constexpr int kPlanWgs = 128;      // (query, split) pairs aimed at over the launch (two or more workgroups each)
 constexpr int kPlanMinRows = 64;   // rows per split at least
 
-void mqa_plan(int n_queries, int max_rows, int *n_splits, int *rows_per_split) {
-    // about kPlanWgs workgroups, at least kPlanMinRows rows per split, whole tiles
+void mqa_plan(int n_queries, int max_rows, int *n_splits, int *n_tiles) {
+    // about kPlanWgs (query, split) pairs, at least kPlanMinRows rows (whole
+    // tiles) per split; the tiles are dealt evenly, so splits differ by at most
+    // one tile
+    const int tiles = (max_rows + kTile - 1) / kTile;
     const int want_splits = (kPlanWgs + n_queries - 1) / n_queries;
-    int rps = (max_rows + want_splits - 1) / want_splits;
-    if (rps < kPlanMinRows) rps = kPlanMinRows;
-    rps = (rps + kTile - 1) / kTile * kTile;
-    int s = (max_rows + rps - 1) / rps;
+    int s = tiles / (kPlanMinRows / kTile);
+    if (s > want_splits) s = want_splits;
+    if (s > kCombineMaxSplits) s = kCombineMaxSplits;
     if (s < 1) s = 1;
-    if (s > kCombineMaxSplits) {
-        s = kCombineMaxSplits;
-        rps = ((max_rows + s - 1) / s + kTile - 1) / kTile * kTile;
-        s = (max_rows + rps - 1) / rps;
-    }
     *n_splits = s;
-    *rows_per_split = rps;
+    *n_tiles = tiles > 0 ? tiles : 1;
 }
 
 size_t mqa_workspace_bytes(int dtype, int n_queries, int H, int D, int max_rows) {
     if (dtype != kBF16) return 0;
-    int s, rps;
-    mqa_plan(n_queries, max_rows, &s, &rps);
+    int s, tiles;
+    mqa_plan(n_queries, max_rows, &s, &tiles);
     if (s == 1) return 0;
     const size_t n = (size_t)n_queries * s * H;
     return n * D * 2 + n * 2 * 4 + 256;

@@ -88,12 +88,13 @@ struct MqaArgs {
     void *part_o;                   // [Q, S, 8, 8, 64] 16-byte fp16 vectors: split partials O / l
     float *part_ml;                 // [Q, S, H, 2]
     int B, T, H, D, K, W, ratio;
-    int n_splits, rows_per_split;
+    int n_splits, n_tiles;          // splits per query; kTile-row tiles of the longest row list
     float scale;                    // softmax scale (natural units)
 };
 
 // Split plan for the bf16 split-K kernel: max_rows = largest row count of a query.
-void mqa_plan(int n_queries, int max_rows, int *n_splits, int *rows_per_split);
+// Split s of a query takes tiles [s * n_tiles / n_splits, (s + 1) * n_tiles / n_splits).
+void mqa_plan(int n_queries, int max_rows, int *n_splits, int *n_tiles);
 size_t mqa_workspace_bytes(int dtype, int n_queries, int H, int D, int max_rows);
 void mqa_carve(MqaArgs &a, void *ws, int n_queries);
 hipError_t launch_mqa(const MqaArgs &a, int dtype, hipStream_t stream);
