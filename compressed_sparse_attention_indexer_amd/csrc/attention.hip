@@ -393,8 +393,8 @@ __global__ __launch_bounds__(128 * HG, 2) void mqa_bf16_kernel(MqaArgs a) {
 
 // Merge split partials with the sink, counted once (H = 64 or 128).
 // Workgroup = (16-head group hg, lane group g, dim part dq of Zq, query):
-// heads h0 .. h0 + 3 (h0 = 16hg + 4g) at 512 / Zq of the dims (Zq = 1, 2 or 4,
-// chosen so the launch has about 256 workgroups).  A 16-byte partial vector
+// heads h0 .. h0 + 3 (h0 = 16hg + 4g) at 512 / Zq of the dims (Zq = 1, 2, 4 or 8,
+// chosen so the launch has about 256 workgroups, 512 with many splits).  A 16-byte partial vector
 // holds those 4 heads at two dims; the part's 256 / Zq vector positions of a
 // split are spread over 256 / Zq threads (position: half dh, dt pair p,
 // column e), and thread group sg of Zq folds splits sg, sg + Zq, ... , so with
@@ -412,7 +412,7 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(MqaArgs a) {
     constexpr int kBatch = 16;
     __shared__ float s_w[kCombineMaxSplits][4];
     __shared__ float s_M[4], s_L[4];
-    __shared__ float s_acc[1536];  // (Zq - 1) groups x 8 sums x 256 / Zq positions
+    __shared__ float s_acc[1792];  // (Zq - 1) groups x 8 sums x 256 / Zq positions
     const int qi = blockIdx.y, dq = blockIdx.z;
     const int hg = blockIdx.x >> 2, g = blockIdx.x & 3;
     const int tid = threadIdx.x, wv = tid >> 6, ln = tid & 63;
@@ -570,8 +570,12 @@ hipError_t launch_mqa(const MqaArgs &a, int dtype, hipStream_t stream) {
     if (a.n_splits > 1) {
         int zq = 1;  // dim parts of the combine: about 256 workgroups
         while (zq < 4 && (long)Q * (a.H / 4) * zq * 2 <= 256) zq *= 2;
+        // many splits (the HCA layer): eight dim parts, so each thread folds fewer splits
+        if (zq == 4 && a.n_splits >= 16 && (long)Q * (a.H / 4) * 8 <= 512) zq = 8;
         const dim3 grid(a.H / 4, Q, zq);
-        if (zq == 4)
+        if (zq == 8)
+            hipLaunchKernelGGL(mqa_combine_kernel<8>, grid, dim3(256), 0, stream, a);
+        else if (zq == 4)
             hipLaunchKernelGGL(mqa_combine_kernel<4>, grid, dim3(256), 0, stream, a);
         else if (zq == 2)
             hipLaunchKernelGGL(mqa_combine_kernel<2>, grid, dim3(256), 0, stream, a);
