@@ -416,7 +416,7 @@ def _dense_brute(case):
     f = lambda x: inputs.as_float64(x, wl.dtype)
     B, T, H, D = case.q.shape
     scale = 1.0 / math.sqrt(D)
-    outs = np.zeros((B, T, H, D))
+    outs, lses = np.zeros((B, T, H, D)), np.zeros((B, T, H))
     for b, t in itertools.product(range(B), range(T)):
         p = int(case.q_pos[b * T + t])
         N = int(case.seq_len[b]) // wl.ratio
@@ -440,15 +440,95 @@ def _dense_brute(case):
         pr = np.exp(zs - zs.max(1, keepdims=True))
         pr /= pr.sum(1, keepdims=True)
         outs[b, t] = pr[:, :-1] @ allv
-    return outs
+        lses[b, t] = zs.max(1) + np.log(np.exp(zs - zs.max(1, keepdims=True)).sum(1))
+    return outs, lses
 
 
 @pytest.mark.parametrize("L,K", [(512, 32), (160, 64), (64, 8)])
 def test_whole_step_against_dense_brute_force(L, K):
     wl = inputs.scaled(inputs.WORKLOADS["fixture_b2_l512_fp32"], f"tiny_{L}_{K}", seq_len=L, topk=K)
     case = inputs.make_case(wl)
-    _, _, out, _ = oracle.csa_attention(case)
-    np.testing.assert_allclose(out, _dense_brute(case), rtol=1e-9, atol=1e-12)
+    _, _, out, lse = oracle.csa_attention(case)
+    want, want_lse = _dense_brute(case)
+    np.testing.assert_allclose(out, want, rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(lse, want_lse, rtol=1e-12, atol=1e-12)
+
+
+def _causal_multi_query_case(seed=31):
+    """Two sequences of ragged raw lengths (70 and 53), six queries each at
+    distinct positions (causal visibility, as in a prefill chunk): one query
+    sees no compressed entry (p = 2), several see fewer than K, and the two
+    sequences' positions differ, so every query indexes its own sequence's
+    caches, position, window and visible count.  The window buffers hold every
+    raw row of their sequence."""
+    base = inputs.WORKLOADS["fixture_b2_l512_fp32"]
+    B, T, H, D, HI, DI, K, W, r = 2, 6, 4, 16, 4, 16, 5, 8, 4
+    wl = inputs.scaled(base, "tiny_causal_b2_t6", q_len=T, topk=K, window=W, seq_len=None,
+                       seq_len_range=(53, 70), q_pos0=0)
+    g = _rng(seed)
+    L = np.array([70, 53], np.int32)
+    q_pos = np.array([20, 33, 34, 47, 60, 69, 2, 11, 12, 30, 44, 52], np.int32)
+    nrm = lambda *shape: (g.standard_normal(shape) / math.sqrt(shape[-1])).astype(np.float32)
+    return inputs.Case(
+        wl=wl, seq_len=L, q_pos=q_pos,
+        q=nrm(B, T, H, D), q_idx=nrm(B, T, HI, DI), w=g.random((B, T, HI)).astype(np.float32),
+        k_idx=[nrm(int(n) // r, DI) for n in L], kv=[nrm(int(n) // r, D) for n in L],
+        v=[nrm(int(n) // r, D) for n in L], win=[nrm(int(n), D) for n in L], win_v=[nrm(int(n), D) for n in L],
+        win_pos0=np.zeros(B, np.int32), win_rows=L.copy(), sink=g.standard_normal(H).astype(np.float32))
+
+
+def test_multi_query_causal_scores_topk_and_attention_against_dense_brute():
+    """Several queries per sequence (T > 1) at their own positions: scores by
+    einsum with the causal mask, top-k by rank counting, attention by the dense
+    masked softmax, each query against its own sequence (b = query // T) and
+    its own position."""
+    case = _causal_multi_query_case()
+    wl = case.wl
+    B, T = wl.batch, wl.q_len
+    n_max = case.max_entries
+    scores = oracle.index_scores(case.q_idx, case.w, case.k_idx, case.seq_len, case.q_pos, ratio=wl.ratio,
+                                 n_max=n_max, dtype=F32)
+    idx = oracle.topk(scores, case.seq_len, case.q_pos, ratio=wl.ratio, k=wl.topk)
+    nvis = []
+    for b, t in itertools.product(range(B), range(T)):
+        p = int(case.q_pos[b * T + t])
+        nv = min(int(case.seq_len[b]) // wl.ratio, (p + 1) // wl.ratio)
+        nvis.append(nv)
+        dots = np.einsum("hd,jd->hj", case.q_idx[b, t].astype(np.float64), case.k_idx[b][:nv].astype(np.float64))
+        want = (case.w[b, t].astype(np.float64)[:, None] * np.maximum(dots, 0)).sum(0)
+        np.testing.assert_allclose(scores[b, t, :nv], want, rtol=1e-6)
+        assert np.isneginf(scores[b, t, nv:]).all()
+        assert idx[b, t].tolist() == _brute_topk(scores[b, t, :nv].tolist(), wl.topk)
+    assert 0 in nvis and any(0 < n < wl.topk for n in nvis) and max(nvis) > wl.topk
+    s2, idx2, out, lse = oracle.csa_attention(case)
+    np.testing.assert_array_equal(s2, scores)
+    np.testing.assert_array_equal(idx2, idx)
+    want, want_lse = _dense_brute(case)
+    np.testing.assert_allclose(out, want, rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(lse, want_lse, rtol=1e-12, atol=1e-12)
+
+
+def test_multi_query_hca_against_dense_brute():
+    """The dense (HCA) path with T > 1: every visible entry of the query's own
+    sequence at its own position, then its window, in one softmax with the sink."""
+    case = _causal_multi_query_case(32)
+    wl = case.wl
+    B, T, H, D = case.q.shape
+    out, lse = oracle.hca_mqa(case.q, case.kv, case.v, case.win, case.win_v, case.win_pos0, case.win_rows,
+                              case.seq_len, case.q_pos, case.sink, window=wl.window, ratio=wl.ratio,
+                              scale=0.25, dtype=F32)
+    for b, t in itertools.product(range(B), range(T)):
+        p = int(case.q_pos[b * T + t])
+        nv = min(int(case.seq_len[b]) // wl.ratio, (p + 1) // wl.ratio)
+        lo = max(0, p - wl.window + 1)
+        keys = np.concatenate([case.kv[b][:nv], case.win[b][lo:p + 1]]).astype(np.float64)
+        vals = np.concatenate([case.v[b][:nv], case.win_v[b][lo:p + 1]]).astype(np.float64)
+        z = 0.25 * case.q[b, t].astype(np.float64) @ keys.T
+        zs = np.concatenate([z, case.sink.astype(np.float64)[:, None]], axis=1)
+        pr = np.exp(zs - zs.max(1, keepdims=True))
+        np.testing.assert_allclose(out[b, t], (pr[:, :-1] @ vals) / pr.sum(1, keepdims=True), rtol=1e-9,
+                                   atol=1e-12)
+        np.testing.assert_allclose(lse[b, t], zs.max(1) + np.log(pr.sum(1)), rtol=1e-12)
 
 
 def test_fixture_golden_file_matches():
@@ -633,6 +713,54 @@ def test_compress_hadamard_is_the_normalized_sylvester_matrix():
     rot = oracle.compress(x, wkv, wg, ape, gamma, pos0=0, ratio=4, window=8, first_entry=1, n_entries=3,
                           hadamard=True)
     np.testing.assert_allclose(rot, plain @ (hadamard(16) / 4.0).T, rtol=1e-12, atol=1e-14)
+
+
+def _one_hot_tokens(n_tokens, hidden):
+    x = np.zeros((n_tokens, hidden), np.float32)
+    x[np.arange(n_tokens), np.arange(n_tokens)] = 1.0
+    return inputs.bf16_bits(x)
+
+
+def test_compress_gate_term_weights_the_tokens():
+    """Two one-hot tokens and no position embeddings: token t's projection is
+    column t of wkv and its gate logit column t of wgate, so per dim d the pooled
+    value is sigma(g0 - g1) kv0 + sigma(g1 - g0) kv1 with g = wgate[d, t], here
+    different per dim (a per-dim softmax, not one shared by all dims)."""
+    hidden, out_dim = 32, 16
+    g = _rng(40)
+    x = _one_hot_tokens(2, hidden)
+    wkv = inputs.bf16_bits(g.standard_normal((out_dim, hidden)).astype(np.float32))
+    wg = np.zeros((out_dim, hidden), np.float32)
+    wg[:, 0] = np.arange(out_dim) % 5 - 2.0       # gate logit of token 0, per dim: -2 .. 2
+    wg[:, 1] = -0.5 * (np.arange(out_dim) % 3)    # token 1: 0, -0.5, -1
+    wg = inputs.bf16_bits(wg)
+    gamma = g.uniform(0.5, 1.5, out_dim).astype(np.float32)
+    out = oracle.compress(x, wkv, wg, np.zeros((2, out_dim), np.float32), gamma, pos0=0, ratio=2, window=2,
+                          first_entry=0, n_entries=1)
+    g0, g1 = _f64(wg)[:, 0], _f64(wg)[:, 1]
+    p0 = 1.0 / (1.0 + np.exp(g1 - g0))
+    c = p0 * _f64(wkv)[:, 0] + (1.0 - p0) * _f64(wkv)[:, 1]
+    np.testing.assert_allclose(out[0], _rms_norm(c, gamma), rtol=1e-12, atol=1e-14)
+
+
+def test_compress_gate_adds_the_position_embedding():
+    """With both terms present the logit of token t in window slot i is
+    wgate x_t + ape[i] (a sum): tokens 4..7 of an overlapping 8-token window
+    (slots 4..7), one-hot, so entry 1's weights are a softmax of
+    wgate[d, t] + ape[t, d] over t = 0..7 (entry 1 pools tokens 0..7)."""
+    hidden, out_dim = 32, 8
+    g = _rng(41)
+    x = _one_hot_tokens(8, hidden)
+    wkv = inputs.bf16_bits(g.standard_normal((out_dim, hidden)).astype(np.float32))
+    wg = inputs.bf16_bits(g.standard_normal((out_dim, hidden)).astype(np.float32))
+    ape = g.standard_normal((8, out_dim)).astype(np.float32)
+    out = oracle.compress(x, wkv, wg, ape, np.ones(out_dim, np.float32), pos0=0, ratio=4, window=8,
+                          first_entry=1, n_entries=1)
+    logit = _f64(wg)[:, :8] + ape.astype(np.float64).T          # [d, t]
+    p = np.exp(logit - logit.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    c = (p * _f64(wkv)[:, :8]).sum(1)
+    np.testing.assert_allclose(out[0], _rms_norm(c, np.ones(out_dim)), rtol=1e-12, atol=1e-14)
 
 
 def test_compress_rejects_windows_not_supplied():
