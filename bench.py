@@ -46,8 +46,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--quick", action="store_true", help="skip the other decode workloads")
     p.add_argument("--prefill", action="store_true", help="also time the 2048-token prefill chunk")
-    p.add_argument("--profile-kernels", action="store_true",
-                   help="run only eager scorer launches (for rocprofv3 counter runs)")
+    p.add_argument("--profile-kernels", nargs="?", const="scorer", default=None,
+                   choices=("scorer", "step", "hca", "fp8", "prefill"),
+                   help="run only eager launches of one part (for rocprofv3 counter runs): the bf16 scorer, "
+                        "the fused decode step, the HCA layer, the fp8 scorer or the prefill chunk")
     return p.parse_args()
 
 
@@ -378,6 +380,49 @@ def cpu_baseline(case):
                       f"top-k, attention), repeated {runs} times, {t_total:.1f} s in all"}
 
 
+def profile_kernels(torch, csa, inputs, case, args):
+    """Eager launches of one part of the path, then a plain 256 MiB device copy
+    (the calibration for the byte counters), for rocprofv3 counter runs."""
+    from compressed_sparse_attention_indexer_amd.staging import DeviceCase
+    what = args.profile_kernels
+    if what == "prefill":
+        case = inputs.make_case(inputs.WORKLOADS["prefill_t2048_1m"], with_hca=False)
+    dc = DeviceCase(case)
+    if what in ("scorer", "step", "prefill"):
+        r = CsaRunner(torch, csa, dc, args.copies if what != "prefill" else 1)
+        fn = r.scores_call if what == "scorer" else r.fused
+    elif what == "hca":
+        d = dc.hca_dims()
+        out = torch.empty((d.batch, d.q_len, d.n_heads, d.head_dim), dtype=torch.float32, device="cuda")
+        lse = torch.empty((d.batch, d.q_len, d.n_heads), dtype=torch.float32, device="cuda")
+        ws = torch.zeros(max(256, csa.workspace_size(d, csa._lib.CSA_OP_HCA_MQA)), dtype=torch.uint8, device="cuda")
+
+        def fn(i):
+            csa.hca_mqa_decode(d, dc.hca_q, dc.hca_kv_p, None, dc.hca_win_p, None, dc.win_pos0, dc.win_rows,
+                               dc.seq_len, dc.q_pos, dc.hca_sink, out=out, lse=lse, workspace=ws)
+    else:  # fp8 scorer
+        wl = case.wl
+        q8, qs, k8, ks = inputs.make_fp8_index(case)
+        t = lambda a: torch.from_numpy(a).to("cuda")
+        q8_t, qs_t, w_t = t(q8), t(qs), t(case.w)
+        k_t, s_t = [t(k) for k in k8], [t(x) for x in ks]
+        kp, sp = csa.ptr_array(k_t, "cuda"), csa.ptr_array(s_t, "cuda")
+        dims = csa.make_dims(batch=wl.batch, q_len=wl.q_len, max_entries=case.max_entries)
+        scores = torch.empty((wl.batch, wl.q_len, case.max_entries), dtype=torch.float32, device="cuda")
+
+        def fn(i):
+            csa.csa_index_scores_fp8(dims, q8_t, qs_t, w_t, kp, sp, dc.seq_len, dc.q_pos, scores=scores)
+    for i in range(args.steps):
+        fn(i)
+    torch.cuda.synchronize()
+    src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_kernels": what, "launches": args.steps, "copy_bytes": src.numel() * 4}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -396,19 +441,8 @@ def main():
     case = inputs.make_case(wl)
     print(f"[bench] generated {wl.name} in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
 
-    if args.profile_kernels:  # eager scorer launches only, for counter collection
-        from compressed_sparse_attention_indexer_amd.staging import DeviceCase
-        r = CsaRunner(torch, csa, DeviceCase(case), args.copies)
-        for i in range(args.steps):
-            r.scores_call(i)
-        torch.cuda.synchronize()
-        # calibration for the byte counters: a plain device copy of 256 MiB
-        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"profile_kernels": args.steps, "copy_bytes": src.numel() * 4}))
+    if args.profile_kernels:  # eager launches of one part only, for counter collection
+        profile_kernels(torch, csa, inputs, case, args)
         return
 
     main_res, runner = bench_csa(torch, csa, case, args, detail=True)

@@ -22,21 +22,45 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+def _flags(extra_flags):
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+            # keep the compiler from emitting packed fp32 arithmetic
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}", *extra_flags]
+
+
+def _quiet(text):
+    return "\n".join(l for l in text.splitlines() if "packed-fp32-ops" not in l)
+
+
 def build_library(verbose: bool = False, extra_flags=()) -> str:
+    """Compile every source to an object (in parallel), then link libcsa.so."""
+    from concurrent.futures import ThreadPoolExecutor
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    cc = hipcc()
+
+    def compile_one(src):
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+        cmd = [cc, *_flags(extra_flags), "-c", os.path.join(CSRC, src), "-o", obj]
+        res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        return src, obj, " ".join(cmd), res.returncode, _quiet(res.stdout)
+
+    jobs = min(len(SOURCES), max(1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
+    with ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(compile_one, SOURCES))
+    for src, obj, cmd, rc, out in results:
+        if verbose:
+            print(cmd, flush=True)
+        if rc != 0:
+            raise RuntimeError(f"hipcc failed on {src} ({rc}):\n{out}")
+        if verbose and out.strip():
+            print(out)
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           # keep the compiler from emitting packed fp32 arithmetic
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}", *extra_flags,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *[r[1] for r in results], "-o", tmp]
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    out = "\n".join(l for l in res.stdout.splitlines() if "packed-fp32-ops" not in l)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
-    if verbose and out.strip():
-        print(out)
+        raise RuntimeError(f"link failed ({res.returncode}):\n{_quiet(res.stdout)}")
     os.replace(tmp, LIB)
     return LIB
 

@@ -103,8 +103,15 @@ int win_count(const csa_dims *d, bool fused) {
     if (csa::score_uses_tiles(csa::kBF16, d->q_len)) return csa::tiled_windows(d->batch, d->q_len, d->max_entries);
     return csa::score_workgroups(d->max_entries, n_queries(d));
 }
+// Entries per decode-scorer workgroup handed to the selection in the fused
+// call (0: the selection scans the scores itself).
+int emit_cap(const csa_dims *d, bool fused) {
+    if (!fused || d->dtype != CSA_BF16 || csa::score_uses_tiles(csa::kBF16, d->q_len)) return 0;
+    if (!csa::topk_uses_histogram(d->max_entries)) return 0;
+    return csa::score_emit_cap(d->max_entries, n_queries(d), d->topk);
+}
 size_t ws_topk(const csa_dims *d, bool fused = false) {
-    return csa::topk_workspace_bytes(n_queries(d), d->topk, d->max_entries, win_count(d, fused));
+    return csa::topk_workspace_bytes(n_queries(d), d->topk, d->max_entries, win_count(d, fused), emit_cap(d, fused));
 }
 size_t ws_sparse(const csa_dims *d) {
     return csa::mqa_workspace_bytes(d->dtype, n_queries(d), d->n_heads, d->head_dim, d->topk + d->window);
@@ -165,7 +172,7 @@ csa::TopkArgs topk_args(const csa_dims *d, const float *scores, const int32_t *s
     a.ratio = d->ratio;
     a.K = d->topk;
     a.n_max = d->max_entries;
-    csa::topk_carve(a, ws, n_queries(d), win_count(d, fused));
+    csa::topk_carve(a, ws, n_queries(d), win_count(d, fused), emit_cap(d, fused));
     return a;
 }
 
@@ -491,6 +498,10 @@ csa_status csa_attention(const csa_dims *d, const void *q, const void *q_idx, co
         sa.win_hdr = ta.win_hdr;
         sa.win_cnt = ta.win_cnt;
         sa.K = d->topk;
+        sa.em_cap = ta.em_cap;  // the decode scorer also hands the selection its high entries
+        sa.em_hdr = ta.em_hdr;
+        sa.em_key = ta.em_key;
+        sa.em_idx = ta.em_idx;
     }
     hipError_t e = csa::launch_index_scores(sa, d->dtype, st);
     if (e != hipSuccess) return hip_status(e, "csa_attention/scores");

@@ -23,6 +23,11 @@ struct ScoreArgs {
     int32_t *win_hdr;           // [Q, n_win]
     uint32_t *win_cnt;          // [Q, n_win, kTopkWin]
     int K;
+    // optional emitted entries of each workgroup for the selection (em_cap 0: none)
+    int em_cap;                 // entries per workgroup at most
+    int32_t *em_hdr;            // [Q, n_win, 2]: cut bin, count
+    uint32_t *em_key;           // [Q, n_win, em_cap]
+    int32_t *em_idx;            // [Q, n_win, em_cap]
     // fp8 (E4M3) index tensors: per-row scales (null for bf16 / fp32)
     const float *q_scale;       // [Q, HI]
     const void *const *k_scale; // [B] -> [N_b] float
@@ -32,6 +37,8 @@ hipError_t launch_index_scores(const ScoreArgs &a, int dtype, hipStream_t stream
 // fp8 (E4M3) index queries and keys with per-row scales, HI = 64, DI = 128
 hipError_t launch_index_scores_fp8(const ScoreArgs &a, hipStream_t stream);
 int score_workgroups(int n_max, int n_queries);  // bf16 scorer workgroups per query
+// entries per workgroup the decode scorer can hand the selection, 0 if it cannot
+int score_emit_cap(int n_max, int n_queries, int K);
 // many queries per sequence: the GEMM-tiled scorer
 bool score_uses_tiles(int dtype, int T);
 // histogram windows per query the tiled scorer can write (its entry chunks), 0 if it cannot
@@ -48,6 +55,8 @@ constexpr int kFltAboveCap = 64;          // per filter workgroup: entries above
 constexpr int kFltCandCap = 256;          // per filter workgroup: candidates inside it
 constexpr int kFltRegionWords = 2 + kFltAboveCap + 2 * kFltCandCap;
 constexpr int kTopkManyQueries = 256;     // from this many queries on: one selecting workgroup per query
+constexpr int kTopkMaxRegions = 256;      // emitted regions (decode-scorer workgroups) per query at most
+constexpr int kTopkMaxSlots = 8192;       // emitted slots (regions x entries per region) per query at most
 
 struct TopkArgs {
     const float *scores;        // [Q, n_max]
@@ -62,11 +71,17 @@ struct TopkArgs {
     uint32_t *win_cnt;          // [Q, n_win, kTopkWin]
     uint32_t *bin;              // [Q] threshold bin (long rows)
     uint32_t *flt;              // [Q, n_flt, kFltRegionWords] per-filter-workgroup lists (long rows)
+    // the scorer's emitted entries, one region per window (em_cap 0: not used)
+    int em_cap;
+    int32_t *em_hdr;            // [Q, n_win, 2]
+    uint32_t *em_key;           // [Q, n_win, em_cap]
+    int32_t *em_idx;            // [Q, n_win, em_cap]
 };
 
-// n_win: windows per query (scorer workgroups per query in the fused path, else 0 = own histogram kernel)
-size_t topk_workspace_bytes(int n_queries, int K, int n_max, int n_win);
-void topk_carve(TopkArgs &a, void *ws, int n_queries, int n_win);
+// n_win: windows per query (scorer workgroups per query in the fused path, else 0 = own histogram kernel);
+// em_cap: entries per window region the scorer emits (0: none)
+size_t topk_workspace_bytes(int n_queries, int K, int n_max, int n_win, int em_cap = 0);
+void topk_carve(TopkArgs &a, void *ws, int n_queries, int n_win, int em_cap = 0);
 // hist_done: the scorer already wrote the histogram windows (fused path)
 hipError_t launch_topk(const TopkArgs &a, hipStream_t stream, bool hist_done = false);
 bool topk_uses_histogram(int n_max);

@@ -66,7 +66,8 @@ __global__ __launch_bounds__(256) void index_scores_f32_kernel(ScoreArgs a) {
 // their first loads, read the four 8 KiB blocks of each step together (on this
 // part that streams HBM about 7% faster than dealing the steps round-robin).
 // Optionally each workgroup also histograms the keys of the scores it writes,
-// for the top-k.
+// for the top-k, and (when the caller asks and its stretch fits in LDS) keeps
+// its keys and hands the selection its entries at and above a cut bin.
 namespace {
 constexpr int kWaveStep = 32;                         // entries per wave and step
 constexpr int kWgStep = kScoreWaves * kWaveStep;      // entries per workgroup step
@@ -74,13 +75,18 @@ constexpr int kScoreDepth = 2;                        // key steps in flight per
 typedef bf16x8_t KeyFrag[2][4];
 typedef u32x4_t KeyRaw[8];  // a wave-step of keys as loaded: 8 KiB, 16 B per lane per load
 constexpr int kRawRowWords = kDI / 2 + 4;  // LDS row of 128 bf16 + 16 B pad
+constexpr int kEmitMax = 8192;             // entries of a stretch whose keys stay in LDS for the emission
+constexpr int kEmitCapMax = 512;           // emitted entries per workgroup at most
 }  // namespace
 
 template <int kAct, bool kHist, int kDepth>
 __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(ScoreArgs a) {
     __shared__ uint32_t lh[kHist ? kTopkBins : 1];
+    __shared__ uint32_t lkeys[kHist ? kEmitMax : 1];  // keys of this workgroup's stretch (emission)
     __shared__ __attribute__((aligned(16))) uint32_t kraw[kScoreWaves][kWaveStep * kRawRowWords];
     __shared__ int s_red[4];
+    __shared__ int s_scan[4];  // the emission's scans (s_red may still be read after the window store)
+    __shared__ int s_cut;
     const int qi = blockIdx.y;
     const int b = qi / a.T;
     const int lane = threadIdx.x & 63;
@@ -122,6 +128,9 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(
     const int n_load = vis_steps - s0 < chunk ? (vis_steps - s0 > 0 ? vis_steps - s0 : 0) : chunk;
     const int stride = kWgStep;
     const int base0 = s0 * kWgStep + wave * kWaveStep;
+    // emission: the host enables it only when every stretch fits in lkeys
+    const bool emit = kHist && with_hist && a.em_cap > 0;
+    const int stretch0 = s0 * kWgStep;
 
     // Every load is unconditional (indices clamped into the visible rows) so
     // the loop body is straight-line code and the compiler can wait for one
@@ -184,10 +193,12 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(
         const float sv = j < nvis ? (g == 0 ? part[0] : part[1]) : -INFINITY;
         if (live && g < 2 && j < a.n_max) srow[j] = sv;
         if (with_hist) {
-            const uint32_t bin = order_key(sv) >> 20;
+            const uint32_t key = order_key(sv);
+            const uint32_t bin = key >> 20;
             const bool add = live && g < 2 && j < nvis;
             lds_hist_add(lh, bin, add);
             if (add) hmax = max(hmax, (int)bin);
+            if (emit && add) lkeys[j - stretch0] = key;
         }
     };
 
@@ -226,6 +237,12 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(
     if (with_hist) {
         const size_t w = (size_t)qi * gridDim.x + blockIdx.x;
         hist_window_store_top(lh, hmax, a.win_hdr + w, a.win_cnt + w * kTopkWin, s_red);
+        if (emit) {  // hist_window_store_top's barrier also orders the key stores
+            int n_st = min(nvis, (s0 + n_load) * kWgStep) - stretch0;
+            n_st = n_st > 0 ? n_st : 0;
+            emit_region<64 * kScoreWaves>(lh, lkeys, n_st, stretch0, a.em_cap, a.em_hdr + 2 * w,
+                                          a.em_key + w * a.em_cap, a.em_idx + w * a.em_cap, s_scan, &s_cut);
+        }
     }
 }
 
@@ -528,6 +545,20 @@ int tiled_windows(int B, int T, int n_max) {
     a.T = T;
     a.n_max = n_max;
     return tiled_plan(a).n_chunks;
+}
+
+int score_emit_cap(int n_max, int n_queries, int K) {
+    // every workgroup's stretch must fit in LDS: at most ceil(steps / workgroups) steps
+    const int wgs = score_workgroups(n_max, n_queries);
+    const int steps = (n_max + kWgStep - 1) / kWgStep;
+    const int chunk = (steps + wgs - 1) / wgs;
+    if ((long)chunk * kWgStep > kEmitMax) return 0;
+    // about twice a workgroup's expected share of the K selected entries, plus a margin
+    int cap = (2 * K / wgs + 48 + 15) / 16 * 16;
+    cap = cap < 32 ? 32 : (cap > kEmitCapMax ? kEmitCapMax : cap);
+    while (cap > 32 && (long)cap * wgs > kTopkMaxSlots) cap -= 16;
+    // the selection's radix pass over the emitted slots needs more slots than K
+    return (long)cap * wgs <= kTopkMaxSlots && (long)cap * wgs > K ? cap : 0;
 }
 
 int score_workgroups(int n_max, int n_queries) {

@@ -37,15 +37,19 @@ constexpr int kFinalGroup = 8;                           // selection: threads p
 constexpr int kSpecC = 2;                                // candidates per thread loaded in the first round
 
 
-struct TopkShared {
+// Shared state of the radix selection for a workgroup of NT threads.
+template <int NT>
+struct TopkSharedT {
     uint32_t hist[256];
-    uint64_t masks[2][kWaves][2];
+    uint64_t masks[2][NT / 64][2];
     int bcast[2];
 };
+using TopkShared = TopkSharedT<kWG>;
 
 // Wave 0 finds the histogram bin that holds the need-th largest element
 // (counting from bin 255 down) and publishes (bin, rank within the bin).
-__device__ __forceinline__ void find_bin_256(TopkShared &sh, int need) {
+template <int NT>
+__device__ __forceinline__ void find_bin_256(TopkSharedT<NT> &sh, int need) {
     const int lane = threadIdx.x & 63;
     if (threadIdx.x < 64) {
         uint32_t h[4];
@@ -76,10 +80,11 @@ __device__ __forceinline__ void find_bin_256(TopkShared &sh, int need) {
     }
 }
 
-// Exact top-k of one row (n visible entries) by one 1024-thread workgroup.
-template <bool kInLds>
+// Exact top-k of one row (n visible entries) by one workgroup of NT threads.
+template <bool kInLds, int NT = kWG>
 __device__ void topk_row(const float *__restrict__ row, int n, int K, int32_t *__restrict__ out,
-                         uint32_t *keys, TopkShared &sh) {
+                         uint32_t *keys, TopkSharedT<NT> &sh) {
+    constexpr int kWG = NT, kWaves = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (n <= K) {
         for (int i = tid; i < K; i += kWG) out[i] = i < n ? i : -1;
@@ -159,32 +164,6 @@ __device__ __forceinline__ int query_visible(const TopkArgs &a, int qi) {
     return n < a.n_max ? n : a.n_max;
 }
 
-// Block-wide exclusive scan for NT threads (a multiple of 64); s_wave holds
-// NT / 64 ints.  Two barriers.
-template <int NT>
-__device__ __forceinline__ int block_scan_excl(int x, int *s_wave, int *total) {
-    constexpr int NW = NT / 64;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int inc = x;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(inc, o);
-        if (lane >= o) inc += t;
-    }
-    if (lane == 63) s_wave[wave] = inc;
-    __syncthreads();
-    int before = 0, all = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const int c = s_wave[w];
-        before += w < wave ? c : 0;
-        all += c;
-    }
-    __syncthreads();
-    *total = all;
-    return before + inc - x;
-}
-
 // R consecutive scores j_first .. j_first + R - 1 of a row (0 past n).  Whole
 // 16-byte loads when the chunk lies inside the row and the row is aligned.
 template <int R>
@@ -249,15 +228,17 @@ __device__ __forceinline__ void classify_ordered(const float (&x)[R], int j_firs
     n_eq += tot >> 16;
 }
 
-struct SelectShared {
+template <int NT>
+struct SelectSharedT {
     uint32_t words[256];               // second-level histogram
     int32_t sel[kTopkMaxK];            // chosen candidates in index order (ordered selection)
     uint32_t sub_key[kSubCap];
     int32_t sub_idx[kSubCap];
-    int s_wave[kWaves];
+    int s_wave[NT / 64];
     int cnt[2];
     int bcast[2];
 };
+using SelectShared = SelectSharedT<kWG>;
 
 // Ordered selection: v[0..na) (entries above the threshold bin) and the
 // candidates c_key/c_idx[0..nc) (inside it) are both in index order, na < K,
@@ -269,8 +250,10 @@ struct SelectShared {
 // LDS first).  The chosen ones are compacted in index order and merged with v
 // into `out` by binary search.  Returns false (nothing written, same in every
 // thread) if b2 holds more than kSubCap candidates.
+template <int NT = kWG>
 __device__ bool select_ordered(const int32_t *v, int na, const uint32_t *c_key, const int32_t *c_idx, int nc, int K,
-                               int32_t *out, SelectShared &ss) {
+                               int32_t *out, SelectSharedT<NT> &ss) {
+    constexpr int kWG = NT;
     constexpr int kMaxC = kTopkCand / kWG;
     const int tid = threadIdx.x;
     const int need = K - na;
@@ -403,13 +386,49 @@ __global__ __launch_bounds__(kAuxThreads) void topk_hist_kernel(TopkArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Scan a row into the index-ordered lists of entries above the threshold bin
+// (v) and inside it (c_key, c_idx), then select.  The first round of scores
+// (xa: kRound per thread, thread t taking entries kRound t ..) is loaded by the
+// caller, so it can be in flight while the threshold is worked out; later rounds
+// are loaded one ahead of the round being classified.  Each thread takes
+// consecutive scores, so the lists come out in index order.  Returns false
+// (nothing written, the same in every thread) if a list overflowed.
+constexpr int kRound = 16;  // scores per thread per round
+template <int NT>
+struct ScanSharedT {
+    int32_t v[kTopkMaxK];
+    uint32_t c_key[kTopkCand];
+    int32_t c_idx[kTopkCand];
+    SelectSharedT<NT> ss;
+};
+using ScanShared = ScanSharedT<kWG>;
+
+template <int NT = kWG>
+__device__ bool scan_and_select(const float *row, int n, int n_max, bool vec, int K, uint32_t bin, float (&xa)[kRound],
+                                int32_t *out, ScanSharedT<NT> &sc, int *s_red) {
+    constexpr int kWG = NT;
+    constexpr int kSpan = kRound * kWG;
+    const int tid = threadIdx.x;
+    float xb[kRound];
+    int na = 0, nc = 0;
+    for (int j0 = 0; j0 < n; j0 += 2 * kSpan) {
+        if (j0 + kSpan < n) load_chunk<kRound>(row, j0 + kSpan + kRound * tid, n, n_max, vec, xb);
+        classify_ordered<kWG, kRound>(xa, j0 + kRound * tid, n, bin, s_red, na, nc, sc.v, K, sc.c_key, sc.c_idx,
+                                      kTopkCand);
+        if (j0 + kSpan >= n) break;
+        if (j0 + 2 * kSpan < n) load_chunk<kRound>(row, j0 + 2 * kSpan + kRound * tid, n, n_max, vec, xa);
+        classify_ordered<kWG, kRound>(xb, j0 + kSpan + kRound * tid, n, bin, s_red, na, nc, sc.v, K, sc.c_key,
+                                      sc.c_idx, kTopkCand);
+    }
+    __syncthreads();
+    if (!(na < K && nc <= kTopkCand && na + nc >= K)) return false;
+    return select_ordered(sc.v, na, sc.c_key, sc.c_idx, nc, K, out, sc.ss);
+}
+
 // One workgroup per query (rows up to kTopkOneKernelMax, or many queries):
 // threshold from the histogram windows, scan and selection.
 __global__ __launch_bounds__(kWG) void topk_onekernel_kernel(TopkArgs a) {
-    __shared__ __attribute__((aligned(16))) int32_t v[kTopkMaxK];
-    __shared__ uint32_t c_key[kTopkCand];
-    __shared__ int32_t c_idx[kTopkCand];
-    __shared__ SelectShared ss;
+    __shared__ __attribute__((aligned(16))) ScanShared sc;
     __shared__ TopkShared sh;
     __shared__ uint32_t s_hist[kTopkWin];
     __shared__ int s_red[kWaves];
@@ -423,32 +442,141 @@ __global__ __launch_bounds__(kWG) void topk_onekernel_kernel(TopkArgs a) {
         for (int i = tid; i < K; i += kWG) out[i] = i < n ? i : -1;
         return;
     }
-    // The first round of scores goes out together with the window loads;
-    // later rounds are loaded one ahead of the round being classified.  Each
-    // thread takes consecutive scores, so the lists come out in index order.
-    constexpr int kRound = 16;  // scores per thread per round
-    constexpr int kSpan = kRound * kWG;
+    // the first round of scores goes out together with the window loads
     const bool vec = (a.n_max & 3) == 0 && ((uintptr_t)a.scores & 15) == 0;
-    float xa[kRound], xb[kRound];
+    float xa[kRound];
     load_chunk<kRound>(row, kRound * tid, n, a.n_max, vec, xa);
     const uint32_t bin = window_threshold(a.win_hdr + (size_t)qi * a.n_win,
                                           a.win_cnt + (size_t)qi * a.n_win * kTopkWin, a.n_win, K, s_red, s_hist);
-    bool ok = bin != kNoBin;
+    bool ok = bin != kNoBin && scan_and_select(row, n, a.n_max, vec, K, bin, xa, out, sc, s_red);
+    if (!ok) {
+        __syncthreads();
+        topk_row<false>(row, n, K, out, nullptr, sh);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Selection from the entries the decode scorer emitted (fused decode path).
+// Per query, in one load round: the histogram windows (which give the
+// threshold bin), each region's header (cut bin, count) and every emitted slot
+// (regions in stretch order, each region's entries in index order, so slot
+// order is index order; slot r * kWG + t goes to thread t, so each load
+// instruction of a wave reads 256 contiguous bytes; the scorer zero-fills a
+// region's slots past its count, and no real key is 0).  If every region's cut
+// lies at or below the threshold bin, the emitted entries hold every entry at
+// or above it: they are split into the above and candidate lists in slot
+// order (per round and wave a ballot, one scan of the round-by-wave counts)
+// and selected as usual.  Otherwise (a region with too many high entries to
+// emit them all) the whole row is scanned with the threshold instead, and
+// without a usable threshold the exact radix selection runs.
+constexpr int kListRounds = kTopkMaxSlots / kWG;  // rounds of kWG slots at most
+__global__ __launch_bounds__(kWG) void topk_lists_kernel(TopkArgs a) {
+    __shared__ __attribute__((aligned(16))) ScanShared sc;
+    __shared__ TopkShared sh;
+    __shared__ uint32_t s_hist[kTopkWin];
+    __shared__ int s_red[kWaves];
+    __shared__ uint32_t s_base[kListRounds * kWaves];  // packed (above, candidates) before each (round, wave)
+    __shared__ uint32_t s_all;
+    const int qi = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int K = a.K;
+    const float *row = a.scores + (size_t)qi * a.n_max;
+    int32_t *out = a.idx + (size_t)qi * K;
+    const int R = a.n_win, cap = a.em_cap, slots = R * cap;
+    const int rounds = (slots + kWG - 1) / kWG;  // the same in every thread
+    const size_t q0 = (size_t)qi * R;
+    const uint32_t *ekey = a.em_key + q0 * cap;
+    const int32_t *eidx = a.em_idx + q0 * cap;
+    // load round: this thread's slots, a region header, then the windows
+    uint32_t key[kListRounds];
+    int32_t idx[kListRounds];
+#pragma unroll
+    for (int r = 0; r < kListRounds; ++r) {
+        if (r < rounds) {
+            const int p = r * kWG + tid;
+            key[r] = p < slots ? ekey[p] : 0u;
+            idx[r] = p < slots ? eidx[p] : 0;
+        }
+    }
+    int cut = 0, cnt = 0;
+    if (tid < R) {
+        cut = a.em_hdr[2 * (q0 + tid)];
+        cnt = a.em_hdr[2 * (q0 + tid) + 1];
+    }
+    const int n = query_visible(a, qi);
+    if (n <= K) {
+        for (int i = tid; i < K; i += kWG) out[i] = i < n ? i : -1;
+        return;
+    }
+    const uint32_t bin = window_threshold(a.win_hdr + q0, a.win_cnt + q0 * kTopkWin, R, K, s_red, s_hist);
+    // every region emitted all of its entries at or above the threshold bin?
+    bool ok = bin != kNoBin && !__syncthreads_or(tid < R && ((uint32_t)cut > bin || cnt > cap));
     if (ok) {
-        int na = 0, nc = 0;
-        for (int j0 = 0; j0 < n; j0 += 2 * kSpan) {
-            if (j0 + kSpan < n) load_chunk<kRound>(row, j0 + kSpan + kRound * tid, n, a.n_max, vec, xb);
-            classify_ordered<kWG, kRound>(xa, j0 + kRound * tid, n, bin, s_red, na, nc, v, K, c_key, c_idx, kTopkCand);
-            if (j0 + kSpan >= n) break;
-            if (j0 + 2 * kSpan < n) load_chunk<kRound>(row, j0 + 2 * kSpan + kRound * tid, n, a.n_max, vec, xa);
-            classify_ordered<kWG, kRound>(xb, j0 + kSpan + kRound * tid, n, bin, s_red, na, nc, v, K, c_key, c_idx,
-                                          kTopkCand);
+        // pass 1: per (round, wave) counts of above-threshold and candidate slots
+        uint32_t cls = 0;  // bit 2r: above, bit 2r + 1: candidate
+#pragma unroll
+        for (int r = 0; r < kListRounds; ++r) {
+            if (r < rounds) {
+                const uint32_t b = key[r] >> 20;
+                const bool ga = key[r] != 0u && b > bin, gc = key[r] != 0u && b == bin;
+                cls |= (uint32_t)ga << (2 * r) | (uint32_t)gc << (2 * r + 1);
+                const uint32_t na = (uint32_t)__popcll(__ballot(ga)), nc = (uint32_t)__popcll(__ballot(gc));
+                if (lane == 0) s_base[r * kWaves + wave] = na | nc << 16;
+            }
         }
         __syncthreads();
-        ok = na < K && nc <= kTopkCand && na + nc >= K;
-        if (ok) {
-            ok = select_ordered(v, na, c_key, c_idx, nc, K, out, ss);
+        if (tid < 64) {  // exclusive scan of the (round, wave) counts in slot order, 2 entries per lane
+            const int m = rounds * kWaves;
+            uint32_t c[2], sum = 0;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                c[i] = 2 * tid + i < m ? s_base[2 * tid + i] : 0u;
+                sum += c[i];
+            }
+            uint32_t inc = sum;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t t = __shfl_up(inc, o);
+                if (tid >= o) inc += t;
+            }
+            uint32_t run = inc - sum;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                if (2 * tid + i < m) s_base[2 * tid + i] = run;
+                run += c[i];
+            }
+            if (tid == 63) s_all = inc;
         }
+        __syncthreads();
+        const uint32_t all = s_all;
+        const int na = (int)(all & 0xFFFFu), nc = (int)(all >> 16);
+        ok = na < K && nc <= kTopkCand && na + nc >= K;
+        if (ok) {  // pass 2: slot-ordered writes into the two lists
+            const uint64_t lt = lanemask_lt();
+#pragma unroll
+            for (int r = 0; r < kListRounds; ++r) {
+                if (r < rounds) {
+                    const bool ga = (cls >> (2 * r)) & 1u, gc = (cls >> (2 * r + 1)) & 1u;
+                    const uint64_t mga = __ballot(ga), mgc = __ballot(gc);
+                    const uint32_t base = s_base[r * kWaves + wave];
+                    if (ga) sc.v[(base & 0xFFFFu) + __popcll(mga & lt)] = idx[r];
+                    if (gc) {
+                        const int pos = (int)(base >> 16) + __popcll(mgc & lt);
+                        sc.c_key[pos] = key[r];
+                        sc.c_idx[pos] = idx[r];
+                    }
+                }
+            }
+            __syncthreads();
+            ok = select_ordered(sc.v, na, sc.c_key, sc.c_idx, nc, K, out, sc.ss);
+        }
+    }
+    if (!ok && bin != kNoBin) {  // lists not usable: scan the row with the threshold
+        __syncthreads();
+        const bool vec = (a.n_max & 3) == 0 && ((uintptr_t)a.scores & 15) == 0;
+        float xa[kRound];
+        load_chunk<kRound>(row, kRound * tid, n, a.n_max, vec, xa);
+        ok = scan_and_select(row, n, a.n_max, vec, K, bin, xa, out, sc, s_red);
     }
     if (!ok) {
         __syncthreads();
@@ -464,8 +592,9 @@ __global__ __launch_bounds__(kWG) void topk_onekernel_kernel(TopkArgs a) {
 // [0] above count (0xFFFFFFFF when a list overflowed or there is no usable
 // threshold), [1] candidate count, then the above list, candidate keys and
 // candidate indices.
-// kVec: the rows are 16-byte aligned and n_max is a multiple of 4 (whole
-// 16-byte score loads; decided on the host, so the loads need no branch).
+// kVec: the rows are 16-byte aligned and n_max is a multiple of kPerThread
+// (whole 16-byte score loads, a thread's chunk never crosses the row end;
+// decided on the host, so the loads need no branch).
 template <bool kVec>
 __global__ __launch_bounds__(kAuxThreads) void topk_filter_kernel(TopkArgs a) {
     __shared__ int32_t l_above[kFltAboveCap];
@@ -485,7 +614,7 @@ __global__ __launch_bounds__(kAuxThreads) void topk_filter_kernel(TopkArgs a) {
     // do leaves after the window merge (whose result it then ignores).
     const int seq_len = a.seq_len[qi / a.T], q_pos = a.q_pos[qi];  // read now, used after the merge
     float x[kPerThread];
-    if (kVec) {  // n_max % 4 == 0, so a chunk starting inside the row ends inside it
+    if (kVec) {  // n_max % kPerThread == 0, so a chunk starting inside the row ends inside it
         const int jf = j_first < a.n_max ? j_first : a.n_max - kPerThread;
 #pragma unroll
         for (int k = 0; k < kPerThread; k += 4) {
@@ -653,21 +782,26 @@ static int hist_chunk(int n_max, int nw) {
     return (per + kTopkAuxChunk - 1) / kTopkAuxChunk * kTopkAuxChunk;
 }
 
-size_t topk_workspace_bytes(int n_queries, int K, int n_max, int n_win) {
+size_t topk_workspace_bytes(int n_queries, int K, int n_max, int n_win, int em_cap) {
     (void)K;
     if (!topk_uses_histogram(n_max)) return 0;
     const size_t Q = (size_t)n_queries;
     const size_t nw = (size_t)n_windows(n_max, n_win, n_queries);
     size_t b = Q * nw * 4 + Q * nw * kTopkWin * 4 + Q * 4 + 4 * 256;
-    if (!one_kernel(n_max, n_queries)) b += Q * (size_t)n_filters(n_max) * kFltRegionWords * 4;
+    if (em_cap > 0) {
+        b += Q * nw * (2 + 2 * (size_t)em_cap) * 4 + 3 * 256;
+    } else if (!one_kernel(n_max, n_queries)) {
+        b += Q * (size_t)n_filters(n_max) * kFltRegionWords * 4;
+    }
     return b;
 }
 
 static inline char *align256(char *p) { return (char *)(((uintptr_t)p + 255) & ~(uintptr_t)255); }
 
-void topk_carve(TopkArgs &a, void *ws, int n_queries, int n_win) {
+void topk_carve(TopkArgs &a, void *ws, int n_queries, int n_win, int em_cap) {
     a.n_win = n_windows(a.n_max, n_win, n_queries);
     a.hist_chunk = hist_chunk(a.n_max, a.n_win);
+    a.em_cap = 0;
     if (!topk_uses_histogram(a.n_max)) return;
     const size_t Q = (size_t)n_queries;
     char *p = align256((char *)ws);
@@ -678,6 +812,14 @@ void topk_carve(TopkArgs &a, void *ws, int n_queries, int n_win) {
     a.bin = (uint32_t *)p;
     p = align256(p + Q * 4);
     a.flt = (uint32_t *)p;
+    if (em_cap > 0) {  // the emitted regions take the place of the filter lists
+        a.em_cap = em_cap;
+        a.em_hdr = (int32_t *)p;
+        p = align256(p + Q * a.n_win * 2 * 4);
+        a.em_key = (uint32_t *)p;
+        p = align256(p + Q * a.n_win * (size_t)em_cap * 4);
+        a.em_idx = (int32_t *)p;
+    }
 }
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t stream, bool hist_done) {
@@ -686,13 +828,17 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t stream, bool hist_done) {
         hipLaunchKernelGGL(topk_lds_kernel, dim3(Q), dim3(kWG), 0, stream, a);
         return hipGetLastError();
     }
+    if (a.em_cap > 0) {  // the scorer wrote the windows and its emitted entries
+        hipLaunchKernelGGL(topk_lists_kernel, dim3(Q), dim3(kWG), 0, stream, a);
+        return hipGetLastError();
+    }
     if (!hist_done) hipLaunchKernelGGL(topk_hist_kernel, dim3(a.n_win, Q), dim3(kAuxThreads), 0, stream, a);
     if (one_kernel(a.n_max, Q)) {
         hipLaunchKernelGGL(topk_onekernel_kernel, dim3(Q), dim3(kWG), 0, stream, a);
         return hipGetLastError();
     }
     const int nf = n_filters(a.n_max);
-    if ((a.n_max & 3) == 0 && ((uintptr_t)a.scores & 15) == 0 && a.n_max >= kPerThread)
+    if (a.n_max % kPerThread == 0 && ((uintptr_t)a.scores & 15) == 0)
         hipLaunchKernelGGL(topk_filter_kernel<true>, dim3(nf, Q), dim3(kAuxThreads), 0, stream, a);
     else
         hipLaunchKernelGGL(topk_filter_kernel<false>, dim3(nf, Q), dim3(kAuxThreads), 0, stream, a);

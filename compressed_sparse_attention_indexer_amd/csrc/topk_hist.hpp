@@ -11,6 +11,32 @@ namespace csa {
 
 constexpr uint32_t kNoBin = 0xFFFFFFFFu;
 
+// Block-wide exclusive scan for NT threads (a multiple of 64); s_wave holds
+// NT / 64 ints.  Two barriers.
+template <int NT>
+__device__ __forceinline__ int block_scan_excl(int x, int *s_wave, int *total) {
+    constexpr int NW = NT / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int inc = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(inc, o);
+        if (lane >= o) inc += t;
+    }
+    if (lane == 63) s_wave[wave] = inc;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const int c = s_wave[w];
+        before += w < wave ? c : 0;
+        all += c;
+    }
+    __syncthreads();
+    *total = all;
+    return before + inc - x;
+}
+
 // LDS histogram add.  Scores often crowd into one bin, and same-address LDS
 // atomics serialize lane by lane, so lanes that share the first active lane's
 // bin are counted with one atomic; the other lanes add on their own.
@@ -135,6 +161,78 @@ __device__ __forceinline__ uint32_t window_threshold(const int32_t *hdr, const u
     const uint32_t result = (uint32_t)s_red[0];
     __syncthreads();
     return result;
+}
+
+// A scorer workgroup's entries for the selection (fused decode path): every
+// entry of its stretch whose key bin is at or above `cut`, the lowest bin with
+// at most `cap` entries at or above it.  lh is the stretch's kTopkBins-bin key
+// histogram, keys[i] the key of entry first + i (i < n).  Writes hdr = {cut,
+// count} and the emitted keys and indices in index order, keys past the count
+// zeroed.  The selection can
+// use the lists when every region's cut lies at or below the threshold bin:
+// then each holds all of its region's entries at or above the threshold.
+// NT threads (a multiple of 64 dividing kTopkBins); s_wave NT / 64 ints.
+template <int NT>
+__device__ void emit_region(const uint32_t *lh, const uint32_t *keys, int n, int first, int cap, int32_t *hdr,
+                            uint32_t *okey, int32_t *oidx, int *s_wave, int *s_cut) {
+    constexpr int kPer = kTopkBins / NT;
+    constexpr int kE = 8;  // consecutive entries per thread and round of the compaction
+    const int tid = threadIdx.x;
+    const int v = NT - 1 - tid;  // this thread's bins [kPer v, kPer v + kPer): thread 0 takes the top range
+    uint32_t h[kPer];
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        h[i] = lh[kPer * v + i];
+        c += (int)h[i];
+    }
+    int tot;
+    const int above = block_scan_excl<NT>(c, s_wave, &tot);  // entries in the bins above this thread's range
+    if (tot <= cap) {
+        if (tid == 0) *s_cut = 0;
+    } else if (above <= cap && above + c > cap) {  // the range where the count from the top passes cap
+        int run = above, cut = kPer * v + kPer;
+        for (int i = kPer - 1; i >= 0; --i) {
+            run += (int)h[i];
+            if (run > cap) break;
+            cut = kPer * v + i;
+        }
+        *s_cut = cut;
+    }
+    __syncthreads();
+    const uint32_t cut = (uint32_t)*s_cut;
+    int written = 0;
+    for (int i0 = 0; i0 < n; i0 += NT * kE) {
+        uint32_t k[kE];
+        int m = 0;
+#pragma unroll
+        for (int e = 0; e < kE; ++e) {
+            const int i = i0 + kE * tid + e;
+            k[e] = i < n ? keys[i] : 0u;
+            m += i < n && (k[e] >> 20) >= cut;
+        }
+        int rt;
+        int pos = written + block_scan_excl<NT>(m, s_wave, &rt);
+#pragma unroll
+        for (int e = 0; e < kE; ++e) {
+            const int i = i0 + kE * tid + e;
+            if (i < n && (k[e] >> 20) >= cut) {
+                if (pos < cap) {
+                    okey[pos] = k[e];
+                    oidx[pos] = first + i;
+                }
+                ++pos;
+            }
+        }
+        written += rt;
+    }
+    // the slots past the count read as key 0 (no real key is 0), so the
+    // selection can tell used slots without the count
+    for (int i = written + tid; i < cap; i += NT) okey[i] = 0u;
+    if (tid == 0) {
+        hdr[0] = (int32_t)cut;
+        hdr[1] = written;  // at most cap by the choice of cut
+    }
 }
 
 }  // namespace csa

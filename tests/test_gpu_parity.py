@@ -137,6 +137,58 @@ def test_flash_sharp_logits_and_sink():
     check_whole_step(case, ATT_TOL_BF16)
 
 
+# --------------------------------------------------------------------------- tensor-level calls
+
+def test_tensor_level_attention_on_a_side_stream():
+    """csa.attention with sizes taken from the tensors and keyword options, on
+    a stream other than the current one (its temporaries and outputs are made
+    on that stream), against the oracle: the selected sets under the band rule,
+    attention on the GPU's own set."""
+    wl, sl = flash_case("flash_tensor_api", [4 * 9000 + 1, 4 * 3000 + 2, 4 * 100 + 3])
+    case = make_case_with_lens(wl, sl)
+    say(f"[case] {wl.name} tensor-level attention on a side stream")
+    dc = DeviceCase(case)
+    side = torch.cuda.Stream()
+    out, lse, idx = csa.attention(dc.q, dc.q_idx, dc.w, dc.k_idx, dc.kv, dc.win, case.seq_len.tolist(), dc.q_pos,
+                                  dc.sink, topk=wl.topk, window=wl.window, ratio=wl.ratio, stream=side)
+    side.synchronize()
+    g_idx, g_out, g_lse = idx.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy()
+    o_scores = oracle_scores(case)
+    o_idx = oracle.topk(o_scores, case.seq_len, case.q_pos, ratio=wl.ratio, k=wl.topk)
+    assert_topk_band(g_idx, o_idx, o_scores, case)
+    o_out, o_lse = oracle_sparse(case, g_idx)
+    assert_attention_close(g_out, o_out, ATT_TOL_BF16, "out")
+    np.testing.assert_allclose(g_lse, o_lse, atol=1e-3, rtol=0)
+
+
+def test_tensor_level_ops_match_the_abi_calls():
+    """csa.index_scores, csa.topk, csa.sparse_mqa and csa.hca_mqa give the same
+    results as the struct-based calls they marshal to."""
+    wl, sl = flash_case("flash_tensor_ops", [4 * 5000 + 2, 128 * 37 + 5], hca=128)
+    case = make_case_with_lens(wl, sl)
+    say(f"[case] {wl.name} tensor-level ops")
+    dc = DeviceCase(case)
+    dims = dc.csa_dims()
+    s_ref = csa.csa_index_scores(dims, dc.q_idx, dc.w, dc.k_idx_p, dc.seq_len, dc.q_pos)
+    s = csa.index_scores(dc.q_idx, dc.w, dc.k_idx, dc.seq_len, dc.q_pos, ratio=wl.ratio)
+    np.testing.assert_array_equal(_np(s), _np(s_ref))
+    i_ref = csa.csa_topk_select(dims, s_ref, dc.seq_len, dc.q_pos)
+    i = csa.topk(s, dc.seq_len, dc.q_pos, topk=wl.topk, ratio=wl.ratio)
+    np.testing.assert_array_equal(_np(i), _np(i_ref))
+    o_ref, l_ref = csa.csa_sparse_mqa_decode(dims, dc.q, dc.kv_p, None, i_ref, dc.win_p, None, dc.win_pos0,
+                                             dc.win_rows, dc.seq_len, dc.q_pos, dc.sink)
+    o, l = csa.sparse_mqa(dc.q, dc.kv, i, dc.win, dc.seq_len, dc.q_pos, dc.sink, window=wl.window, ratio=wl.ratio,
+                          win_pos0=dc.win_pos0)
+    np.testing.assert_array_equal(_np(o), _np(o_ref))
+    np.testing.assert_array_equal(_np(l), _np(l_ref))
+    h_ref, hl_ref = csa.hca_mqa_decode(dc.hca_dims(), dc.hca_q, dc.hca_kv_p, None, dc.hca_win_p, None, dc.win_pos0,
+                                       dc.win_rows, dc.seq_len, dc.q_pos, dc.hca_sink)
+    h, hl = csa.hca_mqa(dc.hca_q, dc.hca_kv, dc.hca_win, case.seq_len.tolist(), dc.q_pos, dc.hca_sink,
+                        window=wl.window, ratio=128)
+    np.testing.assert_array_equal(_np(h), _np(h_ref))
+    np.testing.assert_array_equal(_np(hl), _np(hl_ref))
+
+
 # --------------------------------------------------------------------------- top-k alone (integer work: exact)
 
 def _topk_case(n_vis_list, n_max, K, seed, ties=False):
@@ -160,6 +212,7 @@ def _topk_case(n_vis_list, n_max, K, seed, ties=False):
     ([262144, 200000, 300, 262144], 262144, 512, True),
     ([262144], 262144, 1, False),
     ([70001, 65537], 70001, 512, True),  # many-workgroup path with a row length that is not a multiple of 4
+    ([65540], 65540, 512, False),        # many-workgroup path, row length 4 mod 8 (last chunk ends mid-thread)
 ])
 def test_topk_exact(n_vis, n_max, K, ties):
     say(f"[case] topk n_vis={n_vis} n_max={n_max} K={K} ties={ties}")
@@ -229,6 +282,32 @@ def test_fused_selection_equals_standalone_topk(act):
     np.testing.assert_array_equal(t_idx, g_idx)
     want = oracle.topk(g_scores, case.seq_len, case.q_pos, ratio=4, k=512)
     np.testing.assert_array_equal(g_idx, want)
+
+
+def test_fused_selection_when_emitted_lists_fall_short():
+    """The decode scorer hands the selection only its workgroups' highest
+    entries.  Sequence 0: a contiguous block of 700 strong index keys puts the
+    whole top-512 into one or two scorer workgroups, more than they can emit,
+    so the selection scans the row instead.  Sequence 1: every index key equal,
+    so every score ties and only the exact radix selection can decide.  Both
+    must equal the oracle's top-k on the same scores, and the attention must
+    match on that selection."""
+    wl, sl = flash_case("flash_lists_fall_short", [4 * 100000, 4 * 60000])
+    case = make_case_with_lens(wl, sl)
+    k0 = inputs.bf16_to_f32(case.k_idx[0])
+    k0[50000:50700] *= np.float32(4.0)
+    case.k_idx[0] = inputs.bf16_bits(k0)
+    case.k_idx[1][:] = case.k_idx[1][0]
+    say(f"[case] {wl.name}: clustered tops and all-equal scores through the fused call")
+    dc = DeviceCase(case)
+    g_scores, g_idx, g_out, g_lse = run_fused(dc)
+    want = oracle.topk(g_scores, case.seq_len, case.q_pos, ratio=4, k=512)
+    np.testing.assert_array_equal(g_idx, want)
+    assert set(g_idx[0, 0].tolist()) <= set(range(50000, 50700))
+    np.testing.assert_array_equal(g_idx[1, 0], np.arange(512))
+    o_out, o_lse = oracle_sparse(case, g_idx)
+    assert_attention_close(g_out, o_out, ATT_TOL_BF16, "out")
+    np.testing.assert_allclose(g_lse, o_lse, atol=1e-3, rtol=0)
 
 
 @pytest.mark.parametrize("n", [40000, 262144])
