@@ -20,6 +20,7 @@ from ._lib import (CSA_ACT_NONE, CSA_ACT_RELU, CSA_BF16, CSA_F32, CSA_OP_ATTENTI
 __all__ = ["CsaDims", "CsaError", "make_dims", "workspace_size", "ptr_array", "csa_index_scores",
            "csa_index_scores_fp8", "CsaCompressDims", "make_compress_dims", "compress_workspace_size",
            "csa_compress", "csa_topk_select", "csa_sparse_mqa_decode", "hca_mqa_decode", "csa_attention",
+           "csa_attention_noalloc",
            "attention", "index_scores", "index_scores_fp8", "topk", "sparse_mqa", "hca_mqa", "load_library",
            "CSA_F32", "CSA_BF16", "CSA_ACT_RELU", "CSA_ACT_NONE"]
 
@@ -197,6 +198,23 @@ def csa_attention(dims: CsaDims, q, q_idx, w, k_idx: PtrArg, kv: PtrArg, v: PtrA
             ctypes.byref(dims), _p(q), _p(q_idx), _p(w), kip, kp, vp, wp, wvp, _p(win_pos0), _p(win_rows),
             _p(seq_len), _p(q_pos), _p(sink), _p(out), _p(lse), _p(topk_idx_out), _p(scores_out), _p(ws), nws,
             st), "csa_attention")
+    return out, lse
+
+
+def csa_attention_noalloc(dims: CsaDims, q, q_idx, w, k_idx: PtrArg, kv: PtrArg, v: PtrArg, win: PtrArg,
+                          win_v: PtrArg, win_pos0, win_rows, seq_len, q_pos, sink, out=None, lse=None,
+                          want_lse=True, topk_idx_out=None, scores_out=None, stream=None):
+    """csa_attention on the library's own static work area (no workspace
+    argument); returns (out, lse).  Pass prebuilt device pointer arrays and
+    outputs to keep the call free of allocations."""
+    dev = q.device
+    with _on_stream(stream) as st:
+        out, lse = _attn_outputs(dims, dev, out, lse, want_lse)
+        (kip, k0), (kp, k1), (vp, k2), (wp, k3), (wvp, k4) = (_pa(x, dev) for x in (k_idx, kv, v, win, win_v))
+        check(load_library().csa_attention_noalloc(
+            ctypes.byref(dims), _p(q), _p(q_idx), _p(w), kip, kp, vp, wp, wvp, _p(win_pos0), _p(win_rows),
+            _p(seq_len), _p(q_pos), _p(sink), _p(out), _p(lse), _p(topk_idx_out), _p(scores_out), st),
+            "csa_attention_noalloc")
     return out, lse
 
 

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libcsa.so")
-SOURCES = ["api.cpp", "scorer.hip", "scorer_fp8.hip", "topk.hip", "attention.hip", "compressor.hip"]
+SOURCES = ["api.cpp", "scorer.hip", "scorer_fp8.hip", "topk.hip", "attention.hip", "compressor.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 

@@ -7,12 +7,14 @@
 #include <cstdio>
 #include <string>
 
+#include "api_internal.hpp"
 #include "launch.hpp"
 
 namespace {
-
 thread_local std::string g_last_error;
+}  // namespace
 
+namespace csa_api {
 csa_status fail(csa_status s, const char *fmt, ...) {
     char buf[512];
     va_list ap;
@@ -22,6 +24,10 @@ csa_status fail(csa_status s, const char *fmt, ...) {
     g_last_error = buf;
     return s;
 }
+}  // namespace csa_api
+
+namespace {
+using csa_api::fail;
 
 csa_status ok() {
     g_last_error.clear();
@@ -471,6 +477,18 @@ csa_status csa_attention(const csa_dims *d, const void *q, const void *q_idx, co
                          const int32_t *win_rows, const int32_t *seq_len, const int32_t *q_pos, const float *sink,
                          float *out, float *lse, int32_t *topk_idx_out, float *scores_out, void *ws,
                          size_t ws_bytes, void *stream) {
+    return csa_api::attention_impl(d, q, q_idx, w, k_idx, kv, v, win, win_v, win_pos0, win_rows, seq_len, q_pos,
+                                   sink, out, lse, topk_idx_out, scores_out, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+csa_status csa_api::attention_impl(const csa_dims *d, const void *q, const void *q_idx, const float *w,
+                                   const void *const *k_idx, const void *const *kv, const void *const *v,
+                                   const void *const *win, const void *const *win_v, const int32_t *win_pos0,
+                                   const int32_t *win_rows, const int32_t *seq_len, const int32_t *q_pos,
+                                   const float *sink, float *out, float *lse, int32_t *topk_idx_out,
+                                   float *scores_out, void *ws, size_t ws_bytes, void *stream) {
     csa_status s;
     if ((s = check_common(d)) || (s = check_scores(d)) || (s = check_topk(d)) || (s = check_attn(d))) return s;
     if ((s = check_attn_ptrs(q, kv, v, win, win_v, win_pos0, win_rows, seq_len, q_pos, sink, out, lse))) return s;
@@ -511,5 +529,3 @@ csa_status csa_attention(const csa_dims *d, const void *q, const void *q_idx, co
                                      base + off_mqa, d->topk + d->window);
     return hip_status(csa::launch_mqa(ma, d->dtype, st), "csa_attention/attention");
 }
-
-}  // extern "C"

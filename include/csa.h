@@ -38,7 +38,9 @@
  * allocates device memory, never synchronizes, and keeps no pointer after a
  * call returns.  Work is enqueued on `stream`; buffers must stay alive until
  * the stream passes the call.  Calls are thread-safe (no shared state except
- * a thread-local error string).
+ * a thread-local error string); the one exception is csa_attention_noalloc,
+ * whose work area is a static device array of the library shared by every
+ * call on a GPU (see there).
  *
  * Errors: all argument checks run on the host before anything is enqueued; on
  * error nothing is launched and the status says why (details in
@@ -225,6 +227,30 @@ csa_status csa_attention(const csa_dims *dims, const void *q, const void *q_idx,
                          const int32_t *seq_len, const int32_t *q_pos, const float *sink,
                          float *out, float *lse, int32_t *topk_idx_out, float *scores_out,
                          void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * csa_attention without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture that may not allocate, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments, results and
+ * errors as csa_attention, minus (workspace, ws_bytes): the work area is a
+ * device array of 64 MiB inside the library, one per GPU it runs on, held until
+ * the process ends.  Sizes whose work area (csa_workspace_size with
+ * CSA_OP_ATTENTION) exceeds 64 MiB return CSA_ERR_WORKSPACE before anything is
+ * enqueued; the decode shapes fit (batch 4 at 262,144 entries needs about
+ * 7 MiB), a 2,048-query prefill chunk over 262,144 entries does not.  The call
+ * allocates nothing; the first call on a device looks up the array's address
+ * there.  `stream` must belong to the current device (else
+ * CSA_ERR_UNSUPPORTED).  Every call on a GPU shares that GPU's array: calls
+ * that overlap on one GPU (other streams or threads) race and must be
+ * serialized by the caller.
+ */
+csa_status csa_attention_noalloc(const csa_dims *dims, const void *q, const void *q_idx, const float *w,
+                                 const void *const *k_idx, const void *const *kv, const void *const *v,
+                                 const void *const *win, const void *const *win_v,
+                                 const int32_t *win_pos0, const int32_t *win_rows,
+                                 const int32_t *seq_len, const int32_t *q_pos, const float *sink,
+                                 float *out, float *lse, int32_t *topk_idx_out, float *scores_out,
+                                 void *stream);
 
 /*
  * KV / index-key compressor -- the step that produces the compressed caches

@@ -148,6 +148,28 @@ def test_workspace_checks():
     assert _fused(f, ws=FAKE, nws=csa.workspace_size(f, _lib.CSA_OP_ATTENTION) - 1) == _lib.CSA_ERR_WORKSPACE
 
 
+def test_noalloc_rejects_before_any_launch():
+    """The allocation-free fused call checks its sizes first: dims errors as
+    csa_attention, and a work area beyond its 64 MiB static one (the 2,048-query
+    prefill chunk needs its 2 GiB of scores) is refused before any HIP call."""
+    L = csa.load_library()
+
+    def call(dims, q_idx=FAKE):
+        return L.csa_attention_noalloc(ctypes.byref(dims), FAKE, q_idx, FAKE, FAKE, FAKE, None, FAKE, None, FAKE,
+                                       FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, None)
+
+    assert L.csa_attention_noalloc(None, *([FAKE] * 17), None) == _lib.CSA_ERR_NULL
+    assert call(_flash(batch=0)) == _lib.CSA_ERR_DIM
+    assert call(_flash(n_heads=96)) == _lib.CSA_ERR_UNSUPPORTED
+    prefill = _flash(batch=1, q_len=2048, max_entries=262144)
+    assert csa.workspace_size(prefill, _lib.CSA_OP_ATTENTION) > 64 << 20
+    assert call(prefill) == _lib.CSA_ERR_WORKSPACE
+    assert "static" in L.csa_last_error().decode()
+    # the decode shapes fit its work area
+    for d in (_flash(), _flash(batch=32, max_entries=32768), _flash(n_heads=128, topk=1024)):
+        assert csa.workspace_size(d, _lib.CSA_OP_ATTENTION) <= 64 << 20
+
+
 def test_workspace_sizes():
     # short rows are selected by one workgroup in LDS: no workspace
     assert csa.workspace_size(_flash(max_entries=4096), _lib.CSA_OP_TOPK) == 0
