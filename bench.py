@@ -31,8 +31,11 @@ METRIC = "CSA decode queries/s at 64K–1M ctx; achieved HBM GB/s vs peak (1 GPU
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # dense bf16 MFMA, MI355X datasheet
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_index_scores_decode_b4_1m.json")
-SCORER_SRC = [os.path.join(ROOT, "compressed_sparse_attention_indexer_amd", "csrc", f)
-              for f in ("scorer.hip", "scorer_common.hpp")]
+PROFILE_STEP = os.path.join(ROOT, "profiles", "trace_decode_b4_1m.json")
+_CSRC = os.path.join(ROOT, "compressed_sparse_attention_indexer_amd", "csrc")
+SCORER_SRC = [os.path.join(_CSRC, f) for f in ("scorer.hip", "scorer_common.hpp")]
+STEP_SRC = [os.path.join(_CSRC, f) for f in ("scorer.hip", "scorer_common.hpp", "topk.hip", "topk_hist.hpp",
+                                              "attention.hip", "common.hpp", "launch.hpp", "api.cpp")]
 
 
 def parse():
@@ -42,10 +45,12 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="decode_b4_1m")
     p.add_argument("--copies", type=int, default=2, help="device copies of the caches, rotated per step")
-    p.add_argument("--graph-steps", type=int, default=10, help="steps captured per graph")
+    p.add_argument("--graph-steps", type=int, default=2,
+                   help="steps captured per graph (at least the cache copies); each replay is one timing sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--quick", action="store_true", help="skip the other decode workloads")
-    p.add_argument("--prefill", action="store_true", help="also time the 2048-token prefill chunk")
+    p.add_argument("--no-prefill", action="store_true", help="skip the 2048-token prefill chunk")
+    p.add_argument("--prefill", action="store_true", help=argparse.SUPPRESS)  # timed by default
     p.add_argument("--profile-kernels", nargs="?", const="scorer", default=None,
                    choices=("scorer", "step", "hca", "fp8", "prefill"),
                    help="run only eager launches of one part (for rocprofv3 counter runs): the bf16 scorer, "
@@ -188,22 +193,30 @@ def rotation(bytes_per_copy, minimum):
 
 
 def time_graph(torch, g, graph_steps, steps, warmup):
+    """W untimed warmup steps, then about `steps` steps as replays of g (graph_steps
+    steps each) between two synchronizations.  Returns the mean over the timed
+    steps (first to last HIP event), the distribution of per-replay step times
+    (a HIP event after every replay), the wall time and the number of steps."""
     for _ in range(max(1, warmup // graph_steps)):
         g.replay()
     torch.cuda.synchronize()
     reps = max(1, steps // graph_steps)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     t0 = time.perf_counter()
-    a.record()
-    for _ in range(reps):
+    ev[0].record()
+    for i in range(reps):
         g.replay()
-    b.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return a.elapsed_time(b) / (reps * graph_steps), wall, reps * graph_steps
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) / graph_steps for i in range(reps))
+    pick = lambda f: per[min(len(per) - 1, int(round(f * (len(per) - 1))))]
+    n = reps * graph_steps
+    return {"ms": ev[0].elapsed_time(ev[-1]) / n, "median_ms": pick(0.5), "p10_ms": pick(0.1), "p90_ms": pick(0.9),
+            "samples": reps, "wall_s": wall, "steps": n}
 
 
-def bench_csa(torch, csa, case, args, detail):
+def bench_csa(torch, csa, case, args, detail, min_samples=None):
     from compressed_sparse_attention_indexer_amd.staging import DeviceCase
     dc = DeviceCase(case)
     copies = rotation(sum(x.numel() * x.element_size() for x in dc.k_idx), args.copies)
@@ -212,13 +225,19 @@ def bench_csa(torch, csa, case, args, detail):
     n_ent = case.n_entries
     gs = max(args.graph_steps, copies)  # every copy is used within one replay
     g_step = capture(torch, r.fused, gs)
-    ms, wall, n = time_graph(torch, g_step, gs, args.steps, args.warmup)
+    r.graph = g_step
+    # the headline workload times exactly args.steps steps; the others at least
+    # 50 replays, so that the distribution has 50 samples
+    steps = args.steps if min_samples is None else max(args.steps, min_samples * gs)
+    tg = time_graph(torch, g_step, gs, steps, args.warmup)
+    ms, wall, n = tg["ms"], tg["wall_s"], tg["steps"]
     # graph replay result == eager result (deterministic kernels)
     out_graph = r.out.clone()
     r.fused((n - 1) % copies)
     torch.cuda.synchronize()
     same = bool(torch.equal(out_graph, r.out))
     res = {"ms_per_step": ms, "queries_per_s": Q / (ms * 1e-3), "steps": n, "wall_s": wall, "cache_copies": copies,
+           "median_ms": tg["median_ms"], "p10_ms": tg["p10_ms"], "p90_ms": tg["p90_ms"], "samples": tg["samples"],
            "graph_matches_eager": same,
            "alg_bytes_per_step": csa_step_bytes(n_ent, Q),
            "step_GBps": csa_step_bytes(n_ent, Q) / (ms * 1e-3) / 1e9}
@@ -228,9 +247,9 @@ def bench_csa(torch, csa, case, args, detail):
         for name, fn in (("index_scores", r.scores_call), ("topk_select", r.topk_call),
                          ("sparse_mqa", r.attn_call)):
             g = capture(torch, fn, gs)
-            per[name], _, _ = time_graph(torch, g, gs, args.steps, args.warmup)
+            per[name] = time_graph(torch, g, gs, args.steps, args.warmup)["ms"]
         g_s = capture(torch, r.step, gs)
-        res["separate_entry_points_ms"], _, _ = time_graph(torch, g_s, gs, args.steps, args.warmup)
+        res["separate_entry_points_ms"] = time_graph(torch, g_s, gs, args.steps, args.warmup)["ms"]
         res["kernel_ms"] = per
         res["scorer_alg_bytes"] = scorer_bytes(n_ent, Q)
         # indexer flops: 2 * 64 heads * 128 dims per (query, visible entry)
@@ -263,10 +282,12 @@ def bench_hca(torch, csa, case, args):
                            dc.win_rows, dc.seq_len, dc.q_pos, dc.hca_sink, out=out, lse=lse, workspace=ws)
 
     g = capture(torch, call, gs)
-    ms, _, n = time_graph(torch, g, gs, args.steps, args.warmup)
+    tg = time_graph(torch, g, gs, max(args.steps, 50 * gs), args.warmup)
+    ms = tg["ms"]
     n_h = case.seq_len // case.wl.hca_ratio
     b = hca_bytes(n_h, Q)
-    return {"ms_per_call": ms, "queries_per_s": Q / (ms * 1e-3), "alg_bytes": b, "cache_copies": n_copies,
+    return {"ms_per_call": ms, "median_ms": tg["median_ms"], "p10_ms": tg["p10_ms"], "p90_ms": tg["p90_ms"],
+            "samples": tg["samples"], "queries_per_s": Q / (ms * 1e-3), "alg_bytes": b, "cache_copies": n_copies,
             "GBps": b / (ms * 1e-3) / 1e9, "frac_hbm_peak": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
@@ -302,7 +323,7 @@ def bench_fp8_scores(torch, csa, case, args):
         csa.csa_index_scores_fp8(dims, q8_t, qs_t, w_t, c[2], c[3], seq_t, pos_t, scores=scores)
 
     g = capture(torch, call, gs)
-    ms, _, _ = time_graph(torch, g, gs, args.steps, args.warmup)
+    ms = time_graph(torch, g, gs, args.steps, args.warmup)["ms"]
     Q = wl.batch * wl.q_len
     b = fp8_scorer_bytes(case.n_entries, Q)
     return {"ms_per_call": ms, "alg_bytes": b, "GBps": b / (ms * 1e-3) / 1e9, "cache_copies": n_copies,
@@ -342,7 +363,7 @@ def bench_compress(torch, csa, args):
         ws = torch.empty(max(256, csa.compress_workspace_size(dims)), dtype=torch.uint8, device=dev)
         g = capture(torch, lambda i: csa.csa_compress(dims, X, WK, WG, AP, GM, out=out, workspace=ws),
                     args.graph_steps)
-        ms, _, _ = time_graph(torch, g, args.graph_steps, max(args.steps, 20), args.warmup)
+        ms = time_graph(torch, g, args.graph_steps, max(args.steps, 20), args.warmup)["ms"]
         byt = 2 * D * COMPRESS_HIDDEN * 2 + T * COMPRESS_HIDDEN * 2 + ne * D * 2
         fl = 2.0 * T * COMPRESS_HIDDEN * 2 * D
         gbs, tfs = byt / (ms * 1e-3) / 1e9, fl / (ms * 1e-3) / 1e12
@@ -364,20 +385,163 @@ def traffic_from_profile():
     return int(rec["hbm_bytes_per_launch"]), rec.get("note", "")
 
 
-def cpu_baseline(case):
+def _oracle_step_rate(case, min_s, min_runs, max_runs):
+    """Queries/s of the oracle's whole step on a case: repeated until min_s of CPU
+    work and min_runs runs (at most max_runs), best run."""
     import oracle
-    wl = case.wl
-    # repeat the whole step until about 10 s of CPU work is done
-    runs, t_total = 0, 0.0
-    while runs < 3 or t_total < 10.0:
+    runs, t_total, best = 0, 0.0, float("inf")
+    while runs < max_runs and (runs < min_runs or t_total < min_s):
         t0 = time.perf_counter()
         oracle.csa_attention(case)
-        t_total += time.perf_counter() - t0
+        dt = time.perf_counter() - t0
+        t_total += dt
+        best = min(best, dt)
         runs += 1
+    Q = case.wl.batch * case.wl.q_len
+    return Q / best, runs, t_total
+
+
+def cpu_baseline(case):
+    """The headline workload's whole step on the oracle (host cores)."""
+    import oracle
+    wl = case.wl
+    rate, runs, t_total = _oracle_step_rate(case, 10.0, 3, 50)
     Q = wl.batch * wl.q_len
-    return {"value": Q * runs / t_total, "unit": "queries/s", "cores": oracle.num_threads(), "kind": "oracle",
+    return {"value": rate, "unit": "queries/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "cpu": _cpu_model(),
             "sample": f"whole CSA step of {wl.name} ({Q} queries x {case.max_entries} entries: scores, "
-                      f"top-k, attention), repeated {runs} times, {t_total:.1f} s in all"}
+                      f"top-k, attention), best of {runs} runs ({t_total:.1f} s in all)"}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baselines_other(inputs):
+    """The oracle on the other workloads: the 64K single query (best of 3), the
+    ragged 32-sequence batch (one run) and a sample of the prefill chunk (4
+    evenly spaced queries, extrapolated to its 2,048 queries and labelled so)."""
+    import numpy as np
+    import oracle
+    res = {}
+    c1 = inputs.make_case(inputs.WORKLOADS["decode_b1_64k"])
+    rate, runs, t = _oracle_step_rate(c1, 0.0, 3, 3)
+    res["decode_b1_64k"] = {"value": rate, "unit": "queries/s", "sample": f"whole step, best of {runs} ({t:.1f} s)"}
+    del c1
+    c2 = inputs.make_case(inputs.WORKLOADS["decode_b32_ragged_64k_128k"])
+    rate, runs, t = _oracle_step_rate(c2, 0.0, 1, 1)
+    res["decode_b32_ragged_64k_128k"] = {"value": rate, "unit": "queries/s",
+                                         "sample": f"whole step of 32 queries, one run ({t:.1f} s)"}
+    del c2
+    import dataclasses
+    c4 = inputs.make_case(inputs.WORKLOADS["prefill_t2048_1m"], with_hca=False)
+    ts = np.linspace(0, c4.wl.q_len - 1, 4).astype(int)
+    sub = dataclasses.replace(c4, wl=dataclasses.replace(c4.wl, q_len=len(ts)), q_pos=c4.q_pos[ts].copy(),
+                              q=c4.q[:, ts].copy(), q_idx=c4.q_idx[:, ts].copy(), w=c4.w[:, ts].copy())
+    t0 = time.perf_counter()
+    oracle.csa_attention(sub)
+    t = time.perf_counter() - t0
+    res["prefill_t2048_1m"] = {"value": len(ts) / t, "unit": "queries/s", "extrapolated": True,
+                               "sample": f"queries {ts.tolist()} of the 2,048 ({t:.1f} s); a whole chunk would take "
+                                         f"about {t * c4.wl.q_len / len(ts):.0f} s (extrapolated x{c4.wl.q_len // len(ts)})"}
+    res["cores"] = oracle.num_threads()
+    return res
+
+
+def stream_read_peak(torch):
+    """HBM read bandwidth of a plain streaming-read kernel over a 4 GiB buffer
+    (libcsa_bench.so): the best and the median of several launches at each of a
+    few grid sizes."""
+    import ctypes
+    from compressed_sparse_attention_indexer_amd import build as pkg_build
+    if not os.path.exists(pkg_build.BENCH_LIB):
+        return None
+    lib = ctypes.CDLL(pkg_build.BENCH_LIB)
+    lib.csa_bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                          ctypes.c_void_p]
+    lib.csa_bench_stream_read.restype = ctypes.c_int
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(8192, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    out = {}
+    for blocks in (1024, 2048, 4096, 8192):
+        times = []
+        for rep in range(6):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            rc = lib.csa_bench_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), blocks, st)
+            b.record()
+            if rc != 0:
+                return {"error": f"launch failed ({rc})"}
+            b.synchronize()
+            if rep > 0:
+                times.append(a.elapsed_time(b))
+        times.sort()
+        out[blocks] = (nbytes / (times[0] * 1e-3) / 1e9, nbytes / (times[len(times) // 2] * 1e-3) / 1e9)
+    del buf, sink
+    best = max(v[0] for v in out.values())
+    return {"best_GBps": best, "bytes": nbytes, "by_workgroups": {str(k): {"best_GBps": v[0], "median_GBps": v[1]}
+                                                                   for k, v in out.items()}}
+
+
+_CLOCK_CMDS = (["amd-smi", "metric", "--clock", "--json"], ["amd-smi", "metric", "-c", "--json"])
+
+
+def _clock_summary(text):
+    """GPU (per XCD) and memory clocks from amd-smi's JSON."""
+    data = json.loads(text)
+    gpus = data.get("gpu_data", data) if isinstance(data, dict) else data
+    clk = gpus[0]["clock"]
+    val = lambda e: e["clk"]["value"] if isinstance(e.get("clk"), dict) else None
+    gfx = [val(v) for k, v in sorted(clk.items()) if k.startswith("gfx_")]
+    one = next(v for k, v in clk.items() if k.startswith("gfx_"))
+    return {"gfx_MHz": gfx, "gfx_max_MHz": one["max_clk"]["value"] if isinstance(one.get("max_clk"), dict) else None,
+            "gfx_locked": one.get("clk_locked"), "mem_MHz": val(clk["mem_0"]) if "mem_0" in clk else None}
+
+
+def gpu_clocks(busy=None):
+    """One amd-smi sample of the GPU clocks.  With `busy` (a callable that
+    enqueues GPU work and waits for it), the sample is taken while that work
+    runs back to back, so it shows the clocks under load."""
+    import subprocess
+    for cmd in _CLOCK_CMDS:
+        try:
+            proc = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+        except OSError:
+            continue
+        t0 = time.perf_counter()
+        while busy is not None and proc.poll() is None and time.perf_counter() - t0 < 20:
+            busy()
+        try:
+            out, _ = proc.communicate(timeout=30)
+        except subprocess.TimeoutExpired:
+            proc.kill()
+            proc.communicate()
+            continue
+        if proc.returncode == 0 and out.strip():
+            try:
+                return {"cmd": " ".join(cmd), "under_load": busy is not None, **_clock_summary(out)}
+            except (ValueError, KeyError, IndexError, StopIteration, TypeError):
+                return {"cmd": " ".join(cmd), "under_load": busy is not None, "raw": out.strip()[:400]}
+    return None
+
+
+def step_profile():
+    """Kernel averages of the committed kernel-trace summary of the fused decode
+    step, if its sources are the ones the trace was taken on."""
+    if not os.path.exists(PROFILE_STEP):
+        return None
+    rec = json.load(open(PROFILE_STEP))
+    if rec.get("src_sha") != sha_of(STEP_SRC):
+        return {"note": "the path's sources changed since the trace was taken", "command": rec.get("command")}
+    return rec
 
 
 def profile_kernels(torch, csa, inputs, case, args):
@@ -445,7 +609,14 @@ def main():
         profile_kernels(torch, csa, inputs, case, args)
         return
 
+    clocks = [gpu_clocks()]
     main_res, runner = bench_csa(torch, csa, case, args, detail=True)
+
+    def busy():
+        for _ in range(20):
+            runner.graph.replay()
+        torch.cuda.synchronize()
+    clocks.append(gpu_clocks(busy))
     print(f"[bench] {wl.name}: {main_res['ms_per_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
     breakdown = {wl.name: main_res}
     if case.hca_q is not None:
@@ -459,37 +630,65 @@ def main():
     scorer_ms = main_res["kernel_ms"]["index_scores"]
     alg = main_res["scorer_alg_bytes"]
     traffic, traffic_note = traffic_from_profile()
-    roofline = {"kernel": "index_scores_bf16_kernel", "bound": "hbm",
-                "achieved": alg / (scorer_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": alg / (scorer_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": traffic,
-                "alg_bytes_per_launch": alg, "avg_launch_ms": scorer_ms, "traffic_note": traffic_note}
     del runner
     torch.cuda.empty_cache()
+    peak = stream_read_peak(torch)
+    print(f"[bench] streaming read: {peak and peak.get('best_GBps')}", file=sys.stderr, flush=True)
+    achieved = alg / (scorer_ms * 1e-3) / 1e9
+    step_gbs = main_res["step_GBps"]
+    roofline = {"kernel": "index_scores_bf16_kernel (the indexer scorer, launched alone)", "bound": "hbm",
+                "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                "traffic": traffic, "traffic_note": traffic_note,
+                "alg_bytes_per_launch": alg, "avg_launch_ms": scorer_ms,
+                "measured_stream_read_GBps": peak and peak.get("best_GBps"),
+                "frac_of_measured_stream_read": (achieved / peak["best_GBps"]) if peak and peak.get("best_GBps")
+                else None,
+                "step": {"what": "the whole fused decode step (csa_attention: scorer with the selection's "
+                                 "histograms and emitted entries, selection, attention, combine)",
+                         "alg_bytes": main_res["alg_bytes_per_step"], "ms": main_res["ms_per_step"],
+                         "GBps": step_gbs, "frac": step_gbs / HBM_PEAK_GBS,
+                         "frac_of_measured_stream_read": (step_gbs / peak["best_GBps"]) if peak and
+                         peak.get("best_GBps") else None}}
+    prof = step_profile()
+    if prof and "kernels" in prof:
+        k = prof["kernels"].get(prof.get("scorer_in_step", ""))
+        if k:
+            roofline["in_step_scorer"] = {"kernel": prof["scorer_in_step"], "avg_us_in_trace": k["avg_us"],
+                                          "frac": alg / (k["avg_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                          "source": os.path.relpath(PROFILE_STEP, ROOT)}
+    elif prof:
+        roofline["in_step_scorer"] = prof
 
     if not args.quick:
         for name in ("decode_b1_64k", "decode_b32_ragged_64k_128k", "pro_decode_b4_1m"):
             if name == wl.name:
                 continue
             c2 = inputs.make_case(inputs.WORKLOADS[name])
-            r2, rr = bench_csa(torch, csa, c2, args, detail=True)
+            r2, rr = bench_csa(torch, csa, c2, args, detail=True, min_samples=50)
             breakdown[name] = r2
             del rr, c2
             torch.cuda.empty_cache()
-    if args.prefill:
-        c4 = inputs.make_case(inputs.WORKLOADS["prefill_t2048_1m"])
+    if not args.no_prefill:
+        c4 = inputs.make_case(inputs.WORKLOADS["prefill_t2048_1m"], with_hca=False)
         a2 = argparse.Namespace(**vars(args))
-        a2.steps, a2.warmup, a2.graph_steps, a2.copies = 3, 1, 1, 1  # the rotation still covers 2x the LLC
-        r4, rr = bench_csa(torch, csa, c4, a2, detail=True)
+        a2.steps, a2.warmup, a2.graph_steps, a2.copies = 4, 1, 1, 1  # the rotation still covers 2x the LLC
+        r4, rr = bench_csa(torch, csa, c4, a2, detail=True, min_samples=20)
         breakdown["prefill_t2048_1m"] = r4
         del rr, c4
+        torch.cuda.empty_cache()
+    clocks.append(gpu_clocks())
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(case)
+        if not args.quick:
+            breakdown["cpu_baselines_other_workloads"] = cpu_baselines_other(inputs)
 
     line = {
         "metric": METRIC, "value": main_res["queries_per_s"], "unit": "queries/s", "n_gpus": 1,
         "steps": main_res["steps"], "warmup": args.warmup, "ms_per_step": main_res["ms_per_step"],
+        "median_ms_per_step": main_res["median_ms"], "p10_ms_per_step": main_res["p10_ms"],
+        "p90_ms_per_step": main_res["p90_ms"], "timing_samples": main_res["samples"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded; N(0,1)/sqrt(d) activations and caches, U(0,1) weights, N(0,1) sink)",
         "config": {"workload": wl.name, "batch": wl.batch, "q_len": wl.q_len, "context": wl.seq_len,
@@ -500,6 +699,8 @@ def main():
                    "cache_copies_rotated": main_res["cache_copies"]},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "stream_read_peak": peak,
+        "gpu_clocks": {"before": clocks[0], "under_load": clocks[1], "after": clocks[2]},
         "breakdown": breakdown,
     }
     print(json.dumps(line))

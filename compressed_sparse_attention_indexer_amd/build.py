@@ -11,6 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libcsa.so")
+BENCH_LIB = os.path.join(PKG, "libcsa_bench.so")  # measurement helper of bench.py only
 SOURCES = ["api.cpp", "scorer.hip", "scorer_fp8.hip", "topk.hip", "attention.hip", "compressor.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
@@ -62,6 +63,13 @@ def build_library(verbose: bool = False, extra_flags=()) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed ({res.returncode}):\n{_quiet(res.stdout)}")
     os.replace(tmp, LIB)
+    # the benchmark's measurement helper (streaming-read kernel), a library of its own
+    tmp = BENCH_LIB + ".tmp"
+    cmd = [cc, *_flags(extra_flags), "-shared", os.path.join(CSRC, "bench_probe.hip"), "-o", tmp]
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on bench_probe.hip ({res.returncode}):\n{_quiet(res.stdout)}")
+    os.replace(tmp, BENCH_LIB)
     return LIB
 
 

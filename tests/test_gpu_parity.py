@@ -111,6 +111,27 @@ def test_separate_value_rows(lens, T, q_pos0):
     check_whole_step(make_case_with_lens(dataclasses.replace(wl, separate_v=True), sl), ATT_TOL_BF16)
 
 
+@pytest.mark.parametrize("sharp", [False, True])
+def test_value_rows_near_the_fp16_bound(sharp):
+    """Split partials O/l are kept in fp16, which holds |O/l| <= max |v| while
+    max |v| < 65504.  Value rows scaled so that max |v| is about 60,000 (and,
+    with sharp logits, single rows dominating so that O/l reaches such values):
+    still within the bf16 attention tolerance of the oracle."""
+    import dataclasses
+    wl, sl = flash_case(f"flash_vbound_{int(sharp)}", [4 * 9000 + 1, 4 * 3000 + 2])
+    case = make_case_with_lens(dataclasses.replace(wl, separate_v=True), sl)
+    vmax = max(float(np.max(np.abs(inputs.bf16_to_f32(x)))) for x in case.v + case.win_v)
+    s = np.float32(60000.0 / vmax)
+    case.v = [inputs.bf16_bits(inputs.bf16_to_f32(x) * s) for x in case.v]
+    case.win_v = [inputs.bf16_bits(inputs.bf16_to_f32(x) * s) for x in case.win_v]
+    vmax = max(float(np.max(np.abs(inputs.bf16_to_f32(x)))) for x in case.v + case.win_v)
+    assert 55000 < vmax < 65504
+    if sharp:
+        case.q = inputs.bf16_bits(inputs.bf16_to_f32(case.q) * np.float32(60.0))
+    dc = check_whole_step(case, ATT_TOL_BF16)
+    del dc
+
+
 def test_flash_no_activation():
     wl, sl = flash_case("flash_noact", [4 * 2000, 4 * 900])
     check_whole_step(make_case_with_lens(wl, sl), ATT_TOL_BF16, act=csa.CSA_ACT_NONE)
