@@ -243,11 +243,15 @@ def bench_csa(torch, csa, case, args, detail, min_samples=None):
            "step_GBps": csa_step_bytes(n_ent, Q) / (ms * 1e-3) / 1e9}
     res["step_frac_hbm_peak"] = res["step_GBps"] / HBM_PEAK_GBS
     if detail:
+        # Each entry point alone, 20 launches per graph (copies rotated), so that
+        # the per-launch figure is the kernel time plus the gap between dependent
+        # kernels, and the replay's own launch cost is spread thin.
         per = {}
+        gk = max(gs, 20)
         for name, fn in (("index_scores", r.scores_call), ("topk_select", r.topk_call),
                          ("sparse_mqa", r.attn_call)):
-            g = capture(torch, fn, gs)
-            per[name] = time_graph(torch, g, gs, args.steps, args.warmup)["ms"]
+            g = capture(torch, fn, gk)
+            per[name] = time_graph(torch, g, gk, max(args.steps, 5 * gk), args.warmup)["ms"]
         g_s = capture(torch, r.step, gs)
         res["separate_entry_points_ms"] = time_graph(torch, g_s, gs, args.steps, args.warmup)["ms"]
         res["kernel_ms"] = per
@@ -313,7 +317,7 @@ def bench_fp8_scores(torch, csa, case, args):
         k_t = k_0 if c == 0 else [x.clone() for x in k_0]
         s_t = s_0 if c == 0 else [x.clone() for x in s_0]
         copies.append((k_t, s_t, csa.ptr_array(k_t, dev), csa.ptr_array(s_t, dev)))
-    gs = max(args.graph_steps, n_copies)
+    gs = max(args.graph_steps, n_copies, 20)  # 20 launches per graph, as for the other per-kernel figures
     seq_t, pos_t = torch.from_numpy(case.seq_len).to(dev), torch.from_numpy(case.q_pos).to(dev)
     dims = csa.make_dims(batch=wl.batch, q_len=wl.q_len, max_entries=case.max_entries)
     scores = torch.empty((wl.batch, wl.q_len, case.max_entries), dtype=torch.float32, device=dev)
@@ -323,7 +327,7 @@ def bench_fp8_scores(torch, csa, case, args):
         csa.csa_index_scores_fp8(dims, q8_t, qs_t, w_t, c[2], c[3], seq_t, pos_t, scores=scores)
 
     g = capture(torch, call, gs)
-    ms = time_graph(torch, g, gs, args.steps, args.warmup)["ms"]
+    ms = time_graph(torch, g, gs, max(args.steps, 5 * gs), args.warmup)["ms"]
     Q = wl.batch * wl.q_len
     b = fp8_scorer_bytes(case.n_entries, Q)
     return {"ms_per_call": ms, "alg_bytes": b, "GBps": b / (ms * 1e-3) / 1e9, "cache_copies": n_copies,
@@ -343,6 +347,59 @@ COMPRESS_CASES = (
     ("hca_prefill_chunk_2048", 2048, 512, 128, 128, 8176, 16, False),
 )
 COMPRESS_HIDDEN = 4096
+
+
+def fp8_step_bytes(n_ent, n_queries):
+    """The decode step with fp8 index tensors: the fp8 scorer's bytes plus, per query, q 64 KiB,
+    512 selected + 128 window rows of 1 KiB, sink 256 B and the fp32 output 128 KiB."""
+    return fp8_scorer_bytes(n_ent, n_queries) + (868864 - 16640) * n_queries
+
+
+def bench_fp8_step(torch, csa, case, args):
+    """The whole decode step with fp8 (E4M3) index tensors: csa_attention_fp8
+    (fp8 scorer with the selection's histograms and emitted entries, selection,
+    bf16 attention, combine), graph-replayed like the bf16 step, with the fp8
+    key caches, their scales and the KV cache rotated over copies."""
+    from compressed_sparse_attention_indexer_amd import inputs
+    from compressed_sparse_attention_indexer_amd.staging import DeviceCase
+    dev = "cuda"
+    dc = DeviceCase(case)
+    dims = dc.csa_dims()
+    q8, qs, k8, ks = inputs.make_fp8_index(case)
+    q8_t, qs_t = torch.from_numpy(q8).to(dev), torch.from_numpy(qs).to(dev)
+    k_0 = [torch.from_numpy(k).to(dev) for k in k8]
+    s_0 = [torch.from_numpy(x).to(dev) for x in ks]
+    n_copies = rotation(sum(k.nbytes for k in k8) + sum(x.nbytes for x in ks), args.copies)
+    copies = []
+    for c in range(n_copies):
+        k_t = k_0 if c == 0 else [x.clone() for x in k_0]
+        s_t = s_0 if c == 0 else [x.clone() for x in s_0]
+        v_t = dc.kv if c == 0 else [x.clone() for x in dc.kv]
+        copies.append((k_t, s_t, v_t, csa.ptr_array(k_t, dev), csa.ptr_array(s_t, dev),
+                       dc.kv_p if c == 0 else csa.ptr_array(v_t, dev)))
+    out = torch.empty((dims.batch, dims.q_len, dims.n_heads, dims.head_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((dims.batch, dims.q_len, dims.n_heads), dtype=torch.float32, device=dev)
+    ws = torch.zeros(max(256, csa.workspace_size(dims, csa._lib.CSA_OP_ATTENTION_FP8)), dtype=torch.uint8,
+                     device=dev)
+
+    def call(i):
+        c = copies[i % len(copies)]
+        csa.csa_attention_fp8(dims, dc.q, q8_t, qs_t, dc.w, c[3], c[4], c[5], None, dc.win_p, None, dc.win_pos0,
+                              dc.win_rows, dc.seq_len, dc.q_pos, dc.sink, out=out, lse=lse, workspace=ws)
+
+    gs = max(args.graph_steps, n_copies)
+    g = capture(torch, call, gs)
+    tg = time_graph(torch, g, gs, max(args.steps, 50 * gs), args.warmup)
+    ms = tg["ms"]
+    out_graph = out.clone()
+    call((tg["steps"] - 1) % n_copies)
+    torch.cuda.synchronize()
+    Q = dims.batch * dims.q_len
+    b = fp8_step_bytes(case.n_entries, Q)
+    return {"ms_per_step": ms, "queries_per_s": Q / (ms * 1e-3), "median_ms": tg["median_ms"], "p10_ms": tg["p10_ms"],
+            "p90_ms": tg["p90_ms"], "samples": tg["samples"], "steps": tg["steps"], "cache_copies": n_copies,
+            "graph_matches_eager": bool(torch.equal(out_graph, out)), "alg_bytes_per_step": b,
+            "step_GBps": b / (ms * 1e-3) / 1e9, "step_frac_hbm_peak": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
 def bench_compress(torch, csa, args):
@@ -511,6 +568,9 @@ def gpu_clocks(busy=None):
     enqueues GPU work and waits for it), the sample is taken while that work
     runs back to back, so it shows the clocks under load."""
     import subprocess
+    t0 = time.perf_counter()
+    while busy is not None and time.perf_counter() - t0 < 2.0:  # the clocks settle under the load first
+        busy()
     for cmd in _CLOCK_CMDS:
         try:
             proc = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
@@ -625,6 +685,7 @@ def main():
         f8 = bench_fp8_scores(torch, csa, case, args)
         f8["vs_bf16_scorer"] = main_res["kernel_ms"]["index_scores"] / f8["ms_per_call"]
         breakdown[wl.name + "_fp8_index_scores"] = f8
+        breakdown[wl.name + "_fp8_step"] = bench_fp8_step(torch, csa, case, args)
     breakdown["compressor"] = bench_compress(torch, csa, args)
     Q = wl.batch * wl.q_len
     scorer_ms = main_res["kernel_ms"]["index_scores"]

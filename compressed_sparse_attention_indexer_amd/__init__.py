@@ -13,14 +13,14 @@ import ctypes
 import math
 from typing import List, Optional, Sequence, Union
 
-from ._lib import (CSA_ACT_NONE, CSA_ACT_RELU, CSA_BF16, CSA_F32, CSA_OP_ATTENTION, CSA_OP_HCA_MQA,
+from ._lib import (CSA_ACT_NONE, CSA_ACT_RELU, CSA_BF16, CSA_F32, CSA_OP_ATTENTION, CSA_OP_ATTENTION_FP8, CSA_OP_HCA_MQA,
                    CSA_OP_INDEX_SCORES, CSA_OP_SPARSE_MQA, CSA_OP_TOPK, EXPORTS, CsaCompressDims, CsaDims,
                    CsaError, check, load_library)
 
 __all__ = ["CsaDims", "CsaError", "make_dims", "workspace_size", "ptr_array", "csa_index_scores",
            "csa_index_scores_fp8", "CsaCompressDims", "make_compress_dims", "compress_workspace_size",
            "csa_compress", "csa_topk_select", "csa_sparse_mqa_decode", "hca_mqa_decode", "csa_attention",
-           "csa_attention_noalloc",
+           "csa_attention_fp8", "csa_attention_noalloc",
            "attention", "index_scores", "index_scores_fp8", "topk", "sparse_mqa", "hca_mqa", "load_library",
            "CSA_F32", "CSA_BF16", "CSA_ACT_RELU", "CSA_ACT_NONE"]
 
@@ -198,6 +198,24 @@ def csa_attention(dims: CsaDims, q, q_idx, w, k_idx: PtrArg, kv: PtrArg, v: PtrA
             ctypes.byref(dims), _p(q), _p(q_idx), _p(w), kip, kp, vp, wp, wvp, _p(win_pos0), _p(win_rows),
             _p(seq_len), _p(q_pos), _p(sink), _p(out), _p(lse), _p(topk_idx_out), _p(scores_out), _p(ws), nws,
             st), "csa_attention")
+    return out, lse
+
+
+def csa_attention_fp8(dims: CsaDims, q, q8, q_scale, w, k8: PtrArg, k_scale: PtrArg, kv: PtrArg, v: PtrArg,
+                      win: PtrArg, win_v: PtrArg, win_pos0, win_rows, seq_len, q_pos, sink, out=None, lse=None,
+                      want_lse=True, topk_idx_out=None, scores_out=None, workspace=None, stream=None):
+    """Whole CSA step with fp8 (E4M3) index tensors and per-row scales; bf16
+    attention side; returns (out, lse)."""
+    dev = q.device
+    with _on_stream(stream) as st:
+        out, lse = _attn_outputs(dims, dev, out, lse, want_lse)
+        (k8p, k0), (ksp, k5), (kp, k1), (vp, k2), (wp, k3), (wvp, k4) = (
+            _pa(x, dev) for x in (k8, k_scale, kv, v, win, win_v))
+        ws, nws = _ws(dims, CSA_OP_ATTENTION_FP8, workspace, dev)
+        check(load_library().csa_attention_fp8(
+            ctypes.byref(dims), _p(q), _p(q8), _p(q_scale), _p(w), k8p, ksp, kp, vp, wp, wvp, _p(win_pos0),
+            _p(win_rows), _p(seq_len), _p(q_pos), _p(sink), _p(out), _p(lse), _p(topk_idx_out), _p(scores_out),
+            _p(ws), nws, st), "csa_attention_fp8")
     return out, lse
 
 

@@ -13,11 +13,11 @@ LIB_PATH = os.path.join(PKG, "libcsa.so")
 CSA_OK, CSA_ERR_NULL, CSA_ERR_DIM, CSA_ERR_ALIGN, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE, CSA_ERR_HIP = range(7)
 CSA_F32, CSA_BF16 = 0, 1
 CSA_ACT_RELU, CSA_ACT_NONE = 0, 1
-CSA_OP_INDEX_SCORES, CSA_OP_TOPK, CSA_OP_SPARSE_MQA, CSA_OP_HCA_MQA, CSA_OP_ATTENTION = range(5)
+CSA_OP_INDEX_SCORES, CSA_OP_TOPK, CSA_OP_SPARSE_MQA, CSA_OP_HCA_MQA, CSA_OP_ATTENTION, CSA_OP_ATTENTION_FP8 = range(6)
 
 # every symbol include/csa.h declares
 EXPORTS = ("csa_workspace_size", "csa_index_scores", "csa_index_scores_fp8", "csa_topk_select",
-           "csa_sparse_mqa_decode", "hca_mqa_decode", "csa_attention", "csa_attention_noalloc",
+           "csa_sparse_mqa_decode", "hca_mqa_decode", "csa_attention", "csa_attention_fp8", "csa_attention_noalloc",
            "csa_compress_workspace_size", "csa_compress", "csa_status_string", "csa_last_error", "csa_abi_version")
 
 
@@ -66,13 +66,14 @@ def load_library(path: str = LIB_PATH):
     L.csa_sparse_mqa_decode.argtypes = [DP] + [P] * 13 + [P, SZ, P]
     L.hca_mqa_decode.argtypes = [DP] + [P] * 12 + [P, SZ, P]
     L.csa_attention.argtypes = [DP] + [P] * 17 + [P, SZ, P]
+    L.csa_attention_fp8.argtypes = [DP] + [P] * 19 + [P, SZ, P]
     L.csa_attention_noalloc.argtypes = [DP] + [P] * 17 + [P]
     CP = ctypes.POINTER(CsaCompressDims)
     L.csa_compress_workspace_size.argtypes = [CP, ctypes.POINTER(SZ)]
     L.csa_compress.argtypes = [CP] + [P] * 7 + [SZ, P]
     for f in ("csa_workspace_size", "csa_index_scores", "csa_index_scores_fp8", "csa_topk_select",
-              "csa_sparse_mqa_decode", "hca_mqa_decode", "csa_attention", "csa_attention_noalloc",
-              "csa_compress_workspace_size", "csa_compress"):
+              "csa_sparse_mqa_decode", "hca_mqa_decode", "csa_attention", "csa_attention_fp8",
+              "csa_attention_noalloc", "csa_compress_workspace_size", "csa_compress"):
         getattr(L, f).restype = I32
     _lib = L
     return L

@@ -75,6 +75,16 @@ csa_status check_scores(const csa_dims *d) {
     return CSA_OK;
 }
 
+// fp8 index tensors: the decode scorer's shape (64 heads x 128 dims)
+csa_status check_scores_fp8(const csa_dims *d) {
+    if (d->index_act != CSA_ACT_RELU && d->index_act != CSA_ACT_NONE)
+        return fail(CSA_ERR_UNSUPPORTED, "unknown index_act %d", d->index_act);
+    if (d->index_heads != 64 || d->index_dim != 128)
+        return fail(CSA_ERR_UNSUPPORTED, "fp8 scorer needs index_heads 64 and index_dim 128 (got %d, %d)",
+                    d->index_heads, d->index_dim);
+    return CSA_OK;
+}
+
 csa_status check_topk(const csa_dims *d) {
     if (d->topk < 1 || d->topk > csa::kTopkMaxK) return fail(CSA_ERR_DIM, "topk must be in [1, %d]", csa::kTopkMaxK);
     return CSA_OK;
@@ -101,23 +111,28 @@ float scale_of(const csa_dims *d) {
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Histogram windows come from the bf16 scorer in the fused call (one per scorer
-// workgroup, or per entry chunk of the tiled scorer) and from the top-k's own
-// histogram kernel otherwise (0 here).
-int win_count(const csa_dims *d, bool fused) {
+// Histogram windows come from the bf16 or fp8 scorer in the fused call (one per
+// decode-scorer workgroup, or per entry chunk of the tiled bf16 scorer) and
+// from the top-k's own histogram kernel otherwise (0 here).  The fp8 index
+// path always takes the decode scorer.
+int win_count(const csa_dims *d, bool fused, bool fp8 = false) {
     if (!fused || d->dtype != CSA_BF16) return 0;
+    if (fp8) return csa::score_workgroups_fp8(d->max_entries, n_queries(d));
     if (csa::score_uses_tiles(csa::kBF16, d->q_len)) return csa::tiled_windows(d->batch, d->q_len, d->max_entries);
     return csa::score_workgroups(d->max_entries, n_queries(d));
 }
 // Entries per decode-scorer workgroup handed to the selection in the fused
 // call (0: the selection scans the scores itself).
-int emit_cap(const csa_dims *d, bool fused) {
-    if (!fused || d->dtype != CSA_BF16 || csa::score_uses_tiles(csa::kBF16, d->q_len)) return 0;
+int emit_cap(const csa_dims *d, bool fused, bool fp8 = false) {
+    if (!fused || d->dtype != CSA_BF16) return 0;
     if (!csa::topk_uses_histogram(d->max_entries)) return 0;
+    if (fp8) return csa::score_emit_cap_fp8(d->max_entries, n_queries(d), d->topk);
+    if (csa::score_uses_tiles(csa::kBF16, d->q_len)) return 0;
     return csa::score_emit_cap(d->max_entries, n_queries(d), d->topk);
 }
-size_t ws_topk(const csa_dims *d, bool fused = false) {
-    return csa::topk_workspace_bytes(n_queries(d), d->topk, d->max_entries, win_count(d, fused), emit_cap(d, fused));
+size_t ws_topk(const csa_dims *d, bool fused = false, bool fp8 = false) {
+    return csa::topk_workspace_bytes(n_queries(d), d->topk, d->max_entries, win_count(d, fused, fp8),
+                                     emit_cap(d, fused, fp8));
 }
 size_t ws_sparse(const csa_dims *d) {
     return csa::mqa_workspace_bytes(d->dtype, n_queries(d), d->n_heads, d->head_dim, d->topk + d->window);
@@ -125,13 +140,13 @@ size_t ws_sparse(const csa_dims *d) {
 size_t ws_hca(const csa_dims *d) {
     return csa::mqa_workspace_bytes(d->dtype, n_queries(d), d->n_heads, d->head_dim, d->max_entries + d->window);
 }
-size_t ws_attention_parts(const csa_dims *d, size_t *off_idx, size_t *off_topk, size_t *off_mqa) {
+size_t ws_attention_parts(const csa_dims *d, size_t *off_idx, size_t *off_topk, size_t *off_mqa, bool fp8 = false) {
     const size_t Q = (size_t)n_queries(d);
     const size_t scores = align_up(Q * (size_t)d->max_entries * 4);
     const size_t idx = align_up(Q * (size_t)d->topk * 4);
     *off_idx = scores;
     *off_topk = scores + idx;
-    *off_mqa = *off_topk + align_up(ws_topk(d, true));
+    *off_mqa = *off_topk + align_up(ws_topk(d, true, fp8));
     return *off_mqa + align_up(ws_sparse(d)) + 256;
 }
 
@@ -167,7 +182,7 @@ csa::ScoreArgs score_args(const csa_dims *d, const void *q_idx, const float *w, 
 }
 
 csa::TopkArgs topk_args(const csa_dims *d, const float *scores, const int32_t *seq_len, const int32_t *q_pos,
-                        int32_t *idx, void *ws, bool fused = false) {
+                        int32_t *idx, void *ws, bool fused = false, bool fp8 = false) {
     csa::TopkArgs a{};
     a.scores = scores;
     a.seq_len = seq_len;
@@ -178,7 +193,7 @@ csa::TopkArgs topk_args(const csa_dims *d, const float *scores, const int32_t *s
     a.ratio = d->ratio;
     a.K = d->topk;
     a.n_max = d->max_entries;
-    csa::topk_carve(a, ws, n_queries(d), win_count(d, fused), emit_cap(d, fused));
+    csa::topk_carve(a, ws, n_queries(d), win_count(d, fused, fp8), emit_cap(d, fused, fp8));
     return a;
 }
 
@@ -309,6 +324,13 @@ csa_status csa_workspace_size(const csa_dims *d, int32_t op, size_t *bytes) {
             *bytes = ws_attention_parts(d, &a, &b, &c);
             break;
         }
+        case CSA_OP_ATTENTION_FP8: {
+            if ((s = check_scores_fp8(d)) || (s = check_topk(d)) || (s = check_attn(d))) return s;
+            if (d->dtype != CSA_BF16) return fail(CSA_ERR_UNSUPPORTED, "fp8 index path: attention dtype must be bf16");
+            size_t a, b, c;
+            *bytes = ws_attention_parts(d, &a, &b, &c, true);
+            break;
+        }
         default: return fail(CSA_ERR_UNSUPPORTED, "unknown op %d", op);
     }
     return ok();
@@ -331,11 +353,7 @@ csa_status csa_index_scores_fp8(const csa_dims *d, const uint8_t *q8, const floa
                                 const int32_t *q_pos, float *scores, void *stream) {
     csa_status s;
     if ((s = check_common(d))) return s;
-    if (d->index_act != CSA_ACT_RELU && d->index_act != CSA_ACT_NONE)
-        return fail(CSA_ERR_UNSUPPORTED, "unknown index_act %d", d->index_act);
-    if (d->index_heads != 64 || d->index_dim != 128)
-        return fail(CSA_ERR_UNSUPPORTED, "fp8 scorer needs index_heads 64 and index_dim 128 (got %d, %d)",
-                    d->index_heads, d->index_dim);
+    if ((s = check_scores_fp8(d))) return s;
     if ((s = check_score_ptrs(q8, w, k8, seq_len, q_pos, scores))) return s;
     REQUIRE_PTR(q_scale);
     REQUIRE_PTR(k_scale);
@@ -481,6 +499,21 @@ csa_status csa_attention(const csa_dims *d, const void *q, const void *q_idx, co
                                    sink, out, lse, topk_idx_out, scores_out, ws, ws_bytes, stream);
 }
 
+csa_status csa_attention_fp8(const csa_dims *d, const void *q, const uint8_t *q8, const float *q_scale,
+                             const float *w, const void *const *k8, const void *const *k_scale,
+                             const void *const *kv, const void *const *v, const void *const *win,
+                             const void *const *win_v, const int32_t *win_pos0, const int32_t *win_rows,
+                             const int32_t *seq_len, const int32_t *q_pos, const float *sink, float *out, float *lse,
+                             int32_t *topk_idx_out, float *scores_out, void *ws, size_t ws_bytes, void *stream) {
+    REQUIRE_PTR(q_scale);
+    REQUIRE_PTR(k_scale);
+    REQUIRE_ALIGN(q_scale, 4);
+    REQUIRE_ALIGN(k_scale, 8);
+    const csa_api::IndexFp8 f8{q_scale, k_scale};
+    return csa_api::attention_impl(d, q, q8, w, k8, kv, v, win, win_v, win_pos0, win_rows, seq_len, q_pos, sink,
+                                   out, lse, topk_idx_out, scores_out, ws, ws_bytes, stream, &f8);
+}
+
 }  // extern "C"
 
 csa_status csa_api::attention_impl(const csa_dims *d, const void *q, const void *q_idx, const float *w,
@@ -488,9 +521,13 @@ csa_status csa_api::attention_impl(const csa_dims *d, const void *q, const void 
                                    const void *const *win, const void *const *win_v, const int32_t *win_pos0,
                                    const int32_t *win_rows, const int32_t *seq_len, const int32_t *q_pos,
                                    const float *sink, float *out, float *lse, int32_t *topk_idx_out,
-                                   float *scores_out, void *ws, size_t ws_bytes, void *stream) {
+                                   float *scores_out, void *ws, size_t ws_bytes, void *stream, const IndexFp8 *f8) {
     csa_status s;
-    if ((s = check_common(d)) || (s = check_scores(d)) || (s = check_topk(d)) || (s = check_attn(d))) return s;
+    const bool fp8 = f8 != nullptr;
+    if ((s = check_common(d)) || (s = fp8 ? check_scores_fp8(d) : check_scores(d)) || (s = check_topk(d)) ||
+        (s = check_attn(d)))
+        return s;
+    if (fp8 && d->dtype != CSA_BF16) return fail(CSA_ERR_UNSUPPORTED, "fp8 index path: attention dtype must be bf16");
     if ((s = check_attn_ptrs(q, kv, v, win, win_v, win_pos0, win_rows, seq_len, q_pos, sink, out, lse))) return s;
     REQUIRE_PTR(q_idx);
     REQUIRE_PTR(w);
@@ -501,17 +538,21 @@ csa_status csa_api::attention_impl(const csa_dims *d, const void *q, const void 
     REQUIRE_ALIGN(topk_idx_out, 16);
     REQUIRE_ALIGN(scores_out, 16);
     size_t off_idx, off_topk, off_mqa;
-    const size_t need = ws_attention_parts(d, &off_idx, &off_topk, &off_mqa);
+    const size_t need = ws_attention_parts(d, &off_idx, &off_topk, &off_mqa, fp8);
     if ((s = check_ws(ws, ws_bytes, need))) return s;
     REQUIRE_ALIGN(ws, 16);
     char *base = (char *)ws;
     float *scores = scores_out ? scores_out : (float *)base;
     int32_t *idx = topk_idx_out ? topk_idx_out : (int32_t *)(base + off_idx);
     hipStream_t st = (hipStream_t)stream;
-    const csa::TopkArgs ta = topk_args(d, scores, seq_len, q_pos, idx, base + off_topk, true);
+    const csa::TopkArgs ta = topk_args(d, scores, seq_len, q_pos, idx, base + off_topk, true, fp8);
     csa::ScoreArgs sa = score_args(d, q_idx, w, k_idx, seq_len, q_pos, scores);
-    // the bf16 scorer also writes the top-k key-histogram windows while it writes the scores
-    const bool fused_hist = csa::topk_uses_histogram(d->max_entries) && win_count(d, true) > 0;
+    if (fp8) {
+        sa.q_scale = f8->q_scale;
+        sa.k_scale = f8->k_scale;
+    }
+    // the scorer also writes the top-k key-histogram windows while it writes the scores
+    const bool fused_hist = csa::topk_uses_histogram(d->max_entries) && win_count(d, true, fp8) > 0;
     if (fused_hist) {
         sa.win_hdr = ta.win_hdr;
         sa.win_cnt = ta.win_cnt;
@@ -521,7 +562,7 @@ csa_status csa_api::attention_impl(const csa_dims *d, const void *q, const void 
         sa.em_key = ta.em_key;
         sa.em_idx = ta.em_idx;
     }
-    hipError_t e = csa::launch_index_scores(sa, d->dtype, st);
+    hipError_t e = fp8 ? csa::launch_index_scores_fp8(sa, st) : csa::launch_index_scores(sa, d->dtype, st);
     if (e != hipSuccess) return hip_status(e, "csa_attention/scores");
     e = csa::launch_topk(ta, st, fused_hist);
     if (e != hipSuccess) return hip_status(e, "csa_attention/topk");

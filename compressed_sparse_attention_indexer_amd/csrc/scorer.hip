@@ -75,8 +75,6 @@ constexpr int kScoreDepth = 2;                        // key steps in flight per
 typedef bf16x8_t KeyFrag[2][4];
 typedef u32x4_t KeyRaw[8];  // a wave-step of keys as loaded: 8 KiB, 16 B per lane per load
 constexpr int kRawRowWords = kDI / 2 + 4;  // LDS row of 128 bf16 + 16 B pad
-constexpr int kEmitMax = 8192;             // entries of a stretch whose keys stay in LDS for the emission
-constexpr int kEmitCapMax = 512;           // emitted entries per workgroup at most
 }  // namespace
 
 template <int kAct, bool kHist, int kDepth>
@@ -547,26 +545,8 @@ int tiled_windows(int B, int T, int n_max) {
     return tiled_plan(a).n_chunks;
 }
 
-int score_emit_cap(int n_max, int n_queries, int K) {
-    // every workgroup's stretch must fit in LDS: at most ceil(steps / workgroups) steps
-    const int wgs = score_workgroups(n_max, n_queries);
-    const int steps = (n_max + kWgStep - 1) / kWgStep;
-    const int chunk = (steps + wgs - 1) / wgs;
-    if ((long)chunk * kWgStep > kEmitMax) return 0;
-    // about twice a workgroup's expected share of the K selected entries, plus a margin
-    int cap = (2 * K / wgs + 48 + 15) / 16 * 16;
-    cap = cap < 32 ? 32 : (cap > kEmitCapMax ? kEmitCapMax : cap);
-    while (cap > 32 && (long)cap * wgs > kTopkMaxSlots) cap -= 16;
-    // the selection's radix pass over the emitted slots needs more slots than K
-    return (long)cap * wgs <= kTopkMaxSlots && (long)cap * wgs > K ? cap : 0;
-}
+int score_emit_cap(int n_max, int n_queries, int K) { return decode_emit_cap(n_max, n_queries, K, kWgStep); }
 
-int score_workgroups(int n_max, int n_queries) {
-    // about one workgroup per CU over the launch, at most one per workgroup step
-    int per_query = (kTargetWgs + n_queries - 1) / n_queries;
-    const int steps = (n_max + kWgStep - 1) / kWgStep;
-    if (per_query > steps) per_query = steps;
-    return per_query < 1 ? 1 : per_query;
-}
+int score_workgroups(int n_max, int n_queries) { return decode_score_workgroups(n_max, n_queries, kWgStep); }
 
 }  // namespace csa

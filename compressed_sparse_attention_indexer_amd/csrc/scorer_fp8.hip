@@ -3,22 +3,24 @@
 // Analysis", INNOVATIONS 1, indexer bullet: quantization-aware training).
 #include "common.hpp"
 #include "launch.hpp"
+#include "topk_hist.hpp"
 #include "scorer_common.hpp"
 
 namespace csa {
 
 // ---------------------------------------------------------------------------
 // fp8 (OCP E4M3) decode scorer with per-row scales, HI = 64, DI = 128: the
-// same organisation as the bf16 decode scorer on v_mfma_f32_16x16x32_fp8_fp8
+// organisation of the bf16 decode scorer on v_mfma_f32_16x16x32_fp8_fp8
 // (A: 8 codes of head e's row per lane, B: 8 codes of entry e per lane).
 // Keys are 128 bytes per entry, half the bf16 stream.  Scales are positive,
 // so ReLU commutes with them: s_j = k_scale_j * sum_h (w_h q_scale_h)
 // act(q8_h . k8_j); the head weights absorb the query scales once, and each
 // stored score takes its entry's scale.  A wave-step is 64 entries (8 KiB,
 // 1 KiB contiguous per load instruction), redistributed through a
-// wave-private LDS block as in the bf16 kernel.  Unlike the bf16 kernel, the
-// workgroup steps of a query are dealt round-robin to its workgroups: the
-// contiguous stretches with a start barrier measured slower for these rows.
+// wave-private LDS block; every lane stores one score per step.  As in the
+// bf16 kernel, each workgroup streams one contiguous stretch of its query's
+// entries, its waves lined up by a barrier after their first loads, and it
+// can build the selection's histogram window and emitted entries as it goes.
 namespace {
 constexpr int kF8WaveStep = 64;                        // entries per wave and step
 constexpr int kF8WgStep = kScoreWaves * kF8WaveStep;   // entries per workgroup step
@@ -30,9 +32,14 @@ struct F8Raw {
 };
 }  // namespace
 
-template <int kAct, int kDepth>
+template <int kAct, bool kHist, int kDepth>
 __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_fp8_kernel(ScoreArgs a) {
+    __shared__ uint32_t lh[kHist ? kTopkBins : 1];
+    __shared__ uint32_t lkeys[kHist ? kEmitMax : 1];  // keys of this workgroup's stretch (emission)
     __shared__ __attribute__((aligned(16))) uint32_t kraw[kScoreWaves][kF8WaveStep * kF8RowWords];
+    __shared__ int s_red[4];
+    __shared__ int s_scan[4];  // the emission's scans (s_red may still be read after the window store)
+    __shared__ int s_cut;
     const int qi = blockIdx.y;
     const int b = qi / a.T;
     const int lane = threadIdx.x & 63;
@@ -41,6 +48,7 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_fp8_kernel(S
 
     int nvis = visible_entries(a.seq_len[b], a.q_pos[qi], a.ratio);
     nvis = nvis < a.n_max ? nvis : a.n_max;
+    const bool with_hist = kHist && nvis > a.K;  // same for the whole workgroup
     float *srow = a.scores + (size_t)qi * a.n_max;
 
     // A fragments: head 16*ht + e, codes 32s + 8g .. +8 for k-step s.
@@ -63,10 +71,17 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_fp8_kernel(S
     const uint8_t *kb = (const uint8_t *)a.k_idx[b];
     const float *ksb = (const float *)a.k_scale[b];
     const int last = nvis > 0 ? nvis - 1 : 0;
-    const int stride = gridDim.x * kF8WgStep;
-    const int base0 = blockIdx.x * kF8WgStep + wave * kF8WaveStep;
-    const int n_steps = base0 < a.n_max ? (a.n_max - base0 + stride - 1) / stride : 0;
-    const int n_load = base0 < nvis ? (nvis - base0 + stride - 1) / stride : 0;
+    // Work split as in the bf16 kernel: the query's visible entries, in
+    // workgroup steps of kF8WgStep, are cut into gridDim.x contiguous stretches;
+    // wave w takes entries kF8WaveStep * w .. + kF8WaveStep - 1 of each step.
+    const int vis_steps = (nvis + kF8WgStep - 1) / kF8WgStep;
+    const int chunk = (vis_steps + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int s0 = blockIdx.x * chunk;
+    const int n_load = vis_steps - s0 < chunk ? (vis_steps - s0 > 0 ? vis_steps - s0 : 0) : chunk;
+    const int stride = kF8WgStep;
+    const int base0 = s0 * kF8WgStep + wave * kF8WaveStep;
+    const bool emit = kHist && with_hist && a.em_cap > 0;  // the host enables it only when stretches fit lkeys
+    const int stretch0 = s0 * kF8WgStep;
 
     auto load = [&](F8Raw &kr, int base) {  // unconditional, indices clamped into the visible rows
 #pragma unroll
@@ -80,6 +95,7 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_fp8_kernel(S
         kr.ks = ksb[js];
     };
     uint32_t *kw = kraw[wave];
+    int hmax = -1;  // highest histogram bin this thread added
     auto process = [&](F8Raw &kr, int base, bool live, int next) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) *(u32x4_t *)&kw[(8 * i + (lane >> 3)) * kF8RowWords + 4 * (lane & 7)] = kr.k[i];
@@ -110,38 +126,75 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_fp8_kernel(S
             p = sum_xor32(p);
             if (g == et) mine = p;  // lane group g keeps column tile g
         }
-        if (live && j < a.n_max) srow[j] = j < nvis ? ks * mine : -INFINITY;
+        const float sv = j < nvis ? ks * mine : -INFINITY;
+        if (live && j < a.n_max) srow[j] = sv;
+        if (with_hist) {
+            const uint32_t key = order_key(sv);
+            const uint32_t bin = key >> 20;
+            const bool add = live && j < nvis;
+            lds_hist_add(lh, bin, add);
+            if (add) hmax = max(hmax, (int)bin);
+            if (emit && add) lkeys[j - stretch0] = key;
+        }
     };
 
+    // kDepth steps in flight, unrolled so no load sits behind a branch; steps
+    // past the last one reload the last step and store nothing.  The histogram
+    // is cleared while the first loads are out, then the waves meet.
+    F8Raw kbuf[kDepth];
+    auto step = [&](int k) { return base0 + (k < n_load ? k : n_load - 1) * stride; };
     if (n_load > 0) {
-        // kDepth steps in flight, unrolled so no load sits behind a branch; steps past the
-        // last one reload the last step and store nothing
-        F8Raw kbuf[kDepth];
-        auto step = [&](int k) { return base0 + (k < n_load ? k : n_load - 1) * stride; };
 #pragma unroll
         for (int i = 0; i < kDepth; ++i) load(kbuf[i], step(i));
+    }
+    if (with_hist) {
+        for (int i = threadIdx.x; i < kTopkBins; i += 64 * kScoreWaves) lh[i] = 0u;
+    }
+    __syncthreads();
+    if (n_load > 0) {
         for (int k = 0; k < n_load; k += kDepth) {
 #pragma unroll
             for (int i = 0; i < kDepth; ++i) process(kbuf[i], step(k + i), k + i < n_load, step(k + i + kDepth));
         }
     }
-    for (int k = n_load; k < n_steps; ++k) {  // steps past the visible entries: -inf
-        const int j = base0 + k * stride + 16 * g + e;
+    const int all_steps = (a.n_max + kF8WgStep - 1) / kF8WgStep;
+    for (int st = vis_steps + blockIdx.x; st < all_steps; st += gridDim.x) {  // steps past the visible entries
+        const int j = st * kF8WgStep + wave * kF8WaveStep + 16 * g + e;
         if (j < a.n_max) srow[j] = -INFINITY;
+    }
+    if (with_hist) {
+        const size_t w = (size_t)qi * gridDim.x + blockIdx.x;
+        hist_window_store_top(lh, hmax, a.win_hdr + w, a.win_cnt + w * kTopkWin, s_red);
+        if (emit) {  // hist_window_store_top's barrier also orders the key stores
+            int n_st = min(nvis, (s0 + n_load) * kF8WgStep) - stretch0;
+            n_st = n_st > 0 ? n_st : 0;
+            emit_region<64 * kScoreWaves>(lh, lkeys, n_st, stretch0, a.em_cap, a.em_hdr + 2 * w,
+                                          a.em_key + w * a.em_cap, a.em_idx + w * a.em_cap, s_scan, &s_cut);
+        }
     }
 }
 
+int score_workgroups_fp8(int n_max, int n_queries) {
+    return decode_score_workgroups(n_max, n_queries, kF8WgStep);
+}
+
+int score_emit_cap_fp8(int n_max, int n_queries, int K) { return decode_emit_cap(n_max, n_queries, K, kF8WgStep); }
+
 hipError_t launch_index_scores_fp8(const ScoreArgs &a, hipStream_t stream) {
     const int Q = a.B * a.T;
-    int per_query = (kTargetWgs + Q - 1) / Q;
-    const int steps = (a.n_max + kF8WgStep - 1) / kF8WgStep;
-    if (per_query > steps) per_query = steps;
-    if (per_query < 1) per_query = 1;
-    const dim3 grid(per_query, Q), block(64 * kScoreWaves);
-    if (a.act == 0)
-        hipLaunchKernelGGL((index_scores_fp8_kernel<0, kF8Depth>), grid, block, 0, stream, a);
-    else
-        hipLaunchKernelGGL((index_scores_fp8_kernel<1, kF8Depth>), grid, block, 0, stream, a);
+    const dim3 grid(score_workgroups_fp8(a.n_max, Q), Q), block(64 * kScoreWaves);
+    const bool hist = a.win_hdr != nullptr;  // the caller sized the windows with score_workgroups_fp8
+    if (a.act == 0) {
+        if (hist)
+            hipLaunchKernelGGL((index_scores_fp8_kernel<0, true, kF8Depth>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((index_scores_fp8_kernel<0, false, kF8Depth>), grid, block, 0, stream, a);
+    } else {
+        if (hist)
+            hipLaunchKernelGGL((index_scores_fp8_kernel<1, true, kF8Depth>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((index_scores_fp8_kernel<1, false, kF8Depth>), grid, block, 0, stream, a);
+    }
     return hipGetLastError();
 }
 

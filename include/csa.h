@@ -87,7 +87,8 @@ typedef enum csa_op {
     CSA_OP_TOPK = 1,
     CSA_OP_SPARSE_MQA = 2,
     CSA_OP_HCA_MQA = 3,
-    CSA_OP_ATTENTION = 4
+    CSA_OP_ATTENTION = 4,
+    CSA_OP_ATTENTION_FP8 = 5  /* csa_attention_fp8 */
 } csa_op;
 
 /* Problem sizes (host struct). */
@@ -227,6 +228,28 @@ csa_status csa_attention(const csa_dims *dims, const void *q, const void *q_idx,
                          const int32_t *seq_len, const int32_t *q_pos, const float *sink,
                          float *out, float *lse, int32_t *topk_idx_out, float *scores_out,
                          void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Whole CSA step with fp8 index tensors: csa_index_scores_fp8 ->
+ * csa_topk_select -> csa_sparse_mqa_decode on one stream, the fp8 form of
+ * csa_attention ([C] quantization_config: fp8 E4M3; [A] INNOVATIONS 1, the
+ * indexer in low precision).  The index query and keys are E4M3 codes with
+ * per-row scales, as csa_index_scores_fp8 (q8 16-byte aligned, every k8[b]
+ * 16-byte aligned); the attention side (q, kv, v, win, win_v) is bf16, so
+ * dims->dtype must be CSA_BF16, with index_heads 64 and index_dim 128.  The
+ * fp8 scorer writes the selection's histogram windows and emitted entries as
+ * the bf16 decode scorer does, for every query count (no GEMM-tiled fp8
+ * scorer: many queries per sequence work but re-read the keys per query).
+ * Workspace: csa_workspace_size with CSA_OP_ATTENTION_FP8.  Other arguments,
+ * outputs and errors as csa_attention.
+ */
+csa_status csa_attention_fp8(const csa_dims *dims, const void *q, const uint8_t *q8, const float *q_scale,
+                             const float *w, const void *const *k8, const void *const *k_scale,
+                             const void *const *kv, const void *const *v, const void *const *win,
+                             const void *const *win_v, const int32_t *win_pos0, const int32_t *win_rows,
+                             const int32_t *seq_len, const int32_t *q_pos, const float *sink, float *out,
+                             float *lse, int32_t *topk_idx_out, float *scores_out, void *workspace,
+                             size_t ws_bytes, void *stream);
 
 /*
  * csa_attention without a caller workspace, for callers that cannot allocate

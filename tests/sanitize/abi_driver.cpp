@@ -183,6 +183,27 @@ int main() {
     expect(csa_attention(&d, p, nullptr, fp, pp, pp, nullptr, pp, nullptr, ip, ip, ip, ip, fp, fo, fo, nullptr,
                          nullptr, p, 16, nullptr),
            CSA_ERR_NULL, "attention q_idx NULL");
+    // the fp8 index path: sizes, its own checks
+    d = decode_dims();
+    expect(csa_workspace_size(&d, CSA_OP_ATTENTION_FP8, &bytes), CSA_OK, "fp8 fused sizes");
+    d.dtype = CSA_F32;
+    expect(csa_workspace_size(&d, CSA_OP_ATTENTION_FP8, &bytes), CSA_ERR_UNSUPPORTED, "fp8 fused, fp32 attention");
+    d = decode_dims();
+    d.index_dim = 64;
+    expect(csa_workspace_size(&d, CSA_OP_ATTENTION_FP8, &bytes), CSA_ERR_UNSUPPORTED, "fp8 fused, index_dim 64");
+    d = decode_dims();
+    const uint8_t *q8 = (const uint8_t *)buf;
+    expect(csa_attention_fp8(&d, p, q8, nullptr, fp, pp, pp, pp, nullptr, pp, nullptr, ip, ip, ip, ip, fp, fo, fo,
+                             nullptr, nullptr, p, 1u << 30, nullptr),
+           CSA_ERR_NULL, "fp8 fused q_scale NULL");
+    expect(csa_attention_fp8(&d, p, q8, fp, fp, pp, pp, pp, nullptr, pp, nullptr, ip, ip, ip, ip, fp, fo, fo, nullptr,
+                             nullptr, p, 16, nullptr),
+           CSA_ERR_WORKSPACE, "fp8 fused small workspace");
+    d.q_len = 2048;
+    d.batch = 1;
+    sizes(d, CSA_OK, "prefill sizes before the fp8 ones");
+    expect(csa_workspace_size(&d, CSA_OP_ATTENTION_FP8, &bytes), CSA_OK, "fp8 fused prefill sizes");
+    d = decode_dims();
     d.batch = 1 << 20;  // far beyond the static work area
     expect(csa_attention_noalloc(&d, p, p, fp, pp, pp, nullptr, pp, nullptr, ip, ip, ip, ip, fp, fo, fo, nullptr,
                                  nullptr, nullptr),

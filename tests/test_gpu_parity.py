@@ -558,6 +558,70 @@ def test_fp8_scores_decode_b4_1m_full():
     check_fp8_scores(inputs.make_case(inputs.WORKLOADS["decode_b4_1m"], with_hca=False))
 
 
+def check_fp8_step(case, act=csa.CSA_ACT_RELU, fp8=None):
+    """csa_attention_fp8 (fp8 index, bf16 attention): its scores against the
+    oracle's fp8 definition, its selection against the standalone top-k on the
+    same scores (bit-exact) and the oracle's set (band rule), its attention
+    against the oracle on its own selection."""
+    wl = case.wl
+    say(f"[case] fp8 step {wl.name} B={wl.batch} T={wl.q_len} max_entries={case.max_entries} act={act}")
+    q8, qs, k8, ks = inputs.make_fp8_index(case) if fp8 is None else fp8
+    dev = "cuda"
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    dc = DeviceCase(case)
+    dims = dc.csa_dims(index_act=act)
+    scores = torch.empty((dims.batch, dims.q_len, dims.max_entries), dtype=torch.float32, device=dev)
+    idx = torch.empty((dims.batch, dims.q_len, dims.topk), dtype=torch.int32, device=dev)
+    out, lse = csa.csa_attention_fp8(dims, dc.q, t(q8), t(qs), dc.w, [t(k) for k in k8], [t(x) for x in ks],
+                                     dc.kv_p, dc.v_p, dc.win_p, dc.win_v_p, dc.win_pos0, dc.win_rows, dc.seq_len,
+                                     dc.q_pos, dc.sink, topk_idx_out=idx, scores_out=scores)
+    g_scores, g_idx, g_out, g_lse = _np(scores), _np(idx), _np(out), _np(lse)
+    o_scores = oracle.index_scores_fp8(q8, qs, case.w, k8, ks, case.seq_len, case.q_pos, ratio=wl.ratio,
+                                       n_max=max(1, case.max_entries),
+                                       act=oracle.ACT_NONE if act == csa.CSA_ACT_NONE else oracle.ACT_RELU)
+    assert_scores_close(g_scores, o_scores, case)
+    t_idx = _np(csa.csa_topk_select(dims, scores, dc.seq_len, dc.q_pos))
+    np.testing.assert_array_equal(g_idx, t_idx)
+    o_idx = oracle.topk(o_scores, case.seq_len, case.q_pos, ratio=wl.ratio, k=wl.topk)
+    n_diff = assert_topk_band(g_idx, o_idx, o_scores, case)
+    o_out, o_lse = oracle_sparse(case, g_idx)
+    rel = assert_attention_close(g_out, o_out, ATT_TOL_BF16, "out")
+    np.testing.assert_allclose(g_lse, o_lse, atol=1e-3, rtol=0)
+    say(f"  ok: topk band swaps={n_diff} out err/rms={rel:.2e}")
+
+
+@pytest.mark.parametrize("lens,T,q_pos0", [
+    ([4 * 9000 + 2, 4 * 3000 + 1, 4 * 64 * 7], 1, None),   # ragged, emitted lists, several splits
+    ([50, 4 * 700 + 3], 1, None),                          # nothing compressed visible in one sequence
+    ([4 * 20000 + 3], 12, 4 * 20000 + 3 - 40),              # several queries of one sequence
+])
+def test_fp8_step_small(lens, T, q_pos0):
+    wl, sl = flash_case(f"fp8_step_{T}_{lens[0]}", lens, q_len=T, q_pos0=q_pos0)
+    check_fp8_step(make_case_with_lens(wl, sl))
+
+
+def test_fp8_step_no_activation():
+    wl, sl = flash_case("fp8_step_noact", [4 * 6000 + 1, 4 * 2500])
+    check_fp8_step(make_case_with_lens(wl, sl), act=csa.CSA_ACT_NONE)
+
+
+def test_fp8_step_when_emitted_lists_fall_short():
+    """Every key row of sequence 0 equal (all scores tie) and sequence 1's key
+    codes clustered: the scorer's emitted lists overflow or cut too high and the
+    selection falls back to scanning the scores, still exact."""
+    wl, sl = flash_case("fp8_step_ties", [4 * 30000 + 1, 4 * 16000 + 2])
+    case = make_case_with_lens(wl, sl)
+    q8, qs, k8, ks = inputs.make_fp8_index(case)
+    k8[0][:] = k8[0][0]
+    ks[0][:] = ks[0][0]
+    k8[1][: len(k8[1]) // 2] = k8[1][0]
+    check_fp8_step(case, fp8=(q8, qs, k8, ks))
+
+
+def test_fp8_step_decode_b4_1m_full():
+    check_fp8_step(inputs.make_case(inputs.WORKLOADS["decode_b4_1m"], with_hca=False))
+
+
 # --------------------------------------------------------------------------- V4-Pro shapes (128 heads, top-1024)
 
 def _pro_case(name, lens, index=111):
