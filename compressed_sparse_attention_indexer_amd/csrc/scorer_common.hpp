@@ -12,6 +12,7 @@ constexpr int kScoreWaves = 4;   // waves per decode-scorer workgroup
 constexpr int kTargetWgs = 256;  // decode scorers: about one workgroup per CU
 constexpr int kEmitMax = 8192;   // entries of a stretch whose keys stay in LDS for the emission
 constexpr int kEmitCapMax = 512; // emitted entries per workgroup at most
+constexpr int kEmitTargetSlots = 4096;  // emitted slots per query the cap aims at, at least
 
 // Indexer activation on an MFMA result: ReLU (kAct 0) or identity.  ReLU is
 // a signed-integer max with 0 on the bit pattern (negative floats, -0.0
@@ -41,8 +42,15 @@ inline int decode_emit_cap(int n_max, int n_queries, int K, int wg_step) {
     const int steps = (n_max + wg_step - 1) / wg_step;
     const int chunk = (steps + wgs - 1) / wgs;
     if ((long)chunk * wg_step > kEmitMax) return 0;
-    // about twice a workgroup's expected share of the K selected entries, plus a margin
+    // about twice a workgroup's expected share of the K selected entries, plus a
+    // margin, and at least an even share of 4,096 slots per query: with few
+    // workgroups per query the threshold bin (1/8 octave) can hold more than K
+    // entries, and a region that cannot emit all of its entries at or above it
+    // sends the query to the slower whole-row selection (2 of the 32 queries of
+    // a ragged batch at 64K-128K tokens did with 176 slots per region)
     int cap = (2 * K / wgs + 48 + 15) / 16 * 16;
+    const int even = (kEmitTargetSlots / wgs + 15) / 16 * 16;
+    cap = cap > even ? cap : even;
     cap = cap < 32 ? 32 : (cap > kEmitCapMax ? kEmitCapMax : cap);
     while (cap > 32 && (long)cap * wgs > kTopkMaxSlots) cap -= 16;
     // the selection's radix pass over the emitted slots needs more slots than K

@@ -8,10 +8,18 @@
 
 namespace csa {
 
+typedef int i32x8_t __attribute__((ext_vector_type(8)));  // 32 fp8 codes, an f8f6f4 MFMA operand
+
 // ---------------------------------------------------------------------------
 // fp8 (OCP E4M3) decode scorer with per-row scales, HI = 64, DI = 128: the
-// organisation of the bf16 decode scorer on v_mfma_f32_16x16x32_fp8_fp8
-// (A: 8 codes of head e's row per lane, B: 8 codes of entry e per lane).
+// organisation of the bf16 decode scorer on gfx950's
+// v_mfma_f32_16x16x128_f8f6f4 (both operands E4M3, no block scales), one
+// instruction per 16 heads x 16 entries x all 128 dims: lane (e, g) holds
+// codes 32g .. 32g + 31 of head e's row (A) and of entry e's row (B).  A and B
+// take their codes in the same lane positions, so the sum runs over every dim
+// once whatever order the instruction adds them in.  Against four
+// v_mfma_f32_16x16x32_fp8_fp8 per tile: 31.5 -> 29.3 us for batch 4 x 262,144
+// entries.
 // Keys are 128 bytes per entry, half the bf16 stream.  Scales are positive,
 // so ReLU commutes with them: s_j = k_scale_j * sum_h (w_h q_scale_h)
 // act(q8_h . k8_j); the head weights absorb the query scales once, and each
@@ -51,13 +59,15 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_fp8_kernel(S
     const bool with_hist = kHist && nvis > a.K;  // same for the whole workgroup
     float *srow = a.scores + (size_t)qi * a.n_max;
 
-    // A fragments: head 16*ht + e, codes 32s + 8g .. +8 for k-step s.
-    uint64_t qa[4][4];
+    i32x8_t qa[4];  // A fragments: head 16*ht + e, codes 32g .. 32g + 31
     const uint8_t *qb = (const uint8_t *)a.q_idx + (size_t)qi * kHI * kDI;
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) qa[ht][s] = *(const uint64_t *)(qb + (16 * ht + e) * kDI + 32 * s + 8 * g);
+    for (int ht = 0; ht < 4; ++ht) {
+        const u32x4_t lo = *(const u32x4_t *)(qb + (16 * ht + e) * kDI + 32 * g);
+        const u32x4_t hi = *(const u32x4_t *)(qb + (16 * ht + e) * kDI + 32 * g + 16);
+        qa[ht] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
     // weights of the C-tile rows this lane holds (head 16*ht + 4g + r), times the query-row scales
     float wr[4][4];
 #pragma unroll
@@ -105,18 +115,16 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_fp8_kernel(S
         float mine = 0.f;
 #pragma unroll
         for (int et = 0; et < 4; ++et) {
-            uint64_t kf[4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) kf[s] = *(const uint64_t *)&kw[(16 * et + e) * kF8RowWords + 8 * s + 2 * g];
+            const u32x4_t klo = *(const u32x4_t *)&kw[(16 * et + e) * kF8RowWords + 8 * g];
+            const u32x4_t khi = *(const u32x4_t *)&kw[(16 * et + e) * kF8RowWords + 8 * g + 4];
+            const i32x8_t kf = i32x8_t{(int)klo[0], (int)klo[1], (int)klo[2], (int)klo[3],
+                                       (int)khi[0], (int)khi[1], (int)khi[2], (int)khi[3]};
+            // operand formats 0, 0: E4M3 x E4M3; scale operands 0: no block scaling
+            const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
             f32x4_t acc[4];
 #pragma unroll
-            for (int ht = 0; ht < 4; ++ht) {
-                acc[ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)qa[ht][s], (long)kf[s], acc[ht], 0, 0,
-                                                                        0);
-            }
+            for (int ht = 0; ht < 4; ++ht)
+                acc[ht] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[ht], kf, zero, 0, 0, 0, 0, 0, 0);
             float p = 0.f;
 #pragma unroll
             for (int ht = 0; ht < 4; ++ht)
