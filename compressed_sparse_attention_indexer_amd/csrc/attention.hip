@@ -242,10 +242,17 @@ __global__ __launch_bounds__(128 * HG, 2) void mqa_bf16_kernel(MqaArgs a) {
     // a missing row (padding, out of range, past the list) reads this query's q
     // instead: finite values whose logit is masked to -inf, so its weight is 0
     const uint16_t *dummy = (const uint16_t *)a.q + (size_t)qi * a.H * kD;
-    auto fetch = [&](int t) {
+    // top-k list value of this thread's staging row in tile t (-2 where the row
+    // is not a selected entry), read one tile ahead of the row itself: read
+    // inside the row fetch, each tile's row loads waited a whole global round
+    // trip for their index first
+    auto list_value = [&](int t) {
+        const int i = r0 + t * kTile + srow;
+        return a.topk_idx && i < r1 && i < rl.n_sel ? a.topk_idx[(size_t)qi * a.K + i] : -2;
+    };
+    auto fetch = [&](int t, int jl) {
         const uint16_t *kp, *vp;
-        row_ptrs(a, sq, qi, rl, r0 + t * kTile + srow < r1 ? r0 + t * kTile + srow : -1, &kp, &vp,
-                 t == 0 ? j_first : -2);
+        row_ptrs(a, sq, qi, rl, r0 + t * kTile + srow < r1 ? r0 + t * kTile + srow : -1, &kp, &vp, jl);
         have_row = kp != nullptr;
         if (!have_row) kp = vp = dummy;
 #pragma unroll
@@ -255,7 +262,11 @@ __global__ __launch_bounds__(128 * HG, 2) void mqa_bf16_kernel(MqaArgs a) {
             if (kSepV) vreg[c] = *as_global<u32x4_t>(vp + 8 * ch);
         }
     };
-    if (ntiles > 0) fetch(0);
+    int j_next = -2;  // list value for the next tile's fetch
+    if (ntiles > 0) {
+        fetch(0, j_first);
+        if (ntiles > 1) j_next = list_value(1);
+    }
 
     for (int t = 0; t < ntiles; ++t) {
         __syncthreads();  // previous tile fully consumed
@@ -266,7 +277,10 @@ __global__ __launch_bounds__(128 * HG, 2) void mqa_bf16_kernel(MqaArgs a) {
             if (kSepV) *(u32x4_t *)&vrow_sep[srow * kKrowStride + 8 * ch] = vreg[c];
         }
         if (cg == 0) rowok[srow] = have_row;
-        if (t + 1 < ntiles) fetch(t + 1);
+        if (t + 1 < ntiles) {
+            fetch(t + 1, j_next);
+            if (t + 2 < ntiles) j_next = list_value(t + 2);
+        }
         __syncthreads();
 
         // QK over this wave's 256 dims.

@@ -36,14 +36,22 @@ constexpr int kF8RowWords = 128 / 4 + 4;               // LDS row: 128 codes + 1
 constexpr int kF8Depth = 2;                            // wave-steps of loads in flight
 struct F8Raw {
     u32x4_t k[8];  // 64 rows x 128 bytes, 16 bytes per lane per load
-    float ks;      // scale of the entry this lane stores
+    float ks;      // scale of the entry this lane stores (scales read from global memory per step)
 };
 }  // namespace
 
-template <int kAct, bool kHist, int kDepth>
+// kLdsScale: the stretch's key scales are read into LDS once, before the key
+// stream starts (the host picks it when every stretch fits kEmitMax entries).
+// Read per step from global memory instead, next to the keys, the 4-byte scale
+// loads and the score stores together made the compiler wait for every load
+// in flight at each pass of the loop (vmcnt(0)), so the two steps in flight
+// drained every other step: 27.8 against 24.3 us for the same loop without
+// scales, without the MFMA work.
+template <int kAct, bool kHist, bool kLdsScale, int kDepth>
 __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_fp8_kernel(ScoreArgs a) {
     __shared__ uint32_t lh[kHist ? kTopkBins : 1];
     __shared__ uint32_t lkeys[kHist ? kEmitMax : 1];  // keys of this workgroup's stretch (emission)
+    __shared__ float lks[kLdsScale ? kEmitMax : 1];   // key scales of this workgroup's stretch
     __shared__ __attribute__((aligned(16))) uint32_t kraw[kScoreWaves][kF8WaveStep * kF8RowWords];
     __shared__ int s_red[4];
     __shared__ int s_scan[4];  // the emission's scans (s_red may still be read after the window store)
@@ -100,18 +108,20 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_fp8_kernel(S
             j = j < nvis ? j : last;
             kr.k[i] = __builtin_nontemporal_load(as_global<u32x4_t>(kb + (size_t)j * kDI + 16 * (lane & 7)));
         }
-        int js = base + 16 * g + e;
-        js = js < nvis ? js : last;
-        kr.ks = ksb[js];
+        if (!kLdsScale) {
+            int js = base + 16 * g + e;
+            js = js < nvis ? js : last;
+            kr.ks = ksb[js];
+        }
     };
     uint32_t *kw = kraw[wave];
     int hmax = -1;  // highest histogram bin this thread added
     auto process = [&](F8Raw &kr, int base, bool live, int next) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) *(u32x4_t *)&kw[(8 * i + (lane >> 3)) * kF8RowWords + 4 * (lane & 7)] = kr.k[i];
-        const float ks = kr.ks;
-        load(kr, next);  // registers free again: the next loads go out before the math
         const int j = base + 16 * g + e;  // entry this lane stores
+        const float ks = kLdsScale ? lks[j < nvis ? j - stretch0 : 0] : kr.ks;
+        load(kr, next);  // registers free again: the next loads go out before the math
         float mine = 0.f;
 #pragma unroll
         for (int et = 0; et < 4; ++et) {
@@ -155,6 +165,24 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_fp8_kernel(S
 #pragma unroll
         for (int i = 0; i < kDepth; ++i) load(kbuf[i], step(i));
     }
+    // visible entries of this stretch: stretch0 .. stretch0 + n_st - 1
+    int n_st = min(nvis, (s0 + n_load) * kF8WgStep) - stretch0;
+    n_st = n_st > 0 ? n_st : 0;
+    if (kLdsScale) {  // after the first key loads, so their latency covers these
+        // indices past the stretch are clamped to its last entry: those lanes
+        // read and write that entry's own scale again (no branch around a store)
+        constexpr int kNT = 64 * kScoreWaves, kU = 16;
+        for (int i0 = 0; i0 < n_st; i0 += kNT * kU) {
+            float v[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int i = min(i0 + kNT * u + (int)threadIdx.x, n_st - 1);
+                v[u] = ksb[stretch0 + i];
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u) lks[min(i0 + kNT * u + (int)threadIdx.x, n_st - 1)] = v[u];
+        }
+    }
     if (with_hist) {
         for (int i = threadIdx.x; i < kTopkBins; i += 64 * kScoreWaves) lh[i] = 0u;
     }
@@ -174,8 +202,6 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_fp8_kernel(S
         const size_t w = (size_t)qi * gridDim.x + blockIdx.x;
         hist_window_store_top(lh, hmax, a.win_hdr + w, a.win_cnt + w * kTopkWin, s_red);
         if (emit) {  // hist_window_store_top's barrier also orders the key stores
-            int n_st = min(nvis, (s0 + n_load) * kF8WgStep) - stretch0;
-            n_st = n_st > 0 ? n_st : 0;
             emit_region<64 * kScoreWaves>(lh, lkeys, n_st, stretch0, a.em_cap, a.em_hdr + 2 * w,
                                           a.em_key + w * a.em_cap, a.em_idx + w * a.em_cap, s_scan, &s_cut);
         }
@@ -188,20 +214,28 @@ int score_workgroups_fp8(int n_max, int n_queries) {
 
 int score_emit_cap_fp8(int n_max, int n_queries, int K) { return decode_emit_cap(n_max, n_queries, K, kF8WgStep); }
 
+template <int kAct, bool kHist>
+static void launch_fp8(const ScoreArgs &a, dim3 grid, dim3 block, bool lds_scale, hipStream_t stream) {
+    if (lds_scale)
+        hipLaunchKernelGGL((index_scores_fp8_kernel<kAct, kHist, true, kF8Depth>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((index_scores_fp8_kernel<kAct, kHist, false, kF8Depth>), grid, block, 0, stream, a);
+}
+
 hipError_t launch_index_scores_fp8(const ScoreArgs &a, hipStream_t stream) {
     const int Q = a.B * a.T;
-    const dim3 grid(score_workgroups_fp8(a.n_max, Q), Q), block(64 * kScoreWaves);
+    const int wgs = score_workgroups_fp8(a.n_max, Q);
+    const dim3 grid(wgs, Q), block(64 * kScoreWaves);
     const bool hist = a.win_hdr != nullptr;  // the caller sized the windows with score_workgroups_fp8
+    // every workgroup's stretch (at most ceil(steps / workgroups) steps) fits the LDS scale buffer
+    const int steps = (a.n_max + kF8WgStep - 1) / kF8WgStep;
+    const bool lds_scale = (long)((steps + wgs - 1) / wgs) * kF8WgStep <= kEmitMax;
     if (a.act == 0) {
-        if (hist)
-            hipLaunchKernelGGL((index_scores_fp8_kernel<0, true, kF8Depth>), grid, block, 0, stream, a);
-        else
-            hipLaunchKernelGGL((index_scores_fp8_kernel<0, false, kF8Depth>), grid, block, 0, stream, a);
+        if (hist) launch_fp8<0, true>(a, grid, block, lds_scale, stream);
+        else launch_fp8<0, false>(a, grid, block, lds_scale, stream);
     } else {
-        if (hist)
-            hipLaunchKernelGGL((index_scores_fp8_kernel<1, true, kF8Depth>), grid, block, 0, stream, a);
-        else
-            hipLaunchKernelGGL((index_scores_fp8_kernel<1, false, kF8Depth>), grid, block, 0, stream, a);
+        if (hist) launch_fp8<1, true>(a, grid, block, lds_scale, stream);
+        else launch_fp8<1, false>(a, grid, block, lds_scale, stream);
     }
     return hipGetLastError();
 }
