@@ -464,19 +464,148 @@ __global__ __launch_bounds__(kWG) void topk_onekernel_kernel(TopkArgs a) {
 // instruction of a wave reads 256 contiguous bytes; the scorer zero-fills a
 // region's slots past its count, and no real key is 0).  If every region's cut
 // lies at or below the threshold bin, the emitted entries hold every entry at
-// or above it: they are split into the above and candidate lists in slot
-// order (per round and wave a ballot, one scan of the round-by-wave counts)
-// and selected as usual.  Otherwise (a region with too many high entries to
-// emit them all) the whole row is scanned with the threshold instead, and
-// without a usable threshold the exact radix selection runs.
+// or above it, and the selection runs on the slots as loaded (select_slots).
+// Otherwise (a region with too many high entries to emit them all) the whole
+// row is scanned with the threshold instead, and without a usable threshold
+// the exact radix selection runs.
 constexpr int kListRounds = kTopkMaxSlots / kWG;  // rounds of kWG slots at most
+
+// Selection straight from the slots, held in registers (slot r * kWG + tid in
+// key[r], idx[r]; slot order is index order, dead slots have key 0), given the
+// threshold bin: every live slot above it is taken, and of those inside it
+// ("candidates") the need = K - (above) largest keys, ties to the lower index.
+// Three radix levels over the candidates' low 20 key bits (8, 8 and 4 bits,
+// LDS histograms) give the exact K-th key t and how many slots equal to t are
+// taken; then one scan over the slots, counting per (round, wave) the slots
+// taken outright (above, or a candidate above t) and those equal to t, gives
+// each taken slot its output position: (taken outright before it) +
+// min(equal before it, equal taken).  Returns false (nothing written, the same
+// in every thread) if the counts are not those of a usable threshold.
+__device__ bool select_slots(const uint32_t (&key)[kListRounds], const int32_t (&idx)[kListRounds], int rounds,
+                             uint32_t bin, int K, int32_t *out, TopkShared &sh, uint32_t *s_base, int *s_red) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    auto isum = [](int x) {
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+        return x;
+    };
+    // level 1: candidates by key bits 19..12, and the count above the bin
+    if (tid < 256) sh.hist[tid] = 0u;
+    if (tid < kWaves) s_red[tid] = 0;
+    __syncthreads();
+    int n_above = 0;
+#pragma unroll
+    for (int r = 0; r < kListRounds; ++r) {
+        if (r < rounds) {
+            const uint32_t b = key[r] >> 20;
+            n_above += key[r] != 0u && b > bin;
+            if (key[r] != 0u && b == bin) atomicAdd(&sh.hist[(key[r] >> 12) & 0xFFu], 1u);
+        }
+    }
+    n_above = isum(n_above);
+    if (lane == 0) s_red[wave] = n_above;
+    __syncthreads();
+    int na = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) na += s_red[w];
+    const int need = K - na;
+    int nc = 0;  // candidates: the level-1 histogram's total
+    if (tid < 64) {
+        int c = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c += (int)sh.hist[4 * tid + i];
+        c = isum(c);
+        if (tid == 0) sh.bcast[0] = c;
+    }
+    __syncthreads();
+    nc = sh.bcast[0];
+    if (need < 1 || need > nc) return false;  // the same in every thread
+    __syncthreads();
+    find_bin_256(sh, need);
+    __syncthreads();
+    const uint32_t b2 = (uint32_t)sh.bcast[0];
+    const int need2 = sh.bcast[1];
+    const uint32_t p2 = (bin << 8) | b2;  // key bits 31..12 of the deciding candidates
+    // level 2: bits 11..4 of the candidates with bits 31..12 = p2
+    __syncthreads();
+    if (tid < 256) sh.hist[tid] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kListRounds; ++r)
+        if (r < rounds && key[r] != 0u && (key[r] >> 12) == p2) atomicAdd(&sh.hist[(key[r] >> 4) & 0xFFu], 1u);
+    __syncthreads();
+    find_bin_256(sh, need2);
+    __syncthreads();
+    const uint32_t b3 = (uint32_t)sh.bcast[0];
+    const int need3 = sh.bcast[1];
+    const uint32_t p3 = (p2 << 8) | b3;  // key bits 31..4
+    // level 3: bits 3..0
+    __syncthreads();
+    if (tid < 256) sh.hist[tid] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kListRounds; ++r)
+        if (r < rounds && key[r] != 0u && (key[r] >> 4) == p3) atomicAdd(&sh.hist[key[r] & 0xFu], 1u);
+    __syncthreads();
+    find_bin_256(sh, need3);
+    __syncthreads();
+    const uint32_t t = (p3 << 4) | (uint32_t)sh.bcast[0];  // the K-th key
+    const int n_eq_take = sh.bcast[1];                     // slots equal to t that are taken
+    // per (round, wave): slots taken outright | slots equal to t << 16
+    uint64_t m_def[kListRounds], m_eq[kListRounds];
+#pragma unroll
+    for (int r = 0; r < kListRounds; ++r) {
+        if (r < rounds) {
+            const uint32_t k = key[r];
+            const bool live = k != 0u;
+            m_def[r] = __ballot(live && ((k >> 20) > bin || ((k >> 20) == bin && k > t)));
+            m_eq[r] = __ballot(live && k == t);
+            if (lane == 0) s_base[r * kWaves + wave] = (uint32_t)__popcll(m_def[r]) | (uint32_t)__popcll(m_eq[r]) << 16;
+        }
+    }
+    __syncthreads();
+    if (tid < 64) {  // exclusive scan of the (round, wave) counts in slot order, 2 entries per lane
+        const int m = rounds * kWaves;
+        uint32_t c[2], sum = 0;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            c[i] = 2 * tid + i < m ? s_base[2 * tid + i] : 0u;
+            sum += c[i];
+        }
+        uint32_t inc = sum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t x = __shfl_up(inc, o);
+            if (tid >= o) inc += x;
+        }
+        uint32_t run = inc - sum;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            if (2 * tid + i < m) s_base[2 * tid + i] = run;
+            run += c[i];
+        }
+    }
+    __syncthreads();
+    const uint64_t lt = lanemask_lt();
+#pragma unroll
+    for (int r = 0; r < kListRounds; ++r) {
+        if (r < rounds) {
+            const uint32_t base = s_base[r * kWaves + wave];
+            const int d_before = (int)(base & 0xFFFFu) + __popcll(m_def[r] & lt);
+            const int e_before = (int)(base >> 16) + __popcll(m_eq[r] & lt);
+            if ((m_def[r] >> lane) & 1u) out[d_before + min(e_before, n_eq_take)] = idx[r];
+            else if (((m_eq[r] >> lane) & 1u) && e_before < n_eq_take) out[d_before + e_before] = idx[r];
+        }
+    }
+    return true;
+}
+
 __global__ __launch_bounds__(kWG) void topk_lists_kernel(TopkArgs a) {
     __shared__ __attribute__((aligned(16))) ScanShared sc;
     __shared__ TopkShared sh;
     __shared__ uint32_t s_hist[kTopkWin];
     __shared__ int s_red[kWaves];
-    __shared__ uint32_t s_base[kListRounds * kWaves];  // packed (above, candidates) before each (round, wave)
-    __shared__ uint32_t s_all;
+    __shared__ uint32_t s_base[kListRounds * kWaves];  // packed counts before each (round, wave)
     const int qi = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int K = a.K;
@@ -511,66 +640,7 @@ __global__ __launch_bounds__(kWG) void topk_lists_kernel(TopkArgs a) {
     const uint32_t bin = window_threshold(a.win_hdr + q0, a.win_cnt + q0 * kTopkWin, R, K, s_red, s_hist);
     // every region emitted all of its entries at or above the threshold bin?
     bool ok = bin != kNoBin && !__syncthreads_or(tid < R && ((uint32_t)cut > bin || cnt > cap));
-    if (ok) {
-        // pass 1: per (round, wave) counts of above-threshold and candidate slots
-        uint32_t cls = 0;  // bit 2r: above, bit 2r + 1: candidate
-#pragma unroll
-        for (int r = 0; r < kListRounds; ++r) {
-            if (r < rounds) {
-                const uint32_t b = key[r] >> 20;
-                const bool ga = key[r] != 0u && b > bin, gc = key[r] != 0u && b == bin;
-                cls |= (uint32_t)ga << (2 * r) | (uint32_t)gc << (2 * r + 1);
-                const uint32_t na = (uint32_t)__popcll(__ballot(ga)), nc = (uint32_t)__popcll(__ballot(gc));
-                if (lane == 0) s_base[r * kWaves + wave] = na | nc << 16;
-            }
-        }
-        __syncthreads();
-        if (tid < 64) {  // exclusive scan of the (round, wave) counts in slot order, 2 entries per lane
-            const int m = rounds * kWaves;
-            uint32_t c[2], sum = 0;
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                c[i] = 2 * tid + i < m ? s_base[2 * tid + i] : 0u;
-                sum += c[i];
-            }
-            uint32_t inc = sum;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const uint32_t t = __shfl_up(inc, o);
-                if (tid >= o) inc += t;
-            }
-            uint32_t run = inc - sum;
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                if (2 * tid + i < m) s_base[2 * tid + i] = run;
-                run += c[i];
-            }
-            if (tid == 63) s_all = inc;
-        }
-        __syncthreads();
-        const uint32_t all = s_all;
-        const int na = (int)(all & 0xFFFFu), nc = (int)(all >> 16);
-        ok = na < K && nc <= kTopkCand && na + nc >= K;
-        if (ok) {  // pass 2: slot-ordered writes into the two lists
-            const uint64_t lt = lanemask_lt();
-#pragma unroll
-            for (int r = 0; r < kListRounds; ++r) {
-                if (r < rounds) {
-                    const bool ga = (cls >> (2 * r)) & 1u, gc = (cls >> (2 * r + 1)) & 1u;
-                    const uint64_t mga = __ballot(ga), mgc = __ballot(gc);
-                    const uint32_t base = s_base[r * kWaves + wave];
-                    if (ga) sc.v[(base & 0xFFFFu) + __popcll(mga & lt)] = idx[r];
-                    if (gc) {
-                        const int pos = (int)(base >> 16) + __popcll(mgc & lt);
-                        sc.c_key[pos] = key[r];
-                        sc.c_idx[pos] = idx[r];
-                    }
-                }
-            }
-            __syncthreads();
-            ok = select_ordered(sc.v, na, sc.c_key, sc.c_idx, nc, K, out, sc.ss);
-        }
-    }
+    if (ok) ok = select_slots(key, idx, rounds, bin, K, out, sh, s_base, s_red);
     if (!ok && bin != kNoBin) {  // lists not usable: scan the row with the threshold
         __syncthreads();
         const bool vec = (a.n_max & 3) == 0 && ((uintptr_t)a.scores & 15) == 0;
