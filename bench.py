@@ -8,11 +8,19 @@ Inputs are seeded synthetic tensors, resident in HBM before timing.
 
 One step = one pass of the CSA layer's hot path through the fused entry
 point csa_attention: indexer scores -> top-k -> sparse MQA with sink, over
-the whole batch.  Steps are captured in a HIP graph and replayed; the index-key and KV
-caches rotate between enough device copies (at least twice the 256 MiB
+the whole batch.  Steps are captured in HIP graphs and replayed (two steps
+per replay, a HIP event after every replay: the line gives the mean over the
+timed steps and the p10/median/p90 of the per-replay figures); the index-key
+and KV caches rotate between enough device copies (at least twice the 256 MiB
 last-level cache in all, for every workload) that no step finds the previous
-steps' rows in that cache.  The paired HCA layer, the other
-decode workloads and the per-kernel times are reported under "breakdown".
+steps' rows in that cache.  The roofline block is for the indexer scorer (the
+dominant kernel; each entry point is also timed alone, 20 launches per graph)
+and for the whole step, against the 8 TB/s datasheet figure and against a
+plain streaming-read kernel measured in the same run over the same byte count.
+The breakdown holds the paired HCA layer, the fp8-index scorer and step, the
+compressor, the other decode workloads, the 2,048-query prefill chunk, the
+oracle's rates on the host, and amd-smi clock samples (before, under load and
+after).
 
 Prints one JSON line.
 """

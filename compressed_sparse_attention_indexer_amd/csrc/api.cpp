@@ -115,20 +115,25 @@ size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 // decode-scorer workgroup, or per entry chunk of the tiled bf16 scorer) and
 // from the top-k's own histogram kernel otherwise (0 here).  The fp8 index
 // path always takes the decode scorer.
+// The decode scorer's geometry in the fused call (the tiled bf16 scorer for many
+// queries per sequence has none): windows and regions per query, emitted
+// entries per region.
+bool fused_decode(const csa_dims *d, bool fp8) {
+    return d->dtype == CSA_BF16 && (fp8 || !csa::score_uses_tiles(csa::kBF16, d->q_len));
+}
+csa::DecodeGeom decode_geom(const csa_dims *d, bool fp8) {
+    return csa::decode_geom(fp8, d->max_entries, n_queries(d), d->topk);
+}
 int win_count(const csa_dims *d, bool fused, bool fp8 = false) {
     if (!fused || d->dtype != CSA_BF16) return 0;
-    if (fp8) return csa::score_workgroups_fp8(d->max_entries, n_queries(d));
-    if (csa::score_uses_tiles(csa::kBF16, d->q_len)) return csa::tiled_windows(d->batch, d->q_len, d->max_entries);
-    return csa::score_workgroups(d->max_entries, n_queries(d));
+    if (!fused_decode(d, fp8)) return csa::tiled_windows(d->batch, d->q_len, d->max_entries);
+    return decode_geom(d, fp8).n_win;
 }
-// Entries per decode-scorer workgroup handed to the selection in the fused
-// call (0: the selection scans the scores itself).
+// Entries per decode-scorer region handed to the selection in the fused call
+// (0: the selection scans the scores itself).
 int emit_cap(const csa_dims *d, bool fused, bool fp8 = false) {
-    if (!fused || d->dtype != CSA_BF16) return 0;
-    if (!csa::topk_uses_histogram(d->max_entries)) return 0;
-    if (fp8) return csa::score_emit_cap_fp8(d->max_entries, n_queries(d), d->topk);
-    if (csa::score_uses_tiles(csa::kBF16, d->q_len)) return 0;
-    return csa::score_emit_cap(d->max_entries, n_queries(d), d->topk);
+    if (!fused || !fused_decode(d, fp8) || !csa::topk_uses_histogram(d->max_entries)) return 0;
+    return decode_geom(d, fp8).em_cap;
 }
 size_t ws_topk(const csa_dims *d, bool fused = false, bool fp8 = false) {
     return csa::topk_workspace_bytes(n_queries(d), d->topk, d->max_entries, win_count(d, fused, fp8),

@@ -171,7 +171,7 @@ __global__ __launch_bounds__(256) void mqa_f32_kernel(MqaArgs a) {
 namespace {
 constexpr int kD = 512;
 constexpr int kTile = 32;
-constexpr int kKrowStride = kD + 8;   // bf16 elements per staged row (1040 B)
+constexpr int kKrowStride = kD + 16;  // bf16 elements per staged row (1056 B: HCA 26.3 -> 25.8 us against 1040 B)
 constexpr float kLazyMax = 8.f;       // log2 headroom of the running softmax reference
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef short v8i16_t __attribute__((ext_vector_type(8)));

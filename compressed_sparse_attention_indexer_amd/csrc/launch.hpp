@@ -37,11 +37,14 @@ hipError_t launch_index_scores(const ScoreArgs &a, int dtype, hipStream_t stream
 // fp8 (E4M3) index queries and keys with per-row scales, HI = 64, DI = 128
 // (histogram windows and emitted entries as for the bf16 decode scorer)
 hipError_t launch_index_scores_fp8(const ScoreArgs &a, hipStream_t stream);
-int score_workgroups_fp8(int n_max, int n_queries);             // fp8 scorer workgroups per query
-int score_emit_cap_fp8(int n_max, int n_queries, int K);        // as score_emit_cap, for the fp8 scorer
-int score_workgroups(int n_max, int n_queries);  // bf16 scorer workgroups per query
-// entries per workgroup the decode scorer can hand the selection, 0 if it cannot
-int score_emit_cap(int n_max, int n_queries, int K);
+
+int score_workgroups(int n_max, int n_queries);  // bf16 scorer workgroups per query (even split)
+// Decode-scorer geometry for the fused call: workgroups (= histogram windows
+// and emitted regions) per query, emitted entries per region (0: none)
+struct DecodeGeom {
+    int n_win, em_cap, step;
+};
+DecodeGeom decode_geom(bool fp8, int n_max, int n_queries, int K);
 // many queries per sequence: the GEMM-tiled scorer
 bool score_uses_tiles(int dtype, int T);
 // histogram windows per query the tiled scorer can write (its entry chunks), 0 if it cannot

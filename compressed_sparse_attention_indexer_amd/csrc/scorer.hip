@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void index_scores_f32_kernel(ScoreArgs a) {
 // its keys and hands the selection its entries at and above a cut bin.
 namespace {
 constexpr int kWaveStep = 32;                         // entries per wave and step
-constexpr int kWgStep = kScoreWaves * kWaveStep;      // entries per workgroup step
+constexpr int kWgStep = kBf16WgStep;                  // entries per workgroup step
 constexpr int kScoreDepth = 2;                        // key steps in flight per wave
 typedef bf16x8_t KeyFrag[2][4];
 typedef u32x4_t KeyRaw[8];  // a wave-step of keys as loaded: 8 KiB, 16 B per lane per load
@@ -85,7 +85,8 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(
     __shared__ int s_red[4];
     __shared__ int s_scan[4];  // the emission's scans (s_red may still be read after the window store)
     __shared__ int s_cut;
-    const int qi = blockIdx.y;
+    // this workgroup's query, and its part of the query's entries (of n_parts)
+    const int qi = blockIdx.y, part = blockIdx.x, n_parts = gridDim.x;
     const int b = qi / a.T;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -115,19 +116,20 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(
     const uint16_t *kb = (const uint16_t *)a.k_idx[b];
     const int last = nvis > 0 ? nvis - 1 : 0;
     // Work split: the query's visible entries, in workgroup steps of kWgStep,
-    // are cut into gridDim.x contiguous ranges, one per workgroup, so each
+    // are cut into n_parts contiguous ranges, one per workgroup, so each
     // workgroup streams one stretch of the key rows; wave w takes entries
     // kWaveStep * w .. + kWaveStep - 1 of each step (step k of this wave starts
     // at entry base0 + k * stride).  Steps wholly past the visible entries get
     // -inf only, dealt round-robin.
     const int vis_steps = (nvis + kWgStep - 1) / kWgStep;
-    const int chunk = (vis_steps + (int)gridDim.x - 1) / (int)gridDim.x;
-    const int s0 = blockIdx.x * chunk;
+    const int chunk = (vis_steps + n_parts - 1) / n_parts;
+    const int s0 = part * chunk;
     const int n_load = vis_steps - s0 < chunk ? (vis_steps - s0 > 0 ? vis_steps - s0 : 0) : chunk;
     const int stride = kWgStep;
     const int base0 = s0 * kWgStep + wave * kWaveStep;
-    // emission: the host enables it only when every stretch fits in lkeys
-    const bool emit = kHist && with_hist && a.em_cap > 0;
+    // emission: the host enables it only when every stretch fits in lkeys (checked
+    // here too: a stretch that does not fit marks its region overflowed instead)
+    const bool emit = kHist && with_hist && a.em_cap > 0 && n_load * kWgStep <= kEmitMax;
     const int stretch0 = s0 * kWgStep;
 
     // Every load is unconditional (indices clamped into the visible rows) so
@@ -228,19 +230,14 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(
         }
     }
     const int all_steps = (a.n_max + kWgStep - 1) / kWgStep;
-    for (int st = vis_steps + blockIdx.x; st < all_steps; st += gridDim.x) {  // steps past the visible entries
+    for (int st = vis_steps + part; st < all_steps; st += n_parts) {  // steps past the visible entries
         const int j = st * kWgStep + wave * kWaveStep + 16 * g + e;
         if (g < 2 && j < a.n_max) srow[j] = -INFINITY;
     }
     if (with_hist) {
-        const size_t w = (size_t)qi * gridDim.x + blockIdx.x;
+        const size_t w = (size_t)qi * n_parts + part;
         hist_window_store_top(lh, hmax, a.win_hdr + w, a.win_cnt + w * kTopkWin, s_red);
-        if (emit) {  // hist_window_store_top's barrier also orders the key stores
-            int n_st = min(nvis, (s0 + n_load) * kWgStep) - stretch0;
-            n_st = n_st > 0 ? n_st : 0;
-            emit_region<64 * kScoreWaves>(lh, lkeys, n_st, stretch0, a.em_cap, a.em_hdr + 2 * w,
-                                          a.em_key + w * a.em_cap, a.em_idx + w * a.em_cap, s_scan, &s_cut);
-        }
+        decode_emission<64 * kScoreWaves>(a, lh, lkeys, emit, nvis, s0, n_load, kWgStep, w, s_scan, &s_cut);
     }
 }
 
@@ -520,7 +517,7 @@ hipError_t launch_index_scores(const ScoreArgs &a, int dtype, hipStream_t stream
         }
         return hipGetLastError();
     }
-    dim3 grid(score_workgroups(a.n_max, Q), Q);
+    const dim3 grid(score_workgroups(a.n_max, Q), Q);
     dim3 block(64 * kScoreWaves);
     const bool hist = a.win_hdr != nullptr;
     if (a.act == 0) {
@@ -545,8 +542,10 @@ int tiled_windows(int B, int T, int n_max) {
     return tiled_plan(a).n_chunks;
 }
 
-int score_emit_cap(int n_max, int n_queries, int K) { return decode_emit_cap(n_max, n_queries, K, kWgStep); }
-
 int score_workgroups(int n_max, int n_queries) { return decode_score_workgroups(n_max, n_queries, kWgStep); }
+
+DecodeGeom decode_geom(bool fp8, int n_max, int n_queries, int K) {
+    return decode_geom_for(n_max, n_queries, K, fp8 ? kFp8WgStep : kBf16WgStep);
+}
 
 }  // namespace csa

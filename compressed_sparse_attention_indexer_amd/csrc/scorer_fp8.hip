@@ -31,7 +31,7 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));  // 32 fp8 codes, an f8
 // can build the selection's histogram window and emitted entries as it goes.
 namespace {
 constexpr int kF8WaveStep = 64;                        // entries per wave and step
-constexpr int kF8WgStep = kScoreWaves * kF8WaveStep;   // entries per workgroup step
+constexpr int kF8WgStep = kFp8WgStep;                  // entries per workgroup step
 constexpr int kF8RowWords = 128 / 4 + 4;               // LDS row: 128 codes + 16 B pad
 constexpr int kF8Depth = 2;                            // wave-steps of loads in flight
 struct F8Raw {
@@ -56,7 +56,8 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_fp8_kernel(S
     __shared__ int s_red[4];
     __shared__ int s_scan[4];  // the emission's scans (s_red may still be read after the window store)
     __shared__ int s_cut;
-    const int qi = blockIdx.y;
+    // this workgroup's query, and its part of the query's entries (of n_parts)
+    const int qi = blockIdx.y, part = blockIdx.x, n_parts = gridDim.x;
     const int b = qi / a.T;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -90,15 +91,16 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_fp8_kernel(S
     const float *ksb = (const float *)a.k_scale[b];
     const int last = nvis > 0 ? nvis - 1 : 0;
     // Work split as in the bf16 kernel: the query's visible entries, in
-    // workgroup steps of kF8WgStep, are cut into gridDim.x contiguous stretches;
+    // workgroup steps of kF8WgStep, are cut into n_parts contiguous stretches;
     // wave w takes entries kF8WaveStep * w .. + kF8WaveStep - 1 of each step.
     const int vis_steps = (nvis + kF8WgStep - 1) / kF8WgStep;
-    const int chunk = (vis_steps + (int)gridDim.x - 1) / (int)gridDim.x;
-    const int s0 = blockIdx.x * chunk;
+    const int chunk = (vis_steps + n_parts - 1) / n_parts;
+    const int s0 = part * chunk;
     const int n_load = vis_steps - s0 < chunk ? (vis_steps - s0 > 0 ? vis_steps - s0 : 0) : chunk;
     const int stride = kF8WgStep;
     const int base0 = s0 * kF8WgStep + wave * kF8WaveStep;
-    const bool emit = kHist && with_hist && a.em_cap > 0;  // the host enables it only when stretches fit lkeys
+    // the host enables emission only when every stretch fits lkeys (checked here too)
+    const bool emit = kHist && with_hist && a.em_cap > 0 && n_load * kF8WgStep <= kEmitMax;
     const int stretch0 = s0 * kF8WgStep;
 
     auto load = [&](F8Raw &kr, int base) {  // unconditional, indices clamped into the visible rows
@@ -120,7 +122,7 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_fp8_kernel(S
 #pragma unroll
         for (int i = 0; i < 8; ++i) *(u32x4_t *)&kw[(8 * i + (lane >> 3)) * kF8RowWords + 4 * (lane & 7)] = kr.k[i];
         const int j = base + 16 * g + e;  // entry this lane stores
-        const float ks = kLdsScale ? lks[j < nvis ? j - stretch0 : 0] : kr.ks;
+        const float ks = kLdsScale ? lks[j < nvis ? min(j - stretch0, kEmitMax - 1) : 0] : kr.ks;
         load(kr, next);  // registers free again: the next loads go out before the math
         float mine = 0.f;
 #pragma unroll
@@ -169,6 +171,7 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_fp8_kernel(S
     int n_st = min(nvis, (s0 + n_load) * kF8WgStep) - stretch0;
     n_st = n_st > 0 ? n_st : 0;
     if (kLdsScale) {  // after the first key loads, so their latency covers these
+        n_st = n_st < kEmitMax ? n_st : kEmitMax;  // the host's bound on the stretch makes this a no-op
         // indices past the stretch are clamped to its last entry: those lanes
         // read and write that entry's own scale again (no branch around a store)
         constexpr int kNT = 64 * kScoreWaves, kU = 16;
@@ -194,25 +197,17 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_fp8_kernel(S
         }
     }
     const int all_steps = (a.n_max + kF8WgStep - 1) / kF8WgStep;
-    for (int st = vis_steps + blockIdx.x; st < all_steps; st += gridDim.x) {  // steps past the visible entries
+    for (int st = vis_steps + part; st < all_steps; st += n_parts) {  // steps past the visible entries
         const int j = st * kF8WgStep + wave * kF8WaveStep + 16 * g + e;
         if (j < a.n_max) srow[j] = -INFINITY;
     }
     if (with_hist) {
-        const size_t w = (size_t)qi * gridDim.x + blockIdx.x;
+        const size_t w = (size_t)qi * n_parts + part;
         hist_window_store_top(lh, hmax, a.win_hdr + w, a.win_cnt + w * kTopkWin, s_red);
-        if (emit) {  // hist_window_store_top's barrier also orders the key stores
-            emit_region<64 * kScoreWaves>(lh, lkeys, n_st, stretch0, a.em_cap, a.em_hdr + 2 * w,
-                                          a.em_key + w * a.em_cap, a.em_idx + w * a.em_cap, s_scan, &s_cut);
-        }
+        decode_emission<64 * kScoreWaves>(a, lh, lkeys, emit, nvis, s0, n_load, kF8WgStep, w, s_scan, &s_cut);
     }
 }
 
-int score_workgroups_fp8(int n_max, int n_queries) {
-    return decode_score_workgroups(n_max, n_queries, kF8WgStep);
-}
-
-int score_emit_cap_fp8(int n_max, int n_queries, int K) { return decode_emit_cap(n_max, n_queries, K, kF8WgStep); }
 
 template <int kAct, bool kHist>
 static void launch_fp8(const ScoreArgs &a, dim3 grid, dim3 block, bool lds_scale, hipStream_t stream) {
@@ -224,10 +219,10 @@ static void launch_fp8(const ScoreArgs &a, dim3 grid, dim3 block, bool lds_scale
 
 hipError_t launch_index_scores_fp8(const ScoreArgs &a, hipStream_t stream) {
     const int Q = a.B * a.T;
-    const int wgs = score_workgroups_fp8(a.n_max, Q);
+    const int wgs = decode_score_workgroups(a.n_max, Q, kF8WgStep);
     const dim3 grid(wgs, Q), block(64 * kScoreWaves);
-    const bool hist = a.win_hdr != nullptr;  // the caller sized the windows with score_workgroups_fp8
-    // every workgroup's stretch (at most ceil(steps / workgroups) steps) fits the LDS scale buffer
+    const bool hist = a.win_hdr != nullptr;  // the caller sized the windows with decode_geom
+    // every workgroup's stretch (at most ceil(steps / wgs) steps) fits the LDS scale buffer
     const int steps = (a.n_max + kF8WgStep - 1) / kF8WgStep;
     const bool lds_scale = (long)((steps + wgs - 1) / wgs) * kF8WgStep <= kEmitMax;
     if (a.act == 0) {

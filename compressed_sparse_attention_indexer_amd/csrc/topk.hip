@@ -42,7 +42,7 @@ template <int NT>
 struct TopkSharedT {
     uint32_t hist[256];
     uint64_t masks[2][NT / 64][2];
-    int bcast[2];
+    int bcast[4];
 };
 using TopkShared = TopkSharedT<kWG>;
 
@@ -474,15 +474,21 @@ constexpr int kListRounds = kTopkMaxSlots / kWG;  // rounds of kWG slots at most
 // key[r], idx[r]; slot order is index order, dead slots have key 0), given the
 // threshold bin: every live slot above it is taken, and of those inside it
 // ("candidates") the need = K - (above) largest keys, ties to the lower index.
-// Three radix levels over the candidates' low 20 key bits (8, 8 and 4 bits,
-// LDS histograms) give the exact K-th key t and how many slots equal to t are
-// taken; then one scan over the slots, counting per (round, wave) the slots
-// taken outright (above, or a candidate above t) and those equal to t, gives
-// each taken slot its output position: (taken outright before it) +
-// min(equal before it, equal taken).  Returns false (nothing written, the same
-// in every thread) if the counts are not those of a usable threshold.
+// A 256-bin histogram of the candidates' key bits 19..12 gives the sub-bin b2
+// holding the need-th candidate and how many of b2's members (need2) are
+// taken.  b2's members, when few (kSubFast at most), are gathered in LDS with
+// their slot numbers and each ranks itself among them ((key, lower slot)
+// order); otherwise two more radix levels (bits 11..4, 3..0) give the exact
+// K-th key t and how many slots equal to t are taken.  Then one scan over the
+// slots, counting per (round, wave) the slots taken outright and those equal
+// to t (none on the fast path), gives each taken slot its output position:
+// (taken outright before it) + min(equal before it, equal taken).  Returns
+// false (nothing written, the same in every thread) if the counts are not
+// those of a usable threshold.
+constexpr int kSubFast = 128;  // b2 members ranked pairwise at most
 __device__ bool select_slots(const uint32_t (&key)[kListRounds], const int32_t (&idx)[kListRounds], int rounds,
-                             uint32_t bin, int K, int32_t *out, TopkShared &sh, uint32_t *s_base, int *s_red) {
+                             uint32_t bin, int K, int32_t *out, TopkShared &sh, uint32_t *s_base, int *s_red,
+                             uint32_t *s_mkey, int *s_mslot) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     auto isum = [](int x) {
 #pragma unroll
@@ -491,7 +497,7 @@ __device__ bool select_slots(const uint32_t (&key)[kListRounds], const int32_t (
     };
     // level 1: candidates by key bits 19..12, and the count above the bin
     if (tid < 256) sh.hist[tid] = 0u;
-    if (tid < kWaves) s_red[tid] = 0;
+    if (tid == 0) sh.bcast[2] = 0;  // b2 members gathered
     __syncthreads();
     int n_above = 0;
 #pragma unroll
@@ -509,57 +515,104 @@ __device__ bool select_slots(const uint32_t (&key)[kListRounds], const int32_t (
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) na += s_red[w];
     const int need = K - na;
-    int nc = 0;  // candidates: the level-1 histogram's total
-    if (tid < 64) {
-        int c = 0;
+    if (tid < 64) {  // wave 0: the candidates' total, and the sub-bin of the need-th one (from the top)
+        uint32_t h[4], sum = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) c += (int)sh.hist[4 * tid + i];
-        c = isum(c);
-        if (tid == 0) sh.bcast[0] = c;
+        for (int i = 0; i < 4; ++i) {
+            h[i] = sh.hist[4 * lane + i];
+            sum += h[i];
+        }
+        uint32_t suf = sum;  // over lanes >= this lane
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t x = __shfl_down(suf, o);
+            if (lane + o < 64) suf += x;
+        }
+        const uint32_t total = __shfl(suf, 0);
+        if (lane == 0) sh.bcast[3] = (int)total;
+        if (need >= 1 && (uint32_t)need <= total) {
+            uint32_t above = suf - sum;
+#pragma unroll
+            for (int i = 3; i >= 0; --i) {
+                if (above < (uint32_t)need && (uint32_t)need <= above + h[i]) {
+                    sh.bcast[0] = 4 * lane + i;
+                    sh.bcast[1] = need - (int)above;
+                }
+                above += h[i];
+            }
+        }
     }
     __syncthreads();
-    nc = sh.bcast[0];
-    if (need < 1 || need > nc) return false;  // the same in every thread
-    __syncthreads();
-    find_bin_256(sh, need);
-    __syncthreads();
+    if (need < 1 || need > sh.bcast[3]) return false;  // the same in every thread
     const uint32_t b2 = (uint32_t)sh.bcast[0];
-    const int need2 = sh.bcast[1];
+    int need2 = sh.bcast[1];
     const uint32_t p2 = (bin << 8) | b2;  // key bits 31..12 of the deciding candidates
-    // level 2: bits 11..4 of the candidates with bits 31..12 = p2
-    __syncthreads();
-    if (tid < 256) sh.hist[tid] = 0u;
-    __syncthreads();
+    // gather b2's members (key, slot) while few
 #pragma unroll
-    for (int r = 0; r < kListRounds; ++r)
-        if (r < rounds && key[r] != 0u && (key[r] >> 12) == p2) atomicAdd(&sh.hist[(key[r] >> 4) & 0xFFu], 1u);
+    for (int r = 0; r < kListRounds; ++r) {
+        if (r < rounds && key[r] != 0u && (key[r] >> 12) == p2) {
+            const int at = atomicAdd(&sh.bcast[2], 1);
+            if (at < kSubFast) {
+                s_mkey[at] = key[r];
+                s_mslot[at] = r * kWG + tid;
+            }
+        }
+    }
     __syncthreads();
-    find_bin_256(sh, need2);
-    __syncthreads();
-    const uint32_t b3 = (uint32_t)sh.bcast[0];
-    const int need3 = sh.bcast[1];
-    const uint32_t p3 = (p2 << 8) | b3;  // key bits 31..4
-    // level 3: bits 3..0
-    __syncthreads();
-    if (tid < 256) sh.hist[tid] = 0u;
-    __syncthreads();
+    const int m2 = sh.bcast[2];
+    uint32_t t = 0u;       // the K-th key (slow path)
+    int n_eq_take = 0;     // slots equal to t taken (slow path)
+    uint32_t taken2 = 0u;  // bit r: slot r * kWG + tid is a b2 member that is taken (fast path)
+    if (m2 <= kSubFast) {
 #pragma unroll
-    for (int r = 0; r < kListRounds; ++r)
-        if (r < rounds && key[r] != 0u && (key[r] >> 4) == p3) atomicAdd(&sh.hist[key[r] & 0xFu], 1u);
-    __syncthreads();
-    find_bin_256(sh, need3);
-    __syncthreads();
-    const uint32_t t = (p3 << 4) | (uint32_t)sh.bcast[0];  // the K-th key
-    const int n_eq_take = sh.bcast[1];                     // slots equal to t that are taken
+        for (int r = 0; r < kListRounds; ++r) {
+            if (r < rounds && key[r] != 0u && (key[r] >> 12) == p2) {
+                const uint64_t mine = (uint64_t)key[r] << 32 | (uint32_t)~(uint32_t)(r * kWG + tid);
+                int better = 0;
+                for (int u = 0; u < m2; ++u)
+                    better += ((uint64_t)s_mkey[u] << 32 | (uint32_t)~(uint32_t)s_mslot[u]) > mine;
+                taken2 |= (uint32_t)(better < need2) << r;
+            }
+        }
+        t = 0xFFFFFFFFu;  // no slot is "equal to t" on this path
+    } else {
+        // level 2: bits 11..4 of the candidates with bits 31..12 = p2
+        if (tid < 256) sh.hist[tid] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < kListRounds; ++r)
+            if (r < rounds && key[r] != 0u && (key[r] >> 12) == p2) atomicAdd(&sh.hist[(key[r] >> 4) & 0xFFu], 1u);
+        __syncthreads();
+        find_bin_256(sh, need2);
+        __syncthreads();
+        const uint32_t b3 = (uint32_t)sh.bcast[0];
+        const int need3 = sh.bcast[1];
+        const uint32_t p3 = (p2 << 8) | b3;  // key bits 31..4
+        // level 3: bits 3..0
+        __syncthreads();
+        if (tid < 256) sh.hist[tid] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < kListRounds; ++r)
+            if (r < rounds && key[r] != 0u && (key[r] >> 4) == p3) atomicAdd(&sh.hist[key[r] & 0xFu], 1u);
+        __syncthreads();
+        find_bin_256(sh, need3);
+        __syncthreads();
+        t = (p3 << 4) | (uint32_t)sh.bcast[0];
+        n_eq_take = sh.bcast[1];
+    }
+    const bool fast = m2 <= kSubFast;
     // per (round, wave): slots taken outright | slots equal to t << 16
     uint64_t m_def[kListRounds], m_eq[kListRounds];
 #pragma unroll
     for (int r = 0; r < kListRounds; ++r) {
         if (r < rounds) {
             const uint32_t k = key[r];
-            const bool live = k != 0u;
-            m_def[r] = __ballot(live && ((k >> 20) > bin || ((k >> 20) == bin && k > t)));
-            m_eq[r] = __ballot(live && k == t);
+            const bool live = k != 0u, cand = live && (k >> 20) == bin;
+            const bool def = live && ((k >> 20) > bin ||
+                                      (cand && (fast ? (((k >> 12) & 0xFFu) > b2 || ((taken2 >> r) & 1u)) : k > t)));
+            m_def[r] = __ballot(def);
+            m_eq[r] = __ballot(!fast && live && k == t);
             if (lane == 0) s_base[r * kWaves + wave] = (uint32_t)__popcll(m_def[r]) | (uint32_t)__popcll(m_eq[r]) << 16;
         }
     }
@@ -640,7 +693,7 @@ __global__ __launch_bounds__(kWG) void topk_lists_kernel(TopkArgs a) {
     const uint32_t bin = window_threshold(a.win_hdr + q0, a.win_cnt + q0 * kTopkWin, R, K, s_red, s_hist);
     // every region emitted all of its entries at or above the threshold bin?
     bool ok = bin != kNoBin && !__syncthreads_or(tid < R && ((uint32_t)cut > bin || cnt > cap));
-    if (ok) ok = select_slots(key, idx, rounds, bin, K, out, sh, s_base, s_red);
+    if (ok) ok = select_slots(key, idx, rounds, bin, K, out, sh, s_base, s_red, sc.c_key, sc.c_idx);
     if (!ok && bin != kNoBin) {  // lists not usable: scan the row with the threshold
         __syncthreads();
         const bool vec = (a.n_max & 3) == 0 && ((uintptr_t)a.scores & 15) == 0;

@@ -25,6 +25,12 @@ import compressed_sparse_attention_indexer_amd as csa  # noqa: E402
 from compressed_sparse_attention_indexer_amd.staging import DeviceCase  # noqa: E402
 
 
+# a ragged batch of 12: long and short sequences, one with fewer visible
+# entries than K, one with none (the scorer's balanced split over the queries)
+RAGGED_12 = [4 * 30000 + 1, 4 * 2000, 4 * 90 + 3, 50, 4 * 12000 + 2, 4 * 64000, 4 * 700 + 1, 4 * 5000 + 3,
+             4 * 40000, 4 * 1500 + 2, 4 * 300, 4 * 20000 + 1]
+
+
 def _np(t):
     torch.cuda.synchronize()
     return t.detach().cpu().numpy()
@@ -130,6 +136,14 @@ def test_value_rows_near_the_fp16_bound(sharp):
         case.q = inputs.bf16_bits(inputs.bf16_to_f32(case.q) * np.float32(60.0))
     dc = check_whole_step(case, ATT_TOL_BF16)
     del dc
+
+
+def test_ragged_batch_whole_step():
+    """Twelve sequences of very different lengths (one with fewer visible entries
+    than K, one with none): the scorer's workgroups are dealt to the queries in
+    proportion to their entries."""
+    wl, sl = flash_case("flash_ragged12", RAGGED_12)
+    check_whole_step(make_case_with_lens(wl, sl), ATT_TOL_BF16)
 
 
 def test_flash_no_activation():
@@ -597,6 +611,11 @@ def check_fp8_step(case, act=csa.CSA_ACT_RELU, fp8=None):
 ])
 def test_fp8_step_small(lens, T, q_pos0):
     wl, sl = flash_case(f"fp8_step_{T}_{lens[0]}", lens, q_len=T, q_pos0=q_pos0)
+    check_fp8_step(make_case_with_lens(wl, sl))
+
+
+def test_fp8_step_ragged_batch():
+    wl, sl = flash_case("fp8_step_ragged12", RAGGED_12)
     check_fp8_step(make_case_with_lens(wl, sl))
 
 
