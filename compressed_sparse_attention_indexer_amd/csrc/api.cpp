@@ -129,10 +129,12 @@ int win_count(const csa_dims *d, bool fused, bool fp8 = false) {
     if (!fused_decode(d, fp8)) return csa::tiled_windows(d->batch, d->q_len, d->max_entries);
     return decode_geom(d, fp8).n_win;
 }
-// Entries per decode-scorer region handed to the selection in the fused call
-// (0: the selection scans the scores itself).
+// Entries per scorer region (a decode-scorer workgroup, or a (query, entry
+// chunk) of the tiled scorer) handed to the selection in the fused call (0: the
+// selection scans the scores itself).
 int emit_cap(const csa_dims *d, bool fused, bool fp8 = false) {
-    if (!fused || !fused_decode(d, fp8) || !csa::topk_uses_histogram(d->max_entries)) return 0;
+    if (!fused || d->dtype != CSA_BF16 || !csa::topk_uses_histogram(d->max_entries)) return 0;
+    if (!fused_decode(d, fp8)) return csa::tiled_emit_cap(d->batch, d->q_len, d->max_entries, d->topk);
     return decode_geom(d, fp8).em_cap;
 }
 size_t ws_topk(const csa_dims *d, bool fused = false, bool fp8 = false) {
@@ -199,6 +201,8 @@ csa::TopkArgs topk_args(const csa_dims *d, const float *scores, const int32_t *s
     a.K = d->topk;
     a.n_max = d->max_entries;
     csa::topk_carve(a, ws, n_queries(d), win_count(d, fused, fp8), emit_cap(d, fused, fp8));
+    // after the tiled scorer the top-k emits the regions itself, one per entry chunk
+    if (a.em_cap > 0 && !fused_decode(d, fp8)) a.em_chunk = csa::tiled_chunk_entries(d->batch, d->q_len, d->max_entries);
     return a;
 }
 

@@ -49,6 +49,10 @@ DecodeGeom decode_geom(bool fp8, int n_max, int n_queries, int K);
 bool score_uses_tiles(int dtype, int T);
 // histogram windows per query the tiled scorer can write (its entry chunks), 0 if it cannot
 int tiled_windows(int B, int T, int n_max);
+// entries per (query, chunk) region handed to the selection after the tiled scorer, 0 if it cannot
+int tiled_emit_cap(int B, int T, int n_max, int K);
+// entries per chunk of the tiled scorer (its histogram windows' spans)
+int tiled_chunk_entries(int B, int T, int n_max);
 
 constexpr int kTopkSmallMax = 4096;       // rows up to this length: one workgroup, row kept in LDS
 constexpr int kTopkOneKernelMax = 65536;  // rows up to this length: threshold+scan+select in one kernel
@@ -77,8 +81,10 @@ struct TopkArgs {
     uint32_t *win_cnt;          // [Q, n_win, kTopkWin]
     uint32_t *bin;              // [Q] threshold bin (long rows)
     uint32_t *flt;              // [Q, n_flt, kFltRegionWords] per-filter-workgroup lists (long rows)
-    // the scorer's emitted entries, one region per window (em_cap 0: not used)
-    int em_cap;
+    // the scorer's emitted entries, one region per window (em_cap 0: not used);
+    // em_chunk > 0: the top-k emits the regions itself, one per window of
+    // em_chunk entries, from the scores (after the tiled scorer)
+    int em_cap, em_chunk;
     int32_t *em_hdr;            // [Q, n_win, 2]
     uint32_t *em_key;           // [Q, n_win, em_cap]
     int32_t *em_idx;            // [Q, n_win, em_cap]

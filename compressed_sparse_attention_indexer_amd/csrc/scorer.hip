@@ -542,6 +542,16 @@ int tiled_windows(int B, int T, int n_max) {
     return tiled_plan(a).n_chunks;
 }
 
+int tiled_chunk_entries(int B, int T, int n_max) {
+    ScoreArgs a{};
+    a.B = B;
+    a.T = T;
+    a.n_max = n_max;
+    return tiled_plan(a).tiles_per_chunk * kPfTile;
+}
+
+int tiled_emit_cap(int B, int T, int n_max, int K) { return decode_region_cap(tiled_windows(B, T, n_max), K); }
+
 int score_workgroups(int n_max, int n_queries) { return decode_score_workgroups(n_max, n_queries, kWgStep); }
 
 DecodeGeom decode_geom(bool fp8, int n_max, int n_queries, int K) {

@@ -456,6 +456,78 @@ __global__ __launch_bounds__(kWG) void topk_onekernel_kernel(TopkArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Regions for the selection after the tiled (many-query) scorer, which builds
+// the histogram windows but cannot keep a chunk's keys: workgroup (chunk c,
+// query) re-reads the chunk's visible scores and emits, in index order, those
+// at or above the lowest bin of its window whose count from the top fits the
+// region (em_cap entries), as the decode scorer emits from LDS.  A window
+// whose top bin alone does not fit gets cut = top + 1 and nothing emitted
+// (the selection then scans the row).  Consecutive threads take consecutive
+// 8-entry runs (one 32-byte load each when the row allows), an ordered
+// compaction per round.
+__global__ __launch_bounds__(kAuxThreads) void topk_emit_kernel(TopkArgs a) {
+    constexpr int kE = 8;
+    __shared__ int s_wave[kAuxThreads / 64];
+    __shared__ int s_cut;
+    const int qi = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
+    const int n = query_visible(a, qi);
+    if (n <= a.K) return;  // the selection returns before reading regions for these
+    const size_t w = (size_t)qi * a.n_win + c;
+    const int cap = a.em_cap;
+    if (tid < 64) {
+        const int m_top = a.win_hdr[w];
+        const uint32_t cnt = tid < kTopkWin ? a.win_cnt[w * kTopkWin + tid] : 0u;  // bin m_top - 31 + tid
+        uint32_t suf = cnt;
+#pragma unroll
+        for (int o = 1; o < kTopkWin; o <<= 1) {
+            const uint32_t x = __shfl_down(suf, o);
+            if (tid + o < kTopkWin) suf += x;
+        }
+        const uint64_t fits = __ballot(tid < kTopkWin && suf <= (uint32_t)cap);
+        if (tid == 0)
+            s_cut = m_top < 0 ? 0 : (fits ? m_top - (kTopkWin - 1) + __builtin_ctzll(fits) : m_top + 1);
+    }
+    __syncthreads();
+    const int cut = s_cut;
+    const float *row = a.scores + (size_t)qi * a.n_max;
+    uint32_t *okey = a.em_key + w * cap;
+    int32_t *oidx = a.em_idx + w * cap;
+    const int j0 = c * a.em_chunk, j1 = min(j0 + a.em_chunk, n);
+    const bool vec = (a.n_max & 3) == 0 && ((uintptr_t)a.scores & 15) == 0;
+    int written = 0;
+    for (int i0 = j0; i0 < j1; i0 += kAuxThreads * kE) {
+        float x[kE];
+        load_chunk<kE>(row, i0 + kE * tid, j1, a.n_max, vec, x);
+        uint32_t k[kE];
+        int m = 0;
+#pragma unroll
+        for (int e = 0; e < kE; ++e) {
+            k[e] = order_key(x[e]);
+            m += i0 + kE * tid + e < j1 && (int)(k[e] >> 20) >= cut;
+        }
+        int rt;
+        int pos = written + block_scan_excl<kAuxThreads>(m, s_wave, &rt);
+#pragma unroll
+        for (int e = 0; e < kE; ++e) {
+            const int j = i0 + kE * tid + e;
+            if (j < j1 && (int)(k[e] >> 20) >= cut) {
+                if (pos < cap) {
+                    okey[pos] = k[e];
+                    oidx[pos] = j;
+                }
+                ++pos;
+            }
+        }
+        written += rt;
+    }
+    for (int i = written + tid; i < cap; i += kAuxThreads) okey[i] = 0u;
+    if (tid == 0) {
+        a.em_hdr[2 * w] = cut;
+        a.em_hdr[2 * w + 1] = written;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Selection from the entries the decode scorer emitted (fused decode path).
 // Per query, in one load round: the histogram windows (which give the
 // threshold bin), each region's header (cut bin, count) and every emitted slot
@@ -951,7 +1023,8 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t stream, bool hist_done) {
         hipLaunchKernelGGL(topk_lds_kernel, dim3(Q), dim3(kWG), 0, stream, a);
         return hipGetLastError();
     }
-    if (a.em_cap > 0) {  // the scorer wrote the windows and its emitted entries
+    if (a.em_cap > 0) {  // the scorer wrote the windows and (or, em_chunk > 0, the top-k now) the regions
+        if (a.em_chunk > 0) hipLaunchKernelGGL(topk_emit_kernel, dim3(a.n_win, Q), dim3(kAuxThreads), 0, stream, a);
         hipLaunchKernelGGL(topk_lists_kernel, dim3(Q), dim3(kWG), 0, stream, a);
         return hipGetLastError();
     }
