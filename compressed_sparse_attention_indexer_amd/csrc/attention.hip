@@ -377,16 +377,33 @@ __global__ __launch_bounds__(128 * HG, 2) void mqa_bf16_kernel(MqaArgs a) {
         // [qi, split, head group, dh, dt pair p, lane] (head group = the
         // query's 16-head group h_off / 16 + hg, whatever HG is) holds heads
         // 16hg + 4g + r (r = 0..3) at dims 256dh + 16dt + e for dt = 2p and 2p + 1.
+        // Each head's 256 values of this dim half are scaled by a power of two
+        // that brings their largest magnitude into [2^14, 2^15), and the
+        // inverse kept next to (m, l): any finite bf16 value range fits fp16's
+        // 16 significant bits without overflow or subnormal loss.
         const size_t ps = (size_t)qi * a.n_splits + split;
         if (dh == 0 && g == 0) {
-            a.part_ml[(ps * a.H + h_off + 16 * hg + e) * 2 + 0] = m_run;
-            a.part_ml[(ps * a.H + h_off + 16 * hg + e) * 2 + 1] = l_run;
+            a.part_ml[(ps * a.H + h_off + 16 * hg + e) * 4 + 0] = m_run;
+            a.part_ml[(ps * a.H + h_off + 16 * hg + e) * 4 + 1] = l_run;
         }
         if (ntiles > 0) {
             const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
             float ir[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) ir[r] = __shfl(inv, 4 * g + r);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {  // head 16hg + 4g + r: largest |O/l| over its 256 dims here
+                float mx = 0.f;
+#pragma unroll
+                for (int dt = 0; dt < 16; ++dt) mx = fmaxf(mx, fabsf(o[dt][r]));
+                mx = row16_max(mx) * ir[r];  // over the 16 lanes e
+                // 2^k with k = 14 - floor(log2(mx)) (mx = f 2^x with f in [0.5, 1)),
+                // kept within fp32's normal range
+                int k = mx > 0.f ? 15 - __builtin_amdgcn_frexp_expf(mx) : 0;
+                k = k < -100 ? -100 : (k > 100 ? 100 : k);
+                ir[r] *= ldexpf(1.f, k);
+                if (e == 0) a.part_ml[(ps * a.H + h_off + 16 * hg + 4 * g + r) * 4 + 2 + dh] = ldexpf(1.f, -k);
+            }
             u32x4_t *dst = (u32x4_t *)a.part_o + ((ps * gridDim.z + blockIdx.z) * NW + wave) * 8 * 64 + lane;
 #pragma unroll
             for (int p = 0; p < 8; ++p) {
@@ -424,7 +441,7 @@ constexpr int kCombineMaxSplits = 1024;
 template <int Zq>
 __global__ __launch_bounds__(256) void mqa_combine_kernel(MqaArgs a) {
     constexpr int kBatch = 16;
-    __shared__ float s_w[kCombineMaxSplits][4];
+    __shared__ float s_w[kCombineMaxSplits][4][2];  // split weight times the partial's scale, per dim half
     __shared__ float s_M[4], s_L[4];
     __shared__ float s_acc[1792];  // (Zq - 1) groups x 8 sums x 256 / Zq positions
     const int qi = blockIdx.y, dq = blockIdx.z;
@@ -455,25 +472,27 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(MqaArgs a) {
     if (n_mine > 0) load_batch(ov[0], 0);
     {  // weights of head h0 + wv; the first 64 splits' (m, l) pairs stay in registers
         const float sink2 = a.sink[h0 + wv] * kLog2e;
-        float2 ml0 = float2{0.f, 0.f};
-        if (ln < S) ml0 = *(const float2 *)(a.part_ml + (((size_t)qi * S + ln) * a.H + h0 + wv) * 2);
+        float4 ml0 = float4{0.f, 0.f, 0.f, 0.f};  // m, l, inverse scales of the two dim halves
+        if (ln < S) ml0 = *(const float4 *)(a.part_ml + (((size_t)qi * S + ln) * a.H + h0 + wv) * 4);
         float M = ml0.y > 0.f ? fmaxf(sink2, ml0.x) : sink2;
         for (int s = ln + 64; s < S; s += 64) {
-            const float *ml = a.part_ml + (((size_t)qi * S + s) * a.H + h0 + wv) * 2;
+            const float *ml = a.part_ml + (((size_t)qi * S + s) * a.H + h0 + wv) * 4;
             if (ml[1] > 0.f) M = fmaxf(M, ml[0]);
         }
         M = wave_max(M);
         float L = 0.f;
         if (ln < S) {
             const float w = ml0.y > 0.f ? ml0.y * exp2f(ml0.x - M) : 0.f;
-            s_w[ln][wv] = w;
+            s_w[ln][wv][0] = w > 0.f ? w * ml0.z : 0.f;  // a split without rows never wrote its scales
+            s_w[ln][wv][1] = w > 0.f ? w * ml0.w : 0.f;
             L += w;
         }
         for (int s = ln + 64; s < S; s += 64) {
-            const float *ml = a.part_ml + (((size_t)qi * S + s) * a.H + h0 + wv) * 2;
+            const float *ml = a.part_ml + (((size_t)qi * S + s) * a.H + h0 + wv) * 4;
             const float l = ml[1];
             const float w = l > 0.f ? l * exp2f(ml[0] - M) : 0.f;
-            s_w[s][wv] = w;
+            s_w[s][wv][0] = w > 0.f ? w * ml[2] : 0.f;
+            s_w[s][wv][1] = w > 0.f ? w * ml[3] : 0.f;
             L += w;
         }
         L = wave_sum(L);
@@ -491,7 +510,7 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(MqaArgs a) {
             const int s = sg + Zq * (i0 + u);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float w = s_w[s][r];
+                const float w = s_w[s][r][dh];
                 if (w == 0.f) continue;  // also keeps unwritten partials out
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {  // dt = 2p + kk: word 2kk + r/2, half r%2
@@ -556,7 +575,7 @@ size_t mqa_workspace_bytes(int dtype, int n_queries, int H, int D, int max_rows)
     mqa_plan(n_queries, max_rows, &s, &tiles);
     if (s == 1) return 0;
     const size_t n = (size_t)n_queries * s * H;
-    return n * D * 2 + n * 2 * 4 + 256;
+    return n * D * 2 + n * 4 * 4 + 256;
 }
 
 void mqa_carve(MqaArgs &a, void *ws, int n_queries) {

@@ -82,6 +82,18 @@ __device__ __forceinline__ float max_xor32(float v) {
     return fmaxf(p.lo, p.hi);
 }
 
+// Largest of v over the 16 lanes of each DPP row (lanes 16k .. 16k + 15), in
+// every lane of the row: quad_perm [1,0,3,2] and [2,3,0,1] give each quad's
+// maximum, row_half_mirror (lane i of 8 reads lane 7 - i) joins the two quads
+// of a half row, row_mirror (lane i of 16 reads lane 15 - i) the two halves.
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));
+    return v;
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));

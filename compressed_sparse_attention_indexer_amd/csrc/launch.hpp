@@ -113,7 +113,7 @@ struct MqaArgs {
     float *out;                     // [Q, H, D]
     float *lse;                     // [Q, H] or null
     void *part_o;                   // [Q, S, 8, 8, 64] 16-byte fp16 vectors: split partials O / l
-    float *part_ml;                 // [Q, S, H, 2]
+    float *part_ml;                 // [Q, S, H, 4]: m, l, inverse scales of the two dim halves' O / l
     int B, T, H, D, K, W, ratio;
     int n_splits, n_tiles;          // splits per query; kTile-row tiles of the longest row list
     float scale;                    // softmax scale (natural units)

@@ -117,33 +117,49 @@ def test_separate_value_rows(lens, T, q_pos0):
     check_whole_step(make_case_with_lens(dataclasses.replace(wl, separate_v=True), sl), ATT_TOL_BF16)
 
 
-@pytest.mark.parametrize("sharp", [False, True])
-def test_value_rows_near_the_fp16_bound(sharp):
-    """Split partials O/l are kept in fp16, which holds |O/l| <= max |v| while
-    max |v| < 65504.  Value rows scaled so that max |v| is about 60,000 (and,
-    with sharp logits, single rows dominating so that O/l reaches such values):
-    still within the bf16 attention tolerance of the oracle."""
+@pytest.mark.parametrize("vmax,sharp", [(6e4, False), (6e4, True), (1e6, False), (1e-6, False), (1e-6, True)])
+def test_value_rows_across_the_range(vmax, sharp):
+    """Split partials O/l are kept in fp16, each head's values of a dim half
+    scaled by a power of two into [2^14, 2^15).  Value rows scaled so that
+    max |v| is about 6e4 (near fp16's largest), 1e6 (past it) and 1e-6 (where
+    unscaled fp16 would be subnormal), with sharp logits too (single rows
+    dominating, so that O/l reaches those values): still within the bf16
+    attention tolerance of the oracle."""
     import dataclasses
-    wl, sl = flash_case(f"flash_vbound_{int(sharp)}", [4 * 9000 + 1, 4 * 3000 + 2])
+    wl, sl = flash_case(f"flash_vrange_{vmax:g}_{int(sharp)}", [4 * 9000 + 1, 4 * 3000 + 2])
     case = make_case_with_lens(dataclasses.replace(wl, separate_v=True), sl)
-    vmax = max(float(np.max(np.abs(inputs.bf16_to_f32(x)))) for x in case.v + case.win_v)
-    s = np.float32(60000.0 / vmax)
+    cur = max(float(np.max(np.abs(inputs.bf16_to_f32(x)))) for x in case.v + case.win_v)
+    s = np.float32(vmax / cur)
     case.v = [inputs.bf16_bits(inputs.bf16_to_f32(x) * s) for x in case.v]
     case.win_v = [inputs.bf16_bits(inputs.bf16_to_f32(x) * s) for x in case.win_v]
-    vmax = max(float(np.max(np.abs(inputs.bf16_to_f32(x)))) for x in case.v + case.win_v)
-    assert 55000 < vmax < 65504
+    got = max(float(np.max(np.abs(inputs.bf16_to_f32(x)))) for x in case.v + case.win_v)
+    assert 0.9 * vmax < got < 1.1 * vmax
     if sharp:
         case.q = inputs.bf16_bits(inputs.bf16_to_f32(case.q) * np.float32(60.0))
-    dc = check_whole_step(case, ATT_TOL_BF16)
-    del dc
+    check_whole_step(case, ATT_TOL_BF16)
 
 
-def test_ragged_batch_whole_step():
-    """Twelve sequences of very different lengths (one with fewer visible entries
-    than K, one with none): the scorer's workgroups are dealt to the queries in
-    proportion to their entries."""
-    wl, sl = flash_case("flash_ragged12", RAGGED_12)
-    check_whole_step(make_case_with_lens(wl, sl), ATT_TOL_BF16)
+@pytest.mark.parametrize("sharp", [False, True])
+def test_value_rows_with_two_large_dims(sharp):
+    """One dim in each half of the value rows eight times larger than the
+    others (up to about 6e4, near fp16's largest value): the power of two of a
+    head's dim half must come from the largest magnitude over all of its 256
+    dims (one taken from part of them overflows the large dim, or leaves lanes
+    of one head with different scales).  The ratio is kept at 8: the fp16
+    partials round each value to 2^-11 of its head's largest, which against a
+    bound of 1e-2 times the output's RMS allows a largest-to-RMS ratio of
+    about 20, not a few dims carrying all of the output."""
+    import dataclasses
+    wl, sl = flash_case(f"flash_vdims_{int(sharp)}", [4 * 9000 + 1, 4 * 3000 + 2])
+    case = make_case_with_lens(dataclasses.replace(wl, separate_v=True), sl)
+    cur = max(float(np.max(np.abs(inputs.bf16_to_f32(x)))) for x in case.v + case.win_v)
+    col = np.full(wl.head_dim, np.float32(6e4 / 8 / cur), dtype=np.float32)
+    col[37] = col[300] = np.float32(6e4 / cur)
+    case.v = [inputs.bf16_bits(inputs.bf16_to_f32(x) * col) for x in case.v]
+    case.win_v = [inputs.bf16_bits(inputs.bf16_to_f32(x) * col) for x in case.win_v]
+    if sharp:
+        case.q = inputs.bf16_bits(inputs.bf16_to_f32(case.q) * np.float32(60.0))
+    check_whole_step(case, ATT_TOL_BF16)
 
 
 def test_flash_no_activation():
