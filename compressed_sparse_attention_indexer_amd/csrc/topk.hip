@@ -758,11 +758,15 @@ __global__ __launch_bounds__(kWG) void topk_lists_kernel(TopkArgs a) {
         cnt = a.em_hdr[2 * (q0 + tid) + 1];
     }
     const int n = query_visible(a, qi);
+    // The windows are merged before the visible count is looked at, so their
+    // loads go out in the same round as the slots and the count (a query with
+    // no more than K visible entries wrote no windows and ignores the merge;
+    // the reads stay inside the window arrays either way).
+    const uint32_t bin = window_threshold(a.win_hdr + q0, a.win_cnt + q0 * kTopkWin, R, K, s_red, s_hist);
     if (n <= K) {
         for (int i = tid; i < K; i += kWG) out[i] = i < n ? i : -1;
         return;
     }
-    const uint32_t bin = window_threshold(a.win_hdr + q0, a.win_cnt + q0 * kTopkWin, R, K, s_red, s_hist);
     // every region emitted all of its entries at or above the threshold bin?
     bool ok = bin != kNoBin && !__syncthreads_or(tid < R && ((uint32_t)cut > bin || cnt > cap));
     if (ok) ok = select_slots(key, idx, rounds, bin, K, out, sh, s_base, s_red, sc.c_key, sc.c_idx);
