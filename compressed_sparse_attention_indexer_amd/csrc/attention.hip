@@ -173,6 +173,9 @@ constexpr int kD = 512;
 constexpr int kTile = 32;
 constexpr int kKrowStride = kD + 16;  // bf16 elements per staged row (1056 B: HCA 26.3 -> 25.8 us against 1040 B)
 constexpr float kLazyMax = 8.f;       // log2 headroom of the running softmax reference
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef short v8i16_t __attribute__((ext_vector_type(8)));
 
@@ -283,15 +286,28 @@ __global__ __launch_bounds__(128 * HG, 2) void mqa_bf16_kernel(MqaArgs a) {
         }
         __syncthreads();
 
-        // QK over this wave's 256 dims.
+        // QK over this wave's 256 dims: the two row tiles' chains interleaved,
+        // the fragment reads kept eight ahead of the MFMAs (left to itself the
+        // scheduler let each MFMA wait out the latency of the read just before it)
         f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+        bf16x8_t kf[8][2];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                const bf16x8_t kf = *(const bf16x8_t *)&krow[(16 * mt + e) * kKrowStride + 256 * dh + 32 * ks + 8 * g];
-                sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sacc[mt], 0, 0, 0);
-            }
+            for (int mt = 0; mt < 2; ++mt)
+                kf[ks][mt] = *(const bf16x8_t *)&krow[(16 * mt + e) * kKrowStride + 256 * dh + 32 * ks + 8 * g];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+                sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks][mt], qf[ks], sacc[mt], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 8, 0);
 #pragma unroll
         for (int v = 0; v < 8; ++v) xs[wave][v][lane] = sacc[v >> 2][v & 3];
         __syncthreads();
@@ -342,17 +358,32 @@ __global__ __launch_bounds__(128 * HG, 2) void mqa_bf16_kernel(MqaArgs a) {
         }
         const uint16_t *vrow = kSepV ? vrow_sep : krow;
         const int s16 = lane & 15;  // this lane's address role in the transposing read
-        // PV over this wave's 256 output dims.
+        // PV over this wave's 256 output dims, two dt at a time so consecutive
+        // MFMAs are independent (each accumulator still takes its high part
+        // before its remainder); the transposing reads kept eight ahead.
+        bf16x8_t vf[16];
 #pragma unroll
         for (int dt = 0; dt < 16; ++dt) {
             // B fragment: V[rows 4g .. 4g+3 and 16+4g .. 16+4g+3][d = 256dh + 16dt + e]
             const uint16_t *vp0 = vrow + (4 * g + (s16 >> 2)) * kKrowStride + 256 * dh + 16 * dt + 4 * (s16 & 3);
             const v4i16_t lo = lds_read_tr16(vp0);
             const v4i16_t hi = lds_read_tr16(vp0 + 16 * kKrowStride);
-            const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vf, o[dt], 0, 0, 0);
-            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vf, o[dt], 0, 0, 0);
+            vf[dt] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
+#pragma unroll
+        for (int dt = 0; dt < 16; dt += 2) {
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vf[dt], o[dt], 0, 0, 0);
+            o[dt + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vf[dt + 1], o[dt + 1], 0, 0, 0);
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vf[dt], o[dt], 0, 0, 0);
+            o[dt + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vf[dt + 1], o[dt + 1], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+#pragma unroll
+        for (int i = 0; i < 12; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 8, 0);
     }
 
     // epilogue: C layout holds O[head 16hg + 4g + r][d = 256dh + 16dt + e]
