@@ -189,6 +189,8 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(
             p = sum_xor32(p);
             part[et] = p;
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the fragment reads first
+        __builtin_amdgcn_sched_group_barrier(0x008, 32, 0); // then the MFMAs
         // Lanes of group g < 2 store column tile g: 32 consecutive scores.
         const float sv = j < nvis ? (g == 0 ? part[0] : part[1]) : -INFINITY;
         if (live && g < 2 && j < a.n_max) srow[j] = sv;

@@ -125,12 +125,19 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_fp8_kernel(S
         const float ks = kLdsScale ? lks[j < nvis ? min(j - stretch0, kEmitMax - 1) : 0] : kr.ks;
         load(kr, next);  // registers free again: the next loads go out before the math
         float mine = 0.f;
+        // all four column tiles' fragments read before the MFMAs (read per
+        // tile, each tile's MFMAs waited out its reads' latency)
+        i32x8_t kfs[4];
 #pragma unroll
         for (int et = 0; et < 4; ++et) {
             const u32x4_t klo = *(const u32x4_t *)&kw[(16 * et + e) * kF8RowWords + 8 * g];
             const u32x4_t khi = *(const u32x4_t *)&kw[(16 * et + e) * kF8RowWords + 8 * g + 4];
-            const i32x8_t kf = i32x8_t{(int)klo[0], (int)klo[1], (int)klo[2], (int)klo[3],
-                                       (int)khi[0], (int)khi[1], (int)khi[2], (int)khi[3]};
+            kfs[et] = i32x8_t{(int)klo[0], (int)klo[1], (int)klo[2], (int)klo[3],
+                              (int)khi[0], (int)khi[1], (int)khi[2], (int)khi[3]};
+        }
+#pragma unroll
+        for (int et = 0; et < 4; ++et) {
+            const i32x8_t kf = kfs[et];
             // operand formats 0, 0: E4M3 x E4M3; scale operands 0: no block scaling
             const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
             f32x4_t acc[4];
@@ -146,6 +153,8 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_fp8_kernel(S
             p = sum_xor32(p);
             if (g == et) mine = p;  // lane group g keeps column tile g
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, kLdsScale ? 9 : 8, 0);  // LDS reads (the scale's too)
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);                 // then the MFMAs
         const float sv = j < nvis ? ks * mine : -INFINITY;
         if (live && j < a.n_max) srow[j] = sv;
         if (with_hist) {
