@@ -253,13 +253,14 @@ def bench_csa(torch, csa, case, args, detail, min_samples=None):
     if detail:
         # Each entry point alone, 20 launches per graph (copies rotated), so that
         # the per-launch figure is the kernel time plus the gap between dependent
-        # kernels, and the replay's own launch cost is spread thin.
+        # kernels, and the replay's own launch cost is spread thin; three replays
+        # of warm-up (the first replays of a new graph read high), ten timed.
         per = {}
         gk = max(gs, 20)
         for name, fn in (("index_scores", r.scores_call), ("topk_select", r.topk_call),
                          ("sparse_mqa", r.attn_call)):
             g = capture(torch, fn, gk)
-            per[name] = time_graph(torch, g, gk, max(args.steps, 5 * gk), args.warmup)["ms"]
+            per[name] = time_graph(torch, g, gk, max(args.steps, 10 * gk), max(args.warmup, 3 * gk))["ms"]
         g_s = capture(torch, r.step, gs)
         res["separate_entry_points_ms"] = time_graph(torch, g_s, gs, args.steps, args.warmup)["ms"]
         res["kernel_ms"] = per
