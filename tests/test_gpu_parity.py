@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 from compressed_sparse_attention_indexer_amd import inputs
-from tests.gpu_helpers import (ATT_TOL_BF16, ATT_TOL_F32, assert_attention_close, assert_scores_close,
+from tests.gpu_helpers import (ATT_TOL_BF16, ATT_TOL_F32, SCORE_TOL, assert_attention_close, assert_scores_close,
                                assert_topk_band, check_topk_valid, flash_case, make_case_with_lens, nvis_of,
                                oracle_hca, oracle_scores, oracle_sparse, query_subset, say)
 
@@ -26,7 +26,7 @@ from compressed_sparse_attention_indexer_amd.staging import DeviceCase  # noqa: 
 
 
 # a ragged batch of 12: long and short sequences, one with fewer visible
-# entries than K, one with none (the scorer's balanced split over the queries)
+# entries than K, one with none
 RAGGED_12 = [4 * 30000 + 1, 4 * 2000, 4 * 90 + 3, 50, 4 * 12000 + 2, 4 * 64000, 4 * 700 + 1, 4 * 5000 + 3,
              4 * 40000, 4 * 1500 + 2, 4 * 300, 4 * 20000 + 1]
 
@@ -509,8 +509,10 @@ def test_decode_b4_1m_full_csa_and_hca():
 def test_prefill_t2048_1m_sampled():
     """The 2,048-query chunk over a 1M-token cache at full size: every query's
     selection is checked for validity and every score row for its causal
-    mask; sampled queries (both ends, query-block edges) are compared with
-    the oracle: scores, the selected set, and attention on that set."""
+    mask; every query's scores at 128 sampled entries (seen by all queries)
+    are compared with the oracle's; sampled queries (both ends, query-block
+    edges) are compared with the oracle in full: scores, the selected set,
+    and attention on that set."""
     case = inputs.make_case(inputs.WORKLOADS["prefill_t2048_1m"], with_hca=False)
     wl = case.wl
     say(f"[case] {wl.name} T={wl.q_len} max_entries={case.max_entries}")
@@ -529,6 +531,22 @@ def test_prefill_t2048_1m_sampled():
     for t in range(wl.q_len):
         check_topk_valid(g_idx[0, t], int(nvis[t]), wl.topk)
     assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all())
+    # every query at sampled entries: the oracle scores a cache made of just
+    # those rows, every one visible (entry j's score does not depend on where
+    # the row sits once it is visible)
+    n_common = int(nvis.min())
+    rng = np.random.default_rng(2048)
+    js = np.unique(np.concatenate([[0, n_common - 1], rng.choice(n_common, 126, replace=False)]))
+    k_sub = [np.ascontiguousarray(case.k_idx[0][js])]
+    n_s = len(js)
+    o_s = oracle.index_scores(case.q_idx, case.w, k_sub, np.array([n_s * wl.ratio], np.int32),
+                              np.full(wl.q_len, n_s * wl.ratio - 1, np.int32), ratio=wl.ratio, n_max=n_s,
+                              dtype=wl.dtype)[0].astype(np.float64)
+    g_s = row[:, torch.from_numpy(js).cuda()].cpu().numpy().astype(np.float64)
+    rms = np.sqrt(np.mean(o_s ** 2, axis=1))
+    worst = float(np.max(np.max(np.abs(g_s - o_s), axis=1) / rms))
+    assert worst <= SCORE_TOL, f"sampled entries: worst score err / rms {worst:.2e}"
+    say(f"  ok: all {wl.q_len} queries at {n_s} sampled entries, worst score err/rms={worst:.2e}")
     # sampled queries against the oracle
     ts = [0, 1, 15, 16, 1000, 2046, 2047]
     sub = query_subset(case, ts)
