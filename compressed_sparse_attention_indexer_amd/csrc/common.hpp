@@ -94,17 +94,52 @@ __device__ __forceinline__ float row16_max(float v) {
     return v;
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+// Inclusive prefix sum of x over the 64 lanes, on DPP: row_shr 1, 2, 4, 8
+// within each 16-lane row (lanes shifted in from outside the row add 0), then
+// row_bcast 15 (the last lane of rows 0 and 2 added to rows 1 and 3) and
+// row_bcast 31 (lane 31 added to rows 2 and 3).  No LDS round trip, unlike a
+// scan over __shfl_up.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);
     return x;
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-    return x;
+__device__ __forceinline__ uint32_t wave_incl_scan_u(uint32_t x) { return (uint32_t)wave_incl_scan((int)x); }
+
+// Largest x over the 64 lanes, in every lane: the 16-lane row maximum on DPP
+// (as row16_max), then across rows with the lane swaps.
+__device__ __forceinline__ int wave_max_int(int x) {
+    x = max(x, __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false));
+    x = max(x, __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false));
+    x = max(x, __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false));
+    x = max(x, __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false));
+    const auto a = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+    x = max((int)a[0], (int)a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+    return max((int)b[0], (int)b[1]);
 }
+
+// Sum of v over the 16 lanes of each DPP row, in every lane of the row (the
+// pattern of row16_max; each step adds a lane pair in both orders, which give
+// the same float, so every lane holds the same sum).
+__device__ __forceinline__ float row16_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
+    return v;
+}
+
+// Largest / sum of x over the 64 lanes, in every lane: DPP within the rows,
+// then the lane swaps across them (no LDS round trip).
+__device__ __forceinline__ float wave_max(float x) { return max_xor32(max_xor16(row16_max(x))); }
+
+__device__ __forceinline__ float wave_sum(float x) { return sum_xor32(sum_xor16(row16_sum(x))); }
 
 // Window rows a query at p attends: raw positions [lo, hi], clamped to the
 // window buffer [pos0, pos0 + rows - 1].  Returns the count (>= 0).

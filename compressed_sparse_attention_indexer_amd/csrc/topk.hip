@@ -59,12 +59,8 @@ __device__ __forceinline__ void find_bin_256(TopkSharedT<NT> &sh, int need) {
             h[i] = sh.hist[4 * lane + i];
             s += h[i];
         }
-        uint32_t suf = s;  // sum over lanes >= this lane
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t t = __shfl_down(suf, o);
-            if (lane + o < 64) suf += t;
-        }
+        const uint32_t inc = wave_incl_scan_u(s);
+        const uint32_t suf = __builtin_amdgcn_readlane(inc, 63) - inc + s;  // sum over lanes >= this lane
         const uint32_t above = suf - s;
         if (above < (uint32_t)need && (uint32_t)need <= suf) {
             uint32_t a = above;
@@ -274,12 +270,7 @@ __device__ bool select_ordered(const int32_t *v, int na, const uint32_t *c_key, 
             cb[i] = h[255 - (4 * tid + i)];
             sum += cb[i];
         }
-        uint32_t incl = sum;  // inclusive prefix over lanes (lane 0 = top bins)
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t t = __shfl_up(incl, o);
-            if (tid >= o) incl += t;
-        }
+        const uint32_t incl = wave_incl_scan_u(sum);  // inclusive prefix over lanes (lane 0 = top bins)
         uint32_t acc = incl - sum;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -477,12 +468,9 @@ __global__ __launch_bounds__(kAuxThreads) void topk_emit_kernel(TopkArgs a) {
     if (tid < 64) {
         const int m_top = a.win_hdr[w];
         const uint32_t cnt = tid < kTopkWin ? a.win_cnt[w * kTopkWin + tid] : 0u;  // bin m_top - 31 + tid
-        uint32_t suf = cnt;
-#pragma unroll
-        for (int o = 1; o < kTopkWin; o <<= 1) {
-            const uint32_t x = __shfl_down(suf, o);
-            if (tid + o < kTopkWin) suf += x;
-        }
+        // suffix sums over the window (lanes kTopkWin.. hold 0)
+        const uint32_t inc = wave_incl_scan_u(cnt);
+        const uint32_t suf = __builtin_amdgcn_readlane(inc, 63) - inc + cnt;
         const uint64_t fits = __ballot(tid < kTopkWin && suf <= (uint32_t)cap);
         if (tid == 0)
             s_cut = m_top < 0 ? 0 : (fits ? m_top - (kTopkWin - 1) + __builtin_ctzll(fits) : m_top + 1);
@@ -562,11 +550,7 @@ __device__ bool select_slots(const uint32_t (&key)[kListRounds], const int32_t (
                              uint32_t bin, int K, int32_t *out, TopkShared &sh, uint32_t *s_base, int *s_red,
                              uint32_t *s_mkey, int *s_mslot) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    auto isum = [](int x) {
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-        return x;
-    };
+    auto isum = [](int x) { return __builtin_amdgcn_readlane(wave_incl_scan(x), 63); };
     // level 1: candidates by key bits 19..12, and the count above the bin
     if (tid < 256) sh.hist[tid] = 0u;
     if (tid == 0) sh.bcast[2] = 0;  // b2 members gathered
@@ -594,13 +578,9 @@ __device__ bool select_slots(const uint32_t (&key)[kListRounds], const int32_t (
             h[i] = sh.hist[4 * lane + i];
             sum += h[i];
         }
-        uint32_t suf = sum;  // over lanes >= this lane
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t x = __shfl_down(suf, o);
-            if (lane + o < 64) suf += x;
-        }
-        const uint32_t total = __shfl(suf, 0);
+        const uint32_t inc = wave_incl_scan_u(sum);
+        const uint32_t total = __builtin_amdgcn_readlane(inc, 63);
+        const uint32_t suf = total - inc + sum;  // over lanes >= this lane
         if (lane == 0) sh.bcast[3] = (int)total;
         if (need >= 1 && (uint32_t)need <= total) {
             uint32_t above = suf - sum;
@@ -697,12 +677,7 @@ __device__ bool select_slots(const uint32_t (&key)[kListRounds], const int32_t (
             c[i] = 2 * tid + i < m ? s_base[2 * tid + i] : 0u;
             sum += c[i];
         }
-        uint32_t inc = sum;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t x = __shfl_up(inc, o);
-            if (tid >= o) inc += x;
-        }
+        const uint32_t inc = wave_incl_scan_u(sum);
         uint32_t run = inc - sum;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {

@@ -17,12 +17,7 @@ template <int NT>
 __device__ __forceinline__ int block_scan_excl(int x, int *s_wave, int *total) {
     constexpr int NW = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int inc = x;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(inc, o);
-        if (lane >= o) inc += t;
-    }
+    const int inc = wave_incl_scan(x);
     if (lane == 63) s_wave[wave] = inc;
     __syncthreads();
     int before = 0, all = 0;
@@ -63,8 +58,7 @@ __device__ __forceinline__ void hist_window_store(const uint32_t *lh, int32_t *h
 #pragma unroll
     for (int i = kPer - 1; i >= 0; --i)
         if (mb < 0 && lh[kPer * tid + i]) mb = kPer * tid + i;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mb = max(mb, __shfl_xor(mb, o));
+    mb = wave_max_int(mb);
     if (lane == 0) s_red[wave] = mb;
     __syncthreads();
     const int M = max(max(s_red[0], s_red[1]), max(s_red[2], s_red[3]));
@@ -80,8 +74,7 @@ __device__ __forceinline__ void hist_window_store(const uint32_t *lh, int32_t *h
 __device__ __forceinline__ void hist_window_store_top(const uint32_t *lh, int mb, int32_t *hdr, uint32_t *cnt,
                                                       int *s_red) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mb = max(mb, __shfl_xor(mb, o));
+    mb = wave_max_int(mb);
     if (lane == 0) s_red[wave] = mb;
     __syncthreads();  // also: every add to lh is done
     const int M = max(max(s_red[0], s_red[1]), max(s_red[2], s_red[3]));
@@ -121,8 +114,7 @@ __device__ __forceinline__ uint32_t window_threshold(const int32_t *hdr, const u
     load_window(tid >> 2);  // issued before the header maximum below waits for its loads
     int m = -1;
     for (int w = tid; w < n_win; w += nt) m = max(m, hdr[w]);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = max(m, __shfl_xor(m, o));
+    m = wave_max_int(m);
     if (lane == 0) s_red[wave] = m;
     for (int i = tid; i < kTopkWin; i += nt) s_hist[i] = 0u;
     __syncthreads();
