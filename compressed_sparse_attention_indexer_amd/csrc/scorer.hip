@@ -238,8 +238,8 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(
     }
     if (with_hist) {
         const size_t w = (size_t)qi * n_parts + part;
-        hist_window_store_top(lh, hmax, a.win_hdr + w, a.win_cnt + w * kTopkWin, s_red);
-        decode_emission<64 * kScoreWaves>(a, lh, lkeys, emit, nvis, s0, n_load, kWgStep, w, s_scan, &s_cut);
+        const int top = hist_window_store_top(lh, hmax, a.win_hdr + w, a.win_cnt + w * kTopkWin, s_red);
+        decode_emission<64 * kScoreWaves>(a, lh, lkeys, emit, nvis, s0, n_load, kWgStep, w, top, s_scan, &s_cut);
     }
 }
 

@@ -41,16 +41,18 @@ inline int decode_score_workgroups(int n_max, int n_queries, int wg_step) {
 // emit its region (the stretch's entries at or above a cut bin, at most em_cap
 // of them, in index order), or mark the region overflowed if its stretch did
 // not fit LDS (the host rules that out; the selection would then scan the row).
+// `top` is the stretch's highest non-empty histogram bin (-1 if none), as the
+// window store found it.
 template <int NT>
 __device__ void decode_emission(const ScoreArgs &a, const uint32_t *lh, const uint32_t *lkeys, bool emit, int nvis,
-                                int s0, int n_load, int wg_step, size_t w, int *s_scan, int *s_cut) {
+                                int s0, int n_load, int wg_step, size_t w, int top, int *s_scan, int *s_cut) {
     if (a.em_cap <= 0) return;
     const size_t r0 = w * a.em_cap;
     const int stretch0 = s0 * wg_step;
     if (emit) {
         int n_st = min(nvis, (s0 + n_load) * wg_step) - stretch0;
         n_st = n_st > 0 ? n_st : 0;
-        emit_region<NT>(lh, lkeys, n_st, stretch0, a.em_cap, a.em_hdr + 2 * w, a.em_key + r0, a.em_idx + r0, s_scan,
+        emit_region<NT>(lh, lkeys, n_st, stretch0, a.em_cap, top, a.em_hdr + 2 * w, a.em_key + r0, a.em_idx + r0, s_scan,
                         s_cut);
     } else if (threadIdx.x == 0) {
         a.em_hdr[2 * w] = 0;

@@ -212,8 +212,8 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_fp8_kernel(S
     }
     if (with_hist) {
         const size_t w = (size_t)qi * n_parts + part;
-        hist_window_store_top(lh, hmax, a.win_hdr + w, a.win_cnt + w * kTopkWin, s_red);
-        decode_emission<64 * kScoreWaves>(a, lh, lkeys, emit, nvis, s0, n_load, kF8WgStep, w, s_scan, &s_cut);
+        const int top = hist_window_store_top(lh, hmax, a.win_hdr + w, a.win_cnt + w * kTopkWin, s_red);
+        decode_emission<64 * kScoreWaves>(a, lh, lkeys, emit, nvis, s0, n_load, kF8WgStep, w, top, s_scan, &s_cut);
     }
 }
 

@@ -71,8 +71,8 @@ __device__ __forceinline__ void hist_window_store(const uint32_t *lh, int32_t *h
 
 // The same for a workgroup of 256 threads whose threads already know the
 // highest bin they added (mb, -1 if none): no scan of the histogram.
-__device__ __forceinline__ void hist_window_store_top(const uint32_t *lh, int mb, int32_t *hdr, uint32_t *cnt,
-                                                      int *s_red) {
+__device__ __forceinline__ int hist_window_store_top(const uint32_t *lh, int mb, int32_t *hdr, uint32_t *cnt,
+                                                     int *s_red) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     mb = wave_max_int(mb);
     if (lane == 0) s_red[wave] = mb;
@@ -83,6 +83,7 @@ __device__ __forceinline__ void hist_window_store_top(const uint32_t *lh, int mb
         cnt[tid] = (M >= 0 && b >= 0) ? lh[b] : 0u;
     }
     if (tid == 0) *hdr = M;
+    return M;
 }
 
 // Merge n_win windows (hdr[w], cnt[w][kTopkWin]) into the exact histogram of
@@ -137,17 +138,20 @@ __device__ __forceinline__ uint32_t window_threshold(const int32_t *hdr, const u
         load_window(w0 + (tid >> 2));
     }
     __syncthreads();
-    if (tid == 0) {
-        uint32_t result = kNoBin, acc = 0;
-        for (int t = kTopkWin - 1; t >= 0; --t) {
-            acc += s_hist[t];
-            if (acc >= (uint32_t)K) {
+    if (tid < 64) {  // wave 0: the highest bin t whose count from the top reaches K
+        const uint32_t c = lane < kTopkWin ? s_hist[lane] : 0u;
+        const uint32_t inc = wave_incl_scan_u(c);
+        const uint32_t suf = __builtin_amdgcn_readlane(inc, 63) - inc + c;  // bins t .. kTopkWin - 1
+        const uint64_t reach = __ballot(lane < kTopkWin && suf >= (uint32_t)K);
+        if (lane == 0) {
+            uint32_t result = kNoBin;
+            if (reach) {
+                const int t = 63 - __builtin_clzll(reach);
                 const int b = M - (kTopkWin - 1) + t;
                 result = b >= 0 ? (uint32_t)b : kNoBin;
-                break;
             }
+            s_red[0] = (int)result;
         }
-        s_red[0] = (int)result;
     }
     __syncthreads();
     const uint32_t result = (uint32_t)s_red[0];
@@ -165,33 +169,59 @@ __device__ __forceinline__ uint32_t window_threshold(const int32_t *hdr, const u
 // then each holds all of its region's entries at or above the threshold.
 // NT threads (a multiple of 64 dividing kTopkBins); s_wave NT / 64 ints.
 template <int NT>
-__device__ void emit_region(const uint32_t *lh, const uint32_t *keys, int n, int first, int cap, int32_t *hdr,
-                            uint32_t *okey, int32_t *oidx, int *s_wave, int *s_cut) {
+__device__ void emit_region(const uint32_t *lh, const uint32_t *keys, int n, int first, int cap, int top,
+                            int32_t *hdr, uint32_t *okey, int32_t *oidx, int *s_wave, int *s_cut) {
     constexpr int kPer = kTopkBins / NT;
     constexpr int kE = 8;  // consecutive entries per thread and round of the compaction
-    const int tid = threadIdx.x;
-    const int v = NT - 1 - tid;  // this thread's bins [kPer v, kPer v + kPer): thread 0 takes the top range
-    uint32_t h[kPer];
-    int c = 0;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        h[i] = lh[kPer * v + i];
-        c += (int)h[i];
-    }
-    int tot;
-    const int above = block_scan_excl<NT>(c, s_wave, &tot);  // entries in the bins above this thread's range
-    if (tot <= cap) {
-        if (tid == 0) *s_cut = 0;
-    } else if (above <= cap && above + c > cap) {  // the range where the count from the top passes cap
-        int run = above, cut = kPer * v + kPer;
-        for (int i = kPer - 1; i >= 0; --i) {
-            run += (int)h[i];
-            if (run > cap) break;
-            cut = kPer * v + i;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // The cut from the 64 bins at and below the stretch's highest bin `top`
+    // (wave 0, a DPP suffix sum): it lies there unless those bins hold no more
+    // than cap entries while the stretch holds more, and then the block scan
+    // over all the bins below decides.  A top bin holding more than cap alone
+    // gives cut = top + 1: nothing is emitted, and the selection, seeing the
+    // region's cut above its threshold bin or not, stays exact.
+    if (tid < 64) {
+        int cf = -2;  // -2: not decided here
+        if (n <= cap) {
+            cf = 0;
+        } else if (top >= 0) {
+            const int b = top - 63 + lane;
+            const uint32_t cb = b >= 0 ? lh[b] : 0u;
+            const uint32_t inc = wave_incl_scan_u(cb);
+            const uint32_t tw = __builtin_amdgcn_readlane(inc, 63);
+            const uint32_t suf = tw - inc + cb;  // entries in bins b .. top
+            if (tw > (uint32_t)cap) {
+                const uint64_t fit = __ballot(suf <= (uint32_t)cap);  // lanes l0 .. 63
+                cf = fit ? top - 63 + __builtin_ctzll(fit) : top + 1;
+            }
         }
-        *s_cut = cut;
+        if (lane == 0) *s_cut = cf;
     }
     __syncthreads();
+    if (*s_cut == -2) {  // the same in every thread
+        const int v = NT - 1 - tid;  // this thread's bins [kPer v, kPer v + kPer): thread 0 takes the top range
+        uint32_t h[kPer];
+        int c = 0;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            h[i] = lh[kPer * v + i];
+            c += (int)h[i];
+        }
+        int tot;
+        const int above = block_scan_excl<NT>(c, s_wave, &tot);  // entries in the bins above this thread's range
+        if (tot <= cap) {
+            if (tid == 0) *s_cut = 0;
+        } else if (above <= cap && above + c > cap) {  // the range where the count from the top passes cap
+            int run = above, cut = kPer * v + kPer;
+            for (int i = kPer - 1; i >= 0; --i) {
+                run += (int)h[i];
+                if (run > cap) break;
+                cut = kPer * v + i;
+            }
+            *s_cut = cut;
+        }
+        __syncthreads();
+    }
     const uint32_t cut = (uint32_t)*s_cut;
     int written = 0;
     for (int i0 = 0; i0 < n; i0 += NT * kE) {
