@@ -554,7 +554,7 @@ csa_status csa_api::attention_impl(const csa_dims *d, const void *q, const void 
     float *scores = scores_out ? scores_out : (float *)base;
     int32_t *idx = topk_idx_out ? topk_idx_out : (int32_t *)(base + off_idx);
     hipStream_t st = (hipStream_t)stream;
-    const csa::TopkArgs ta = topk_args(d, scores, seq_len, q_pos, idx, base + off_topk, true, fp8);
+    csa::TopkArgs ta = topk_args(d, scores, seq_len, q_pos, idx, base + off_topk, true, fp8);
     csa::ScoreArgs sa = score_args(d, q_idx, w, k_idx, seq_len, q_pos, scores);
     if (fp8) {
         sa.q_scale = f8->q_scale;
@@ -570,6 +570,17 @@ csa_status csa_api::attention_impl(const csa_dims *d, const void *q, const void 
         sa.em_hdr = ta.em_hdr;
         sa.em_key = ta.em_key;
         sa.em_idx = ta.em_idx;
+        // many queries per sequence and no score output asked for: the tiled
+        // scorer keeps each (query, entry chunk)'s K best entries as it goes
+        // and writes no scores; the selection works from those alone
+        if (!scores_out && !fused_decode(d, fp8) && ta.em_cap >= d->topk && d->topk <= csa::kSelKeepMax &&
+            csa::tiled_chunk_entries(d->batch, d->q_len, d->max_entries) <= csa::kSelChunkMax) {
+            sa.sel_stream = 1;
+            sa.win_hdr = nullptr;
+            sa.win_cnt = nullptr;
+            ta.em_stream = 1;
+            ta.em_chunk = 0;
+        }
     }
     hipError_t e = fp8 ? csa::launch_index_scores_fp8(sa, st) : csa::launch_index_scores(sa, d->dtype, st);
     if (e != hipSuccess) return hip_status(e, "csa_attention/scores");

@@ -28,6 +28,9 @@ struct ScoreArgs {
     int32_t *em_hdr;            // [Q, n_win, 2]: cut bin, count
     uint32_t *em_key;           // [Q, n_win, em_cap]
     int32_t *em_idx;            // [Q, n_win, em_cap]
+    // tiled scorer only: 1 = write no scores; each (query, entry chunk) region
+    // gets the chunk's K best entries (K <= kSelKeepMax <= em_cap)
+    int sel_stream;
     // fp8 (E4M3) index tensors: per-row scales (null for bf16 / fp32)
     const float *q_scale;       // [Q, HI]
     const void *const *k_scale; // [B] -> [N_b] float
@@ -67,6 +70,8 @@ constexpr int kFltRegionWords = 2 + kFltAboveCap + 2 * kFltCandCap;
 constexpr int kTopkManyQueries = 256;     // from this many queries on: one selecting workgroup per query
 constexpr int kTopkMaxRegions = 256;      // emitted regions (decode-scorer workgroups) per query at most
 constexpr int kTopkMaxSlots = 8192;       // emitted slots (regions x entries per region) per query at most
+constexpr int kSelKeepMax = 512;         // K at most for the tiled scorer's streaming selection
+constexpr int kSelChunkMax = 65536;      // entries per chunk at most for it (16-bit offsets)
 
 struct TopkArgs {
     const float *scores;        // [Q, n_max]
@@ -85,6 +90,9 @@ struct TopkArgs {
     // em_chunk > 0: the top-k emits the regions itself, one per window of
     // em_chunk entries, from the scores (after the tiled scorer)
     int em_cap, em_chunk;
+    // 1: each region holds its chunk's K best entries (the tiled scorer's
+    // streaming selection, no scores written); the threshold comes from the slots
+    int em_stream;
     int32_t *em_hdr;            // [Q, n_win, 2]
     uint32_t *em_key;           // [Q, n_win, em_cap]
     int32_t *em_idx;            // [Q, n_win, em_cap]

@@ -259,6 +259,13 @@ __global__ __launch_bounds__(64 * kScoreWaves, 1) void index_scores_bf16_kernel(
 // segment.  The per-element epilogue (activation + weighted add: two VALU
 // instructions per 256 MFMA flops) runs beside the other wave's MFMAs.
 //
+// Selection in the fused call (kMode): none (the scores alone), histogram
+// windows (each wave keeps its query's key histogram over the chunk beside
+// the scores it writes; the top-k then emits and selects from the scores), or
+// streaming: no score is written; each wave keeps its query's K best entries
+// of the chunk in LDS (see wave_keep_top) and writes them as the chunk's
+// region for the selection, which then never reads a score row.
+//
 // Workgroup order: when the entry chunks come in multiples of 8, the
 // workgroups sharing an entry chunk are dealt to one XCD (hardware deals
 // consecutive workgroup ids round-robin over the 8 XCDs), so the key tiles
@@ -274,7 +281,90 @@ constexpr int kPfTargetWgs = 2048;           // about 8 workgroups per CU over t
 constexpr int kPfStage = kPfTile * (kDI / 8) / (64 * kPfWaves);  // 16-byte tile chunks per thread
 static_assert(kPfStage * 64 * kPfWaves == kPfTile * (kDI / 8), "tile staging covers the tile");
 static_assert(kPfTile % 64 == 0, "whole 64-entry groups per tile");
+constexpr int kSelNone = 0, kSelHist = 1, kSelStream = 2;  // the tiled kernel's selection modes
+constexpr int kSelBuf = 1920;                  // stream buffer per wave (entries: key + 16-bit chunk offset)
+constexpr int kSelSlots = kSelBuf / 64;        // buffer entries per lane
+constexpr int kSelSlack = 256;                 // a compaction inside the chunk keeps K .. K + kSelSlack entries
+static_assert(kSelBuf % 64 == 0, "whole lanes per buffer");
+static_assert(kSelKeepMax + kSelSlack + kPfTile <= kSelBuf - kPfTile, "a compaction leaves room for a tile");
 }  // namespace
+
+// Stream selection, one wave: of the n entries in its LDS buffer (keys bk,
+// chunk offsets bo, in index order; n > K), keep the best ones in place and
+// in index order, set n to their count and return a key t such that the chunk's
+// K best so far are all kept and every entry met later (a higher index) needs
+// a key above t to be among them.  The keys are held in registers; t is found
+// bit by bit from the top (the largest value with at least K keys at or above
+// it), starting below the bits all the keys share.  exact: t is the K-th key,
+// and exactly K entries are kept (every key above t and the first ones equal
+// to it: equal keys rank by lower index).  Otherwise the search stops as soon
+// as no more than K + kSelSlack keys are at or above t, and all of them are
+// kept (then at least K keys are at or above t, so a later entry with key t
+// or below ranks under K of them).  LDS accesses of one wave complete in
+// issue order, so the in-place writes (each to a slot at or below the one it
+// came from, after the reads of its 64-slot group) need no barrier.
+__device__ __forceinline__ uint32_t wave_keep_top(uint32_t *bk, uint16_t *bo, int &n, int K, bool exact) {
+    const int lane = threadIdx.x & 63;
+    const uint64_t lt = lanemask_lt();
+    uint32_t k[kSelSlots];
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+    for (int s = 0; s < kSelSlots; ++s) {
+        const bool live = 64 * s + lane < n;
+        k[s] = live ? bk[64 * s + lane] : 0u;  // live keys are > 0
+        kmin = live ? min(kmin, k[s]) : kmin;
+        kmax = max(kmax, k[s]);
+    }
+    // unsigned wave maximum through the signed one (bias by 2^31); the minimum as ~max(~x)
+    auto umax = [](uint32_t x) { return (uint32_t)wave_max_int((int)(x ^ 0x80000000u)) ^ 0x80000000u; };
+    kmin = ~umax(~kmin);
+    kmax = umax(kmax);
+    // every live key shares kmax's bits above the highest bit where kmin and kmax differ
+    const uint32_t diff = kmin ^ kmax;
+    const int top = diff ? 31 - __builtin_clz(diff) : -1;
+    uint32_t t = diff == 0u ? kmax : (top == 31 ? 0u : kmax & ~((2u << top) - 1u));
+    int cnt_t = n;  // keys at or above t
+#pragma unroll 1
+    for (int b = top; b >= 0; --b) {
+        if (!exact && cnt_t <= K + kSelSlack) break;
+        const uint32_t c = t | (1u << b);
+        int cnt = 0;
+#pragma unroll
+        for (int s = 0; s < kSelSlots; ++s) cnt += k[s] >= c;
+        cnt = __builtin_amdgcn_readlane(wave_incl_scan(cnt), 63);
+        if (cnt >= K) {
+            t = c;
+            cnt_t = cnt;
+        }
+    }
+    // equal keys that stop the search short of K + kSelSlack: keep exactly K
+    if (cnt_t > K + kSelSlack) exact = true;
+    int n_eq = n;  // keys equal to t kept: all of them unless exact
+    if (exact) {
+        int above = 0;
+#pragma unroll
+        for (int s = 0; s < kSelSlots; ++s) above += k[s] > t;
+        n_eq = K - __builtin_amdgcn_readlane(wave_incl_scan(above), 63);
+    }
+    int w = 0, eq_seen = 0;
+#pragma unroll
+    for (int s = 0; s < kSelSlots; ++s) {
+        const bool eq = k[s] == t;
+        const uint64_t em = __ballot(eq);
+        const bool keep = k[s] > t || (eq && eq_seen + __popcll(em & lt) < n_eq);
+        const uint64_t km = __ballot(keep);
+        if (keep) {
+            const int p = w + __popcll(km & lt);
+            const uint16_t o = bo[64 * s + lane];
+            bk[p] = k[s];
+            bo[p] = o;
+        }
+        w += __popcll(km);
+        eq_seen += __popcll(em);
+    }
+    n = w;
+    return t;
+}
 
 struct TiledPlan {
     int qb_per_seq;        // query blocks per sequence
@@ -296,9 +386,10 @@ static TiledPlan tiled_plan(const ScoreArgs &a) {
     return p;
 }
 
-template <int kAct, bool kHist>
+template <int kAct, int kMode>
 __global__ __launch_bounds__(64 * kPfWaves, 1) void index_scores_tiled_kernel(ScoreArgs a, TiledPlan pl) {
-    static_assert(!kHist || kPfQW == 1, "one histogram per wave holds one query");
+    constexpr bool kHist = kMode == kSelHist, kStream = kMode == kSelStream;
+    static_assert((!kHist && !kStream) || kPfQW == 1, "one histogram or selection per wave holds one query");
     __shared__ __attribute__((aligned(16))) uint32_t kt[2][kPfTileWords];
     __shared__ int s_nv[kPfWaves];
     // Optional top-k key-histogram window of each wave's query over this
@@ -311,6 +402,19 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void index_scores_tiled_kernel(Sc
     // The 64-entry groups themselves stay free of branches.
     __shared__ uint32_t lh[kHist ? kPfWaves : 1][kHist ? kTopkWin * 64 : 1];
     int m_top = -1;
+    // Stream selection: each wave's buffer of entries (key, offset in the
+    // chunk) above its threshold sel_thr, sel_n of them, in index order
+    // (sel_n and sel_thr are the same in every lane of the wave).  A wave whose
+    // buffer could overflow in the next tile raises its flag at the end of a
+    // tile; after the next tile's barrier every wave sees the flags, and if
+    // any is up, every wave holding more than K + kSelSlack entries compacts
+    // then, so the workgroup waits at its barriers for one round of
+    // compactions instead of one per wave.
+    __shared__ uint32_t sel_key[kStream ? kPfWaves : 1][kStream ? kSelBuf : 1];
+    __shared__ uint16_t sel_off[kStream ? kPfWaves : 1][kStream ? kSelBuf : 1];
+    __shared__ int sel_flag[kStream ? 2 : 1][kPfWaves];  // by tile parity
+    int sel_n = 0;
+    uint32_t sel_thr = 0u;  // live keys are > 0
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int e = lane & 15, g = lane >> 4;
 
@@ -359,9 +463,11 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void index_scores_tiled_kernel(Sc
         }
     }
     const bool with_hist = kHist && qok[0] && nv[0] > a.K;  // one query per wave: its own histogram
+    const bool with_sel = kStream && qok[0] && nv[0] > a.K;
     if (kHist) {
         for (int i = tid; i < kPfWaves * kTopkWin * 64; i += 64 * kPfWaves) (&lh[0][0])[i] = 0u;
     }
+    if (kStream && tid < 2 * kPfWaves) (&sel_flag[0][0])[tid] = 0;
     __syncthreads();
     int nv_max = 0;
 #pragma unroll
@@ -399,6 +505,13 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void index_scores_tiled_kernel(Sc
         stash(buf);
         if (tile + 1 < n_ct) fetch(tile + 1);
         __syncthreads();
+        if (kStream) {  // a round of compactions when some wave's buffer could overflow in this tile
+            int any = 0;
+#pragma unroll
+            for (int w2 = 0; w2 < kPfWaves; ++w2) any |= sel_flag[tile & 1][w2];
+            if (any && sel_n > a.K + kSelSlack)
+                sel_thr = wave_keep_top(sel_key[wave], sel_off[wave], sel_n, a.K, false);
+        }
         int held[kPfTile / 64];  // per group: a bin above m_top, else -1
 #pragma unroll
         for (int grp = 0; grp < kPfTile / 64; ++grp) {  // 64 entries: one butterfly and store
@@ -439,7 +552,21 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void index_scores_tiled_kernel(Sc
                 }
                 const LanePair pr = pair16(k2[0], k2[1]);  // lane group lo keeps k2[lo]
                 const float tot = pr.lo + pr.hi;
-                if (qok[q] && j < a.n_max) a.scores[(size_t)qi[q] * a.n_max + j] = j < nv[q] ? tot : -INFINITY;
+                if (!kStream && qok[q] && j < a.n_max)
+                    a.scores[(size_t)qi[q] * a.n_max + j] = j < nv[q] ? tot : -INFINITY;
+                if (kStream) {
+                    const uint32_t key = order_key(tot);
+                    const bool take = with_sel && j < nv[q] && key > sel_thr;
+                    const uint64_t m = __ballot(take);
+                    if (m) {
+                        if (take) {
+                            const int p = sel_n + __popcll(m & lanemask_lt());
+                            sel_key[wave][p] = key;
+                            sel_off[wave][p] = (uint16_t)(j - j0);
+                        }
+                        sel_n += __popcll(m);
+                    }
+                }
                 if (kHist) {
                     const bool v = with_hist && j < nv[q];
                     const int bin = (int)(order_key(tot) >> 20);
@@ -468,12 +595,32 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void index_scores_tiled_kernel(Sc
                     if (held[g2] >= 0 && m_top - held[g2] < kTopkWin) hw[64 * (m_top - held[g2])] += 1u;
             }
         }
+        // the flag for the next tile (read after its barrier)
+        if (kStream && lane == 0) sel_flag[(tile + 1) & 1][wave] = sel_n > kSelBuf - kPfTile;
     }
     // entries of the chunk no query of the block sees
-    for (int jj = j0 + n_ct * kPfTile + lane; jj < j_end; jj += 64)
+    if (!kStream)
+        for (int jj = j0 + n_ct * kPfTile + lane; jj < j_end; jj += 64)
 #pragma unroll
-        for (int q = 0; q < kPfQW; ++q)
-            if (qok[q]) a.scores[(size_t)qi[q] * a.n_max + jj] = -INFINITY;
+            for (int q = 0; q < kPfQW; ++q)
+                if (qok[q]) a.scores[(size_t)qi[q] * a.n_max + jj] = -INFINITY;
+    if (with_sel) {
+        // the chunk's region: its best K entries in index order, the slots past
+        // them key 0 (no live key is 0); header {cut 0, count}
+        if (sel_n > a.K) wave_keep_top(sel_key[wave], sel_off[wave], sel_n, a.K, true);
+        const size_t w = (size_t)qi[0] * pl.n_chunks + ec;
+        uint32_t *okey = a.em_key + w * a.em_cap;
+        int32_t *oidx = a.em_idx + w * a.em_cap;
+        for (int i = lane; i < a.em_cap; i += 64) {
+            const bool live = i < sel_n;
+            okey[i] = live ? sel_key[wave][i] : 0u;
+            if (live) oidx[i] = j0 + sel_off[wave][i];
+        }
+        if (lane == 0) {
+            a.em_hdr[2 * w] = 0;
+            a.em_hdr[2 * w + 1] = sel_n;
+        }
+    }
     if (kHist) __syncthreads();  // the wave's histogram atomics are done before it is read
     if (with_hist) {
         // the chunk's window as the top-k expects it: hdr = highest non-empty bin
@@ -505,17 +652,25 @@ hipError_t launch_index_scores(const ScoreArgs &a, int dtype, hipStream_t stream
     if (score_uses_tiles(dtype, a.T)) {
         const TiledPlan pl = tiled_plan(a);
         const dim3 grid(a.B * pl.qb_per_seq * pl.n_chunks), block(64 * kPfWaves);
-        const bool hist = a.win_hdr != nullptr;  // the caller sized the windows with tiled_windows
+        // the caller sized the windows (or the stream regions) with tiled_windows
+        const int mode = a.sel_stream ? kSelStream : (a.win_hdr != nullptr ? kSelHist : kSelNone);
+        if (mode == kSelStream &&
+            (a.K < 1 || a.K > kSelKeepMax || a.em_cap < a.K || pl.tiles_per_chunk * kPfTile > kSelChunkMax))
+            return hipErrorInvalidValue;
         if (a.act == 0) {
-            if (hist)
-                hipLaunchKernelGGL((index_scores_tiled_kernel<0, true>), grid, block, 0, stream, a, pl);
+            if (mode == kSelStream)
+                hipLaunchKernelGGL((index_scores_tiled_kernel<0, kSelStream>), grid, block, 0, stream, a, pl);
+            else if (mode == kSelHist)
+                hipLaunchKernelGGL((index_scores_tiled_kernel<0, kSelHist>), grid, block, 0, stream, a, pl);
             else
-                hipLaunchKernelGGL((index_scores_tiled_kernel<0, false>), grid, block, 0, stream, a, pl);
+                hipLaunchKernelGGL((index_scores_tiled_kernel<0, kSelNone>), grid, block, 0, stream, a, pl);
         } else {
-            if (hist)
-                hipLaunchKernelGGL((index_scores_tiled_kernel<1, true>), grid, block, 0, stream, a, pl);
+            if (mode == kSelStream)
+                hipLaunchKernelGGL((index_scores_tiled_kernel<1, kSelStream>), grid, block, 0, stream, a, pl);
+            else if (mode == kSelHist)
+                hipLaunchKernelGGL((index_scores_tiled_kernel<1, kSelHist>), grid, block, 0, stream, a, pl);
             else
-                hipLaunchKernelGGL((index_scores_tiled_kernel<1, false>), grid, block, 0, stream, a, pl);
+                hipLaunchKernelGGL((index_scores_tiled_kernel<1, kSelNone>), grid, block, 0, stream, a, pl);
         }
         return hipGetLastError();
     }
@@ -552,7 +707,15 @@ int tiled_chunk_entries(int B, int T, int n_max) {
     return tiled_plan(a).tiles_per_chunk * kPfTile;
 }
 
-int tiled_emit_cap(int B, int T, int n_max, int K) { return decode_region_cap(tiled_windows(B, T, n_max), K); }
+int tiled_emit_cap(int B, int T, int n_max, int K) {
+    const int n = tiled_windows(B, T, n_max);
+    const int cap = decode_region_cap(n, K);
+    // room for the streaming selection's regions (a chunk's K best) when the
+    // selection can hold them all
+    const int ks = (K + 15) / 16 * 16;
+    if (K <= kSelKeepMax && (long)n * ks <= kTopkMaxSlots) return cap > ks ? cap : ks;
+    return cap;
+}
 
 int score_workgroups(int n_max, int n_queries) { return decode_score_workgroups(n_max, n_queries, kWgStep); }
 

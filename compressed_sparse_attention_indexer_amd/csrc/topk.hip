@@ -700,6 +700,36 @@ __device__ bool select_slots(const uint32_t (&key)[kListRounds], const int32_t (
     return true;
 }
 
+// Threshold bin (key bits 31..20) of the K-th largest live slot key, from the
+// slots themselves (regions that hold each chunk's K best entries: the K-th
+// largest slot key is then the row's K-th largest key).  Two 256-bin levels,
+// key bits 31..24 then 23..20; the live slots must number K or more.
+__device__ uint32_t slots_threshold(const uint32_t (&key)[kListRounds], int rounds, int K, TopkShared &sh) {
+    const int tid = threadIdx.x;
+    if (tid < 256) sh.hist[tid] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kListRounds; ++r)
+        if (r < rounds) lds_hist_add(sh.hist, key[r] >> 24, key[r] != 0u);
+    __syncthreads();
+    find_bin_256(sh, K);
+    __syncthreads();
+    const uint32_t b1 = (uint32_t)sh.bcast[0];
+    const int need = sh.bcast[1];
+    __syncthreads();
+    if (tid < 256) sh.hist[tid] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kListRounds; ++r)
+        if (r < rounds) lds_hist_add(sh.hist, (key[r] >> 20) & 0xFu, key[r] != 0u && (key[r] >> 24) == b1);
+    __syncthreads();
+    find_bin_256(sh, need);
+    __syncthreads();
+    const uint32_t bin = b1 << 4 | (uint32_t)sh.bcast[0];
+    __syncthreads();
+    return bin;
+}
+
 __global__ __launch_bounds__(kWG) void topk_lists_kernel(TopkArgs a) {
     __shared__ __attribute__((aligned(16))) ScanShared sc;
     __shared__ TopkShared sh;
@@ -733,6 +763,16 @@ __global__ __launch_bounds__(kWG) void topk_lists_kernel(TopkArgs a) {
         cnt = a.em_hdr[2 * (q0 + tid) + 1];
     }
     const int n = query_visible(a, qi);
+    if (a.em_stream) {  // every region holds its chunk's K best entries
+        if (n <= K) {
+            for (int i = tid; i < K; i += kWG) out[i] = i < n ? i : -1;
+            return;
+        }
+        const uint32_t bin = slots_threshold(key, rounds, K, sh);
+        if (!select_slots(key, idx, rounds, bin, K, out, sh, s_base, s_red, sc.c_key, sc.c_idx))
+            for (int i = tid; i < K; i += kWG) out[i] = -1;  // not reached: the slots hold the row's K best
+        return;
+    }
     // The windows are merged before the visible count is looked at, so their
     // loads go out in the same round as the slots and the count (a query with
     // no more than K visible entries wrote no windows and ignores the merge;
@@ -1002,7 +1042,7 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t stream, bool hist_done) {
         hipLaunchKernelGGL(topk_lds_kernel, dim3(Q), dim3(kWG), 0, stream, a);
         return hipGetLastError();
     }
-    if (a.em_cap > 0) {  // the scorer wrote the windows and (or, em_chunk > 0, the top-k now) the regions
+    if (a.em_cap > 0) {  // the scorer wrote the windows (or streamed its regions) and (or, em_chunk > 0, the top-k now) the regions
         if (a.em_chunk > 0) hipLaunchKernelGGL(topk_emit_kernel, dim3(a.n_win, Q), dim3(kAuxThreads), 0, stream, a);
         hipLaunchKernelGGL(topk_lists_kernel, dim3(Q), dim3(kWG), 0, stream, a);
         return hipGetLastError();

@@ -220,7 +220,12 @@ csa_status hca_mqa_decode(const csa_dims *dims, const void *q, const void *const
  * (device [B,T,max_entries] float32) are optional outputs; when NULL the
  * intermediates live in the workspace.  With bf16 index tensors the scorer
  * also writes the selection's key-histogram windows (one launch fewer); the
- * selected indices equal csa_topk_select's on the same scores.
+ * selected indices equal csa_topk_select's on the same scores.  With many
+ * queries per sequence (q_len >= 8), K <= 512 and scores_out NULL, the scorer
+ * writes no scores at all when the chunk plan allows it (entry chunks x K <=
+ * 8192, at most 65,536 entries per chunk): each (query, entry chunk) keeps its
+ * K best entries as it goes and the selection works from those, with the same
+ * result; the workspace's score area is then left untouched.
  */
 csa_status csa_attention(const csa_dims *dims, const void *q, const void *q_idx, const float *w,
                          const void *const *k_idx, const void *const *kv, const void *const *v,

@@ -485,6 +485,52 @@ def test_prefill_fused_selection_equals_standalone_topk(lens, T, q_pos0, act):
     np.testing.assert_array_equal(g_idx, want)
 
 
+def run_fused_stream(dc, act=csa.CSA_ACT_RELU, sentinel=0x5A):
+    """csa_attention without a score output (the tiled scorer's streaming
+    selection); the workspace starts filled with `sentinel`, and the bytes
+    where the scores would go are returned as well."""
+    dims = dc.csa_dims(index_act=act)
+    Q = dims.batch * dims.q_len
+    ws = torch.full((max(256, csa.workspace_size(dims, csa._lib.CSA_OP_ATTENTION)),), sentinel, dtype=torch.uint8,
+                    device="cuda")
+    idx = torch.full((dims.batch, dims.q_len, dims.topk), 7777, dtype=torch.int32, device="cuda")
+    out, lse = csa.csa_attention(dims, dc.q, dc.q_idx, dc.w, dc.k_idx_p, dc.kv_p, dc.v_p, dc.win_p, dc.win_v_p,
+                                 dc.win_pos0, dc.win_rows, dc.seq_len, dc.q_pos, dc.sink, topk_idx_out=idx,
+                                 workspace=ws)
+    torch.cuda.synchronize()
+    untouched = bool((ws[:Q * dims.max_entries * 4] == sentinel).all())
+    return idx, out, lse, untouched
+
+
+# (the streaming selection runs when the chunks' K best fit the selection's
+# slots: chunks x K <= 8192, e.g. 16 chunks at K = 512 from 1,024 queries on)
+@pytest.mark.parametrize("lens,T,q_pos0,act,topk", [
+    ([4 * 12000 + 3], 1024, 4 * 12000 + 3 - 1024, csa.CSA_ACT_RELU, 512),  # 16 chunks of 768 entries
+    ([4 * 6000 + 1, 4 * 9000 + 2], 512, 800, csa.CSA_ACT_RELU, 256),     # visible counts cross K inside the chunk
+    ([4 * 30000 + 1], 1024, 4 * 30000 - 1030, csa.CSA_ACT_NONE, 512),   # signed scores: keys in both halves
+    ([4 * 70000], 2048, 4 * 70000 - 2048, csa.CSA_ACT_RELU, 64),        # 8 chunks of 8,832 entries: compactions
+    ([4 * 12000 + 2], 9, 4 * 12000 - 9, csa.CSA_ACT_RELU, 1),            # K = 1, a partial query block
+])
+def test_prefill_streaming_selection(lens, T, q_pos0, act, topk):
+    """Without a score output the tiled scorer keeps each (query, entry
+    chunk)'s K best entries itself and writes no scores, and the selection
+    works from those alone.  Its selection and attention must be those of the
+    call that writes the scores (bit for bit), and the selection the oracle's
+    exact top-k of those scores; no score may be written to the workspace."""
+    wl, sl = flash_case(f"prefill_stream_{len(lens)}_{T}_{topk}", lens, q_len=T, q_pos0=q_pos0, topk=topk)
+    case = make_case_with_lens(wl, sl)
+    say(f"[case] {wl.name} B={wl.batch} T={T} max_entries={case.max_entries} act={act} K={topk}")
+    dc = DeviceCase(case)
+    g_scores, g_idx, g_out, g_lse = run_fused(dc, act)
+    s_idx, s_out, s_lse, untouched = run_fused_stream(dc, act)
+    assert untouched, "the streaming selection wrote scores"
+    np.testing.assert_array_equal(_np(s_idx), g_idx)
+    np.testing.assert_array_equal(_np(s_out), g_out)
+    np.testing.assert_array_equal(_np(s_lse), g_lse)
+    want = oracle.topk(g_scores, case.seq_len, case.q_pos, ratio=4, k=topk)
+    np.testing.assert_array_equal(_np(s_idx), want)
+
+
 # --------------------------------------------------------------------------- full-size workloads
 
 def test_decode_b1_64k_full():
@@ -559,6 +605,16 @@ def test_prefill_t2048_1m_sampled():
     rel = assert_attention_close(out[:, ts].cpu().numpy(), o_out, ATT_TOL_BF16, "out")
     np.testing.assert_allclose(lse[:, ts].cpu().numpy(), o_lse, atol=1e-3, rtol=0)
     say(f"  ok: sampled {len(ts)} queries, topk band swaps={n_diff} out err/rms={rel:.2e}")
+    # the same chunk without a score output (the streaming selection, as the
+    # fused call runs it when no scores are asked for): every query's
+    # selection and attention bit for bit
+    del scores, row, col
+    torch.cuda.empty_cache()
+    s_idx, s_out, s_lse, untouched = run_fused_stream(dc)
+    assert untouched, "the streaming selection wrote scores"
+    assert torch.equal(s_idx, idx), "streaming selection differs"
+    assert torch.equal(s_out, out) and torch.equal(s_lse, lse)
+    say(f"  ok: streaming selection equals the materialized one for all {wl.q_len} queries")
 
 
 # --------------------------------------------------------------------------- fp8 (E4M3) index tensors
