@@ -531,6 +531,32 @@ def test_prefill_streaming_selection(lens, T, q_pos0, act, topk):
     np.testing.assert_array_equal(_np(s_idx), want)
 
 
+@pytest.mark.parametrize("rep", [8, 0])
+def test_prefill_streaming_selection_ties(rep):
+    """Equal scores through the streaming selection: index-key rows repeated
+    `rep` times (rep 0: every row the same, so every visible entry of a query
+    has the same score), so the K-th score is shared by many entries and the
+    lower indices must win; the result must be the materialized call's and
+    the oracle's exact top-k of the same scores."""
+    wl, sl = flash_case(f"prefill_stream_ties_{rep}", [4 * 12000 + 3], q_len=1024, q_pos0=4 * 12000 + 3 - 1024)
+    case = make_case_with_lens(wl, sl)
+    k = case.k_idx[0]
+    src = np.arange(k.shape[0]) // rep if rep else np.zeros(k.shape[0], np.int64)
+    case.k_idx[0] = np.ascontiguousarray(k[src])
+    say(f"[case] {wl.name} T={wl.q_len} max_entries={case.max_entries} rows repeated {rep or 'all'}")
+    dc = DeviceCase(case)
+    g_scores, g_idx, g_out, g_lse = run_fused(dc)
+    s_idx, s_out, s_lse, untouched = run_fused_stream(dc)
+    assert untouched, "the streaming selection wrote scores"
+    want = oracle.topk(g_scores, case.seq_len, case.q_pos, ratio=4, k=wl.topk)
+    np.testing.assert_array_equal(g_idx, want)
+    np.testing.assert_array_equal(_np(s_idx), want)
+    np.testing.assert_array_equal(_np(s_out), g_out)
+    np.testing.assert_array_equal(_np(s_lse), g_lse)
+    if rep == 0:  # every visible entry ties: the K lowest indices
+        np.testing.assert_array_equal(want[0, :, :], np.broadcast_to(np.arange(wl.topk), want.shape[1:]))
+
+
 # --------------------------------------------------------------------------- full-size workloads
 
 def test_decode_b1_64k_full():
