@@ -709,7 +709,7 @@ int tiled_chunk_entries(int B, int T, int n_max) {
 
 int tiled_emit_cap(int B, int T, int n_max, int K) {
     const int n = tiled_windows(B, T, n_max);
-    const int cap = decode_region_cap(n, K);
+    const int cap = decode_region_cap(n, K, tiled_chunk_entries(B, T, n_max));
     // room for the streaming selection's regions (a chunk's K best) when the
     // selection can hold them all
     const int ks = (K + 15) / 16 * 16;

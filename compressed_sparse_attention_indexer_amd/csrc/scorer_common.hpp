@@ -61,16 +61,22 @@ __device__ void decode_emission(const ScoreArgs &a, const uint32_t *lh, const ui
 }
 
 // Slots per region (workgroup) a decode scorer can hand the selection, for
-// `wgs` region slots per query: about twice a workgroup's expected share of
-// the K selected entries plus a margin, and at least an even share of 4,096
-// slots per query (with few workgroups per query the threshold bin, 1/8
-// octave, can hold more than K entries, and a region that cannot emit all of
-// its entries at or above it sends the query to the slower whole-row
-// selection: 2 of the 32 queries of a ragged batch at 64K-128K tokens did with
-// 176 slots per region); the slots of a query must fit the selection and
-// exceed K.  0 if they cannot.
-inline int decode_region_cap(int wgs, int K) {
-    int cap = (2 * K / wgs + 48 + 15) / 16 * 16;
+// `wgs` region slots per query of up to `entries` entries each: about twice a
+// workgroup's expected share of the K selected entries plus a margin for the
+// members of the threshold bin (1/8 octave wide, so their number grows with
+// the region: 48, or a sixteenth of a smaller region), and at least an even
+// share of 4,096 slots per query (with few workgroups per query the threshold
+// bin can hold more than K entries, and a region that cannot emit all of its
+// entries at or above it sends the query to the slower whole-row selection: 2
+// of the 32 queries of a ragged batch at 64K-128K tokens did with 176 slots per
+// region).  On the synthetic decode inputs the most entries at or above the
+// threshold bin in one region are 11 of 128 (one query at 64K tokens, 32
+// slots), 33 of 4,096 (batch 4 at 1M, 64 slots), 52 of 4,096 (K = 1,024, 80
+// slots) and 189 of 3,950 (ragged batch, 512 slots).  The slots of a query must
+// fit the selection and exceed K.  0 if they cannot.
+inline int decode_region_cap(int wgs, int K, long entries) {
+    const int margin = entries / 16 < 48 ? (int)(entries / 16) : 48;
+    int cap = (2 * K / wgs + margin + 15) / 16 * 16;
     const int even = (kEmitTargetSlots / wgs + 15) / 16 * 16;
     cap = cap > even ? cap : even;
     cap = cap < 32 ? 32 : (cap > kEmitCapMax ? kEmitCapMax : cap);
@@ -88,7 +94,7 @@ inline DecodeGeom decode_geom_for(int n_max, int n_queries, int K, int step) {
     g.n_win = decode_score_workgroups(n_max, n_queries, step);
     const int steps = (n_max + step - 1) / step;
     const long stretch = (steps + g.n_win - 1) / g.n_win;
-    g.em_cap = stretch * step <= kEmitMax ? decode_region_cap(g.n_win, K) : 0;
+    g.em_cap = stretch * step <= kEmitMax ? decode_region_cap(g.n_win, K, stretch * step) : 0;
     return g;
 }
 
