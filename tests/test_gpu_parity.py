@@ -257,6 +257,9 @@ def _topk_case(n_vis_list, n_max, K, seed, ties=False):
 
 @pytest.mark.parametrize("n_vis,n_max,K,ties", [
     ([100, 513, 600], 600, 512, False),
+    ([16384], 16384, 512, False),          # one query at 65,536 tokens
+    ([4097, 16384, 9000], 16384, 512, True),
+    ([32769, 100], 32769, 512, True),
     ([5000, 32768, 20000], 32768, 512, True),
     ([32768], 32768, 2048, False),
     ([40000, 33000], 40000, 512, False),
@@ -287,6 +290,19 @@ def test_topk_many_long_rows(n_q, ties):
     got = _np(csa.csa_topk_select(dims, torch.from_numpy(scores).cuda(), torch.from_numpy(seq).cuda(),
                                   torch.from_numpy(pos).cuda()))
     np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("n", [4096, 20000, 32768])
+def test_topk_all_equal_scores_medium_row(n):
+    """Every score equal in a row of up to 32,768 entries (the row kept in LDS,
+    or the one-kernel threshold scan): the lowest K indices are taken."""
+    say(f"[case] topk all equal n={n}")
+    scores = np.full((1, 1, n), -1.5, np.float32)
+    seq = np.array([4 * n], np.int32)
+    dims = csa.make_dims(batch=1, topk=512, max_entries=n)
+    got = _np(csa.csa_topk_select(dims, torch.from_numpy(scores).cuda(), torch.from_numpy(seq).cuda(),
+                                  torch.from_numpy(seq - 1).cuda()))
+    np.testing.assert_array_equal(got.reshape(-1), np.arange(512, dtype=np.int32))
 
 
 def test_topk_all_equal_scores_long_row():
