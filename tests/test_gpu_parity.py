@@ -477,6 +477,24 @@ def test_prefill_chunk_no_activation():
     check_whole_step(make_case_with_lens(wl, sl), ATT_TOL_BF16, act=csa.CSA_ACT_NONE)
 
 
+def test_large_attention_launch_one_split():
+    """300 queries x 2 head groups: more attention workgroups than are resident
+    at once, so they take the one-dimensional order (one split per query: the
+    output is written directly)."""
+    wl, sl = flash_case("prefill_300", [4 * 1200 + 1], q_len=300, q_pos0=4 * 1200 + 1 - 300)
+    check_whole_step(make_case_with_lens(wl, sl), ATT_TOL_BF16)
+
+
+def test_pro_shapes_large_attention_launch_two_splits():
+    """128 heads (four head groups) and 100 causal queries: two splits per
+    query and 800 attention workgroups, so the split partials are written in
+    the one-dimensional order and merged by the combine."""
+    base = inputs.WORKLOADS["pro_decode_b4_1m"]
+    wl = inputs.scaled(base, "pro_q100", index=112, batch=2, q_len=50, seq_len=None, seq_len_range=None,
+                       q_pos0=4 * 2000 + 3 - 50)
+    check_whole_step(inputs.make_case(wl, seq_lens=np.array([4 * 3000 + 1, 4 * 2000 + 3], np.int32)), ATT_TOL_BF16)
+
+
 @pytest.mark.parametrize("lens,T,q_pos0,act", [
     ([4 * 20000 + 3], 300, 4 * 20000 + 3 - 300, csa.CSA_ACT_RELU),  # many queries: one selecting workgroup each
     ([4 * 6000 + 1, 4 * 9000 + 2], 40, 2030, csa.CSA_ACT_RELU),     # visible counts cross K inside the chunk
